@@ -1,0 +1,95 @@
+"""Pins of the oracle's read path (CPU only)."""
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import okv_synth
+import oracle
+
+
+def make_unit(name, t, seed=0):
+    wl = okv_synth.workload(name).with_(batch=1, tokens=t)
+    k, v = okv_synth.kv_tokens(wl, 0, t)
+    k = okv_synth.host_f32(k)[0, :, 0]
+    v = okv_synth.host_f32(v)[0, :, 0]
+    q = okv_synth.host_f32(okv_synth.queries(wl, step=seed))[0, :wl.group]
+    p64 = okv_synth.rotation_params(wl)
+    p32 = p64.astype(np.float32)
+    u = oracle.rotation_matrix(wl.rotation, p32.astype(np.float64), wl.d)
+    return wl, k, v, q, p32, u
+
+
+@pytest.mark.parametrize("name", ["tiny_d128_t256", "so4_d256_b32_t8k"])
+def test_unquantised_rotated_attention_equals_plain(name):
+    # the OIQ report, Section 2.3 / idea card, Mathematical statement: rotating q and k
+    # by U and the output back by U^T leaves attention unchanged (fp64, tiny inputs)
+    wl, k, v, q, _, _ = make_unit(name, 40)
+    u = oracle.rotation_matrix(wl.rotation, okv_synth.rotation_params(wl), wl.d)
+    y_plain = oracle.attend_exact(q, k, v)
+    y_rot = oracle.attend_exact(q @ u.T, k @ u.T, v @ u.T) @ u
+    assert np.abs(y_rot - y_plain).max() <= 1e-12 * np.abs(y_plain).max()
+
+
+def test_attend_exact_matches_torch_sdpa():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 64))
+    k = rng.standard_normal((33, 64))
+    v = rng.standard_normal((33, 64))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None])[0].numpy()
+    assert np.abs(oracle.attend_exact(q, k, v) - ref).max() < 1e-13
+
+
+@pytest.mark.parametrize("name", ["tiny_d128_t256", "so4_d256_b32_t8k",
+                                  "gqa_b16h64kv8_t128k_asym"])
+def test_attend_unit_equals_sdpa_on_unrotated_dequantised_cache(name):
+    # independent route: dequantise, rotate the keys and values back with U^T, and run
+    # torch's scaled-dot-product attention in float64 on the ORIGINAL query
+    wl, k, v, q, p32, u = make_unit(name, 100)
+    c = oracle.write_unit(k, v, wl, p32)
+    y = oracle.attend_unit(q, c["k_codes"], c["k_meta"], c["v_codes"], c["v_meta"], 100, wl, u)
+    k_hat = oracle.dequantize(c["k_u"], c["k_meta"], wl) @ u      # rows of U^T k_hat_rot
+    v_hat = oracle.dequantize(c["v_u"], c["v_meta"], wl) @ u
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None], torch.from_numpy(k_hat)[None],
+        torch.from_numpy(v_hat)[None])[0].numpy()
+    assert np.abs(y - ref).max() < 1e-11 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("name", ["tiny_d128_t256", "gqa_b16h64kv8_t128k_asym"])
+def test_single_token_returns_rotated_back_value(name):
+    # T = 1: the softmax weight is 1, so y = U^T v_hat_rot
+    wl, k, v, q, p32, u = make_unit(name, 1)
+    c = oracle.write_unit(k, v, wl, p32)
+    y = oracle.attend_unit(q, c["k_codes"], c["k_meta"], c["v_codes"], c["v_meta"], 1, wl, u)
+    want = oracle.dequantize(c["v_u"], c["v_meta"], wl)[0] @ u
+    assert np.abs(y - want[None]).max() < 1e-13
+
+
+def test_zero_query_gives_mean_value():
+    wl, k, v, q, p32, u = make_unit("tiny_d128_t256", 70)
+    c = oracle.write_unit(k, v, wl, p32)
+    y = oracle.attend_unit(np.zeros_like(q), c["k_codes"], c["k_meta"], c["v_codes"],
+                           c["v_meta"], 70, wl, u)
+    want = oracle.dequantize(c["v_u"], c["v_meta"], wl).mean(0) @ u
+    assert np.abs(y - want[None]).max() < 1e-13
+
+
+def test_quantised_attention_close_to_exact_and_rotation_helps():
+    # diagnostics on the synthetic outlier model (direction only, as the idea card's
+    # Verification reports): Hadamard rotation lowers the worst block maximum relative
+    # to the vector norm and the attention error of 3-bit storage
+    wl, k, v, q, p32, u = make_unit("mha_b4h32_t128k", 512)
+    y_ref = oracle.attend_exact(q, k, v)
+    c = oracle.write_unit(k, v, wl, p32)
+    y_rot = oracle.attend_unit(q, c["k_codes"], c["k_meta"], c["v_codes"], c["v_meta"], 512, wl, u)
+    ident = SimpleNamespace(**{**wl.__dict__})
+    ku, km = oracle.quantize_f32(k, ident)
+    vu, vm = oracle.quantize_f32(v, ident)
+    y_norot = oracle.attend_exact(q, oracle.dequantize(ku, km, ident), oracle.dequantize(vu, vm, ident))
+    e_rot = np.sqrt(np.mean((y_rot - y_ref) ** 2)) / np.sqrt(np.mean(y_ref ** 2))
+    e_norot = np.sqrt(np.mean((y_norot - y_ref) ** 2)) / np.sqrt(np.mean(y_ref ** 2))
+    assert e_rot < e_norot
+    assert e_rot < 0.5
