@@ -1,0 +1,210 @@
+"""Benchmark of the rotated 3-bit KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch: okv_write appends one new
+token per sequence (rotate, quantise, pack), then okv_decode_attn attends with one
+query per (sequence, query head) over the whole cache (rotate q, fused unpack /
+scale / dot, online softmax, P.V, split-K reduce, rotate back).
+
+Default workload: 7B MHA shape at 128K context (batch 4, 32 heads, d 128,
+131,072 cached tokens per sequence, 8.3 % outlier channels, block 32, fp16 scales).
+Prints one JSON line.  `value` is decode-attention GB/s over the algorithmic bytes
+of the packed cache (codes + scales read, q read, output written), timed over
+whole steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode attn GB/s over packed 3-bit KV (% HBM peak); okv_write tokens/s"
+
+
+def algorithmic_decode_bytes(wl, t):
+    in_b = 4 if wl.in_dtype == "f32" else 2
+    cache = 2 * wl.batch * wl.hkv * t * wl.row_bytes()
+    q = wl.batch * wl.hq * wl.d * in_b
+    out = wl.batch * wl.hq * wl.d * 4
+    return cache, q, out
+
+
+def write_bytes_per_position(wl):
+    in_b = 4 if wl.in_dtype == "f32" else 2
+    return wl.batch * wl.hkv * 2 * (wl.d * in_b + wl.row_bytes())
+
+
+def cpu_baseline(wl, target_s=12.0):
+    """Time the CPU oracle's decode on (sequence, KV head) units of the workload at
+    its full context length (same distributions; values drawn on the host)."""
+    import numpy as np
+
+    import okv_synth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    unit = wl.with_(batch=1, hkv=1, hq=wl.group)
+    p32 = okv_synth.rotation_params(unit, dtype=np.float32)
+    u = oracle.rotation_matrix(unit.rotation, p32.astype(np.float64), unit.d)
+    k, v = okv_synth.kv_tokens(unit, 0, unit.tokens)
+    ref = oracle.write_unit(okv_synth.host_f32(k)[0, :, 0], okv_synth.host_f32(v)[0, :, 0], unit, p32)
+    q = okv_synth.host_f32(okv_synth.queries(unit, 0))[0]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attend_unit(q, ref["k_codes"], ref["k_meta"], ref["v_codes"], ref["v_meta"],
+                           unit.tokens, unit, u)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or n >= 64:
+            break
+    unit_bytes = 2 * unit.tokens * unit.row_bytes()
+    return {
+        "value": round(n * unit_bytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} decode call(s) of one (sequence, KV head) unit: {unit.group} query head(s) "
+                  f"over {unit.tokens} tokens (NumPy, float64 attention from packed codes), "
+                  f"{el:.1f} s; BLAS threads {threads}, unpack/dequantise single-threaded",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mha_b4h32_t128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "copies": 5}))
+        return
+
+    import decode_attention_okv_amd as okv
+    import okv_synth
+
+    wl = okv_synth.workload(args.workload)
+    W, K = args.warmup, args.steps
+    T0 = wl.tokens
+    cap = -(-(T0 + W + K + 1) // 32) * 32
+    p32 = okv_synth.rotation_params(wl, dtype=np.float32)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    cache = okv.OkvCache(batch=wl.batch, num_q_heads=wl.hq, num_kv_heads=wl.hkv, head_dim=wl.d,
+                         max_tokens=cap, block=wl.block, quant=wl.quant, scale_dtype=wl.scale_dtype,
+                         in_dtype=wl.in_dtype, rotation=wl.rotation, eps=wl.eps, rot_params=p32,
+                         device=dev)
+    if args.splits:
+        cache.set_splits(args.splits)
+
+    # ---- prefill (timed separately: okv_write tokens/s)
+    k, v = okv_synth.kv_tokens(wl, 0, T0, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cache.write(k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    del k, v
+    torch.cuda.empty_cache()
+    print(f"# prefill {T0} tokens x {wl.batch} seq: {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    # ---- decode steps: inputs resident before timing
+    steps = W + K
+    news = [okv_synth.kv_tokens(wl, T0 + i, 1, device=dev, step=i) for i in range(steps)]
+    qs = [okv_synth.queries(wl, i, device=dev) for i in range(steps)]
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    for i in range(W):
+        cache.write(*news[i])
+        cache.decode_attn(qs[i], out)
+    torch.cuda.synchronize()
+    splits = cache.splits()
+    cache.timing(True)
+    ts, te = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts.record()
+    for i in range(W, steps):
+        cache.write(*news[i])
+        cache.decode_attn(qs[i], out)
+    te.record()
+    torch.cuda.synchronize()
+    step_ms_total = ts.elapsed_time(te)
+    ncalls, attn_ms, red_ms = cache.timing_read()
+    cache.timing(False)
+    assert ncalls == K, (ncalls, K)
+    assert torch.isfinite(out).all()
+
+    lens = [T0 + i + 1 for i in range(W, steps)]
+    tot_bytes = sum(sum(algorithmic_decode_bytes(wl, t)) for t in lens)
+    value = tot_bytes / (step_ms_total * 1e-3) / 1e9
+    kern_bytes = sum(algorithmic_decode_bytes(wl, t)[0] + algorithmic_decode_bytes(wl, t)[1] for t in lens)
+    achieved = kern_bytes / (attn_ms * 1e-3) / 1e9
+    write_tok_s = wl.batch * T0 / (prefill_ms * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(step_ms_total / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.hq, "kv_heads": wl.hkv,
+                   "head_dim": wl.d, "context": T0, "quant": wl.quant, "block": wl.block,
+                   "scale_dtype": wl.scale_dtype, "rotation": wl.rotation, "splits": splits},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_kernel_us": round(1e3 * attn_ms / K, 2),
+        "reduce_kernel_us": round(1e3 * red_ms / K, 2),
+        "write_tokens_per_s": round(write_tok_s, 1),
+        "write_prefill_ms": round(prefill_ms, 3),
+        "write_prefill_GBs": round(write_bytes_per_position(wl) * T0 / (prefill_ms * 1e-3) / 1e9, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    cache.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

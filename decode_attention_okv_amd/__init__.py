@@ -1,0 +1,303 @@
+"""Python binding of libokv (Hadamard-rotated 3-bit KV cache for MI355X).
+
+Argument marshalling only: every step of the write and read paths runs in the
+HIP kernels of ``libokv.so``.  PyTorch provides device memory and streams.
+
+The module-level functions carry the names of the C entry points
+(``okv_create``, ``okv_write``, ``okv_decode_attn``, ``okv_destroy`` and the
+auxiliary calls); :class:`OkvCache` owns the four cache tensors and a handle.
+
+Importing this package fails loudly when ``libokv.so`` has not been built
+(``python -m decode_attention_okv_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "OKV_OK", "OKV_E_INVALID", "OKV_E_ALIGN", "OKV_E_CAPACITY", "OKV_E_UNSUPPORTED", "OKV_E_HIP",
+    "OkvError", "OkvConfig", "OkvLayout", "lib", "LIB_PATH", "EXPORTS",
+    "okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror", "okv_layout",
+    "okv_get_len", "okv_set_len", "okv_set_splits", "okv_get_splits", "okv_max_splits",
+    "okv_timing_enable", "okv_timing_read", "make_config", "OkvCache",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libokv.so")
+
+OKV_ABI_VERSION = 1
+OKV_OK, OKV_E_INVALID, OKV_E_ALIGN, OKV_E_CAPACITY, OKV_E_UNSUPPORTED, OKV_E_HIP = range(6)
+QUANT = {"sym": 0, "asym": 1}
+DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+ROTATION = {"sign": 0, "so4": 1}
+
+EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror",
+           "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
+           "okv_get_splits", "okv_timing_enable", "okv_timing_read")
+
+
+class OkvConfig(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("quant", ctypes.c_int32),
+        ("scale_dtype", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("rotation", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("rot_params", ctypes.POINTER(ctypes.c_float)),
+        ("k_codes", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("k_meta", ctypes.c_void_p),
+        ("v_meta", ctypes.c_void_p),
+    ]
+
+
+class OkvLayout(ctypes.Structure):
+    _fields_ = [("k_codes_bytes", ctypes.c_uint64), ("v_codes_bytes", ctypes.c_uint64),
+                ("k_meta_bytes", ctypes.c_uint64), ("v_meta_bytes", ctypes.c_uint64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m decode_attention_okv_amd.build`")
+    so = ctypes.CDLL(LIB_PATH)
+    vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
+    sig = {
+        "okv_create": (i32, [P(OkvConfig), P(vp)]),
+        "okv_write": (i32, [vp, vp, vp, i32, vp]),
+        "okv_decode_attn": (i32, [vp, vp, vp, vp]),
+        "okv_destroy": (i32, [vp]),
+        "okv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "okv_layout": (i32, [P(OkvConfig), P(OkvLayout)]),
+        "okv_get_len": (i32, [vp, P(i32)]),
+        "okv_set_len": (i32, [vp, i32]),
+        "okv_set_splits": (i32, [vp, i32]),
+        "okv_max_splits": (i32, [vp, P(i32)]),
+        "okv_get_splits": (i32, [vp, P(i32)]),
+        "okv_timing_enable": (i32, [vp, i32]),
+        "okv_timing_read": (i32, [vp, P(i32), P(ctypes.c_double), P(ctypes.c_double)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(so, name)
+        fn.restype = res
+        fn.argtypes = args
+    return so
+
+
+lib = _load()
+
+
+class OkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.okv_strerror(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != OKV_OK:
+        raise OkvError(status, where)
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+# ---- C entry points with the C names (status codes are returned, not raised) ----
+
+def okv_strerror(status: int) -> str:
+    return lib.okv_strerror(status).decode()
+
+
+def okv_layout(cfg: OkvConfig):
+    info = OkvLayout()
+    st = lib.okv_layout(ctypes.byref(cfg), ctypes.byref(info))
+    return st, info
+
+
+def okv_create(cfg: OkvConfig):
+    h = ctypes.c_void_p()
+    st = lib.okv_create(ctypes.byref(cfg), ctypes.byref(h))
+    return st, h
+
+
+def okv_write(h, k_ptr: int, v_ptr: int, n_new: int, stream=None) -> int:
+    return lib.okv_write(h, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), n_new, _stream_ptr(stream))
+
+
+def okv_decode_attn(h, q_ptr: int, out_ptr: int, stream=None) -> int:
+    return lib.okv_decode_attn(h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(out_ptr), _stream_ptr(stream))
+
+
+def okv_destroy(h) -> int:
+    return lib.okv_destroy(h)
+
+
+def okv_get_len(h):
+    n = ctypes.c_int32()
+    return lib.okv_get_len(h, ctypes.byref(n)), n.value
+
+
+def okv_set_len(h, n: int) -> int:
+    return lib.okv_set_len(h, n)
+
+
+def okv_set_splits(h, n: int) -> int:
+    return lib.okv_set_splits(h, n)
+
+
+def okv_get_splits(h):
+    n = ctypes.c_int32()
+    return lib.okv_get_splits(h, ctypes.byref(n)), n.value
+
+
+def okv_max_splits(h):
+    n = ctypes.c_int32()
+    return lib.okv_max_splits(h, ctypes.byref(n)), n.value
+
+
+def okv_timing_enable(h, on: bool) -> int:
+    return lib.okv_timing_enable(h, 1 if on else 0)
+
+
+def okv_timing_read(h):
+    n, a, r = ctypes.c_int32(), ctypes.c_double(), ctypes.c_double()
+    st = lib.okv_timing_read(h, ctypes.byref(n), ctypes.byref(a), ctypes.byref(r))
+    return st, n.value, a.value, r.value
+
+
+def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block=32,
+                quant="sym", scale_dtype="f16", in_dtype="bf16", rotation="sign", eps=1e-6,
+                rot_params=None, k_codes=0, v_codes=0, k_meta=0, v_meta=0):
+    """Fill an OkvConfig; ``rot_params`` is a float32 sequence (kept alive on the
+    returned object until okv_create copies it)."""
+    import array
+    cfg = OkvConfig()
+    cfg.abi_version = OKV_ABI_VERSION
+    cfg.batch, cfg.num_q_heads, cfg.num_kv_heads = batch, num_q_heads, num_kv_heads
+    cfg.head_dim, cfg.max_tokens, cfg.block = head_dim, max_tokens, block
+    cfg.quant = QUANT[quant] if isinstance(quant, str) else quant
+    cfg.scale_dtype = DTYPE[scale_dtype] if isinstance(scale_dtype, str) else scale_dtype
+    cfg.in_dtype = DTYPE[in_dtype] if isinstance(in_dtype, str) else in_dtype
+    cfg.rotation = ROTATION[rotation] if isinstance(rotation, str) else rotation
+    cfg.eps = eps
+    if rot_params is not None:
+        buf = array.array("f", [float(x) for x in rot_params])
+        cfg._rot_buf = buf  # keep alive
+        addr, _ = buf.buffer_info()
+        cfg.rot_params = ctypes.cast(ctypes.c_void_p(addr), ctypes.POINTER(ctypes.c_float))
+    cfg.k_codes, cfg.v_codes, cfg.k_meta, cfg.v_meta = k_codes, v_codes, k_meta, v_meta
+    return cfg
+
+
+class OkvCache:
+    """A rotated 3-bit KV cache on one GPU: four caller-side tensors plus a handle.
+
+    Shapes follow include/okv.h.  ``rot_params`` is the float32 sign vector (d) or
+    the (d/4, 4, 4) SO(4) matrices.
+    """
+
+    def __init__(self, *, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block=32,
+                 quant="sym", scale_dtype="f16", in_dtype="bf16", rotation="sign", eps=1e-6,
+                 rot_params=None, device="cuda"):
+        import numpy as np
+        import torch
+        self.batch, self.hq, self.hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
+        self.max_tokens, self.block, self.quant, self.scale_dtype = max_tokens, block, quant, scale_dtype
+        self.in_dtype = in_dtype
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        rp = np.asarray(rot_params, dtype=np.float32).ravel()
+        cfg = make_config(batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                          head_dim=head_dim, max_tokens=max_tokens, block=block, quant=quant,
+                          scale_dtype=scale_dtype, in_dtype=in_dtype, rotation=rotation, eps=eps,
+                          rot_params=rp)
+        st, lay = okv_layout(cfg)
+        _check(st, "okv_layout")
+        nb = head_dim // block
+        shp = (batch, num_kv_heads, max_tokens)
+        self.k_codes = torch.empty(shp + (3 * head_dim // 8,), dtype=torch.uint8, device=self.device)
+        self.v_codes = torch.empty((batch, num_kv_heads, max_tokens // 32, head_dim, 12),
+                                   dtype=torch.uint8, device=self.device)
+        if quant == "asym":
+            meta_shape, meta_dtype = shp + (nb, 2), torch.uint8
+        else:
+            meta_shape, meta_dtype = shp + (nb,), (torch.float32 if scale_dtype == "f32" else torch.float16)
+        self.k_meta = torch.empty(meta_shape, dtype=meta_dtype, device=self.device)
+        self.v_meta = torch.empty(meta_shape, dtype=meta_dtype, device=self.device)
+        for t, n in ((self.k_codes, lay.k_codes_bytes), (self.v_codes, lay.v_codes_bytes),
+                     (self.k_meta, lay.k_meta_bytes), (self.v_meta, lay.v_meta_bytes)):
+            assert t.numel() * t.element_size() == n
+        cfg.k_codes, cfg.v_codes = self.k_codes.data_ptr(), self.v_codes.data_ptr()
+        cfg.k_meta, cfg.v_meta = self.k_meta.data_ptr(), self.v_meta.data_ptr()
+        with torch.cuda.device(self.device):
+            st, self.handle = okv_create(cfg)
+        _check(st, "okv_create")
+
+    def _in_check(self, t, shape):
+        import torch
+        want = torch.float32 if self.in_dtype == "f32" else torch.bfloat16
+        if t.dtype != want or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != self.device:
+            raise ValueError(f"expected contiguous {want} {tuple(shape)} on {self.device}, "
+                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+    def write(self, k, v, stream=None):
+        n_new = k.shape[1]
+        shape = (self.batch, n_new, self.hkv, self.d)
+        self._in_check(k, shape)
+        self._in_check(v, shape)
+        _check(okv_write(self.handle, k.data_ptr(), v.data_ptr(), n_new, stream), "okv_write")
+
+    def decode_attn(self, q, out=None, stream=None):
+        import torch
+        self._in_check(q, (self.batch, self.hq, self.d))
+        if out is None:
+            out = torch.empty((self.batch, self.hq, self.d), dtype=torch.float32, device=self.device)
+        _check(okv_decode_attn(self.handle, q.data_ptr(), out.data_ptr(), stream), "okv_decode_attn")
+        return out
+
+    @property
+    def length(self) -> int:
+        st, n = okv_get_len(self.handle)
+        _check(st, "okv_get_len")
+        return n
+
+    def set_length(self, n: int) -> None:
+        _check(okv_set_len(self.handle, n), "okv_set_len")
+
+    def set_splits(self, n: int) -> None:
+        _check(okv_set_splits(self.handle, n), "okv_set_splits")
+
+    def splits(self) -> int:
+        st, n = okv_get_splits(self.handle)
+        _check(st, "okv_get_splits")
+        return n
+
+    def timing(self, on: bool) -> None:
+        _check(okv_timing_enable(self.handle, on), "okv_timing_enable")
+
+    def timing_read(self):
+        st, n, a, r = okv_timing_read(self.handle)
+        _check(st, "okv_timing_read")
+        return n, a, r
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            okv_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

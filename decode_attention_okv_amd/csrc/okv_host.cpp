@@ -1,0 +1,355 @@
+// Host runtime of libokv: argument validation, cache layout arithmetic, device
+// copies of the rotation parameters, the split-K workspace and kernel launches.
+// Implements include/okv.h.
+#include "okv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "okv_kernels.hpp"
+
+namespace {
+
+constexpr int kMaxSplits = 256;      // split-K workspace capacity per (sequence, query head)
+constexpr int kTargetGroups = 4096;  // workgroups the automatic split count aims for
+constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int meta_entry_bytes(const okv_config& c) {
+  if (c.quant == OKV_QUANT_ASYM3) return 2;           // E4M3 scale + zero-point
+  return c.scale_dtype == OKV_DT_F32 ? 4 : 2;
+}
+
+// Shape / enum checks shared by okv_layout and okv_create.
+int validate_shape(const okv_config* c) {
+  if (c == nullptr) return OKV_E_INVALID;
+  if (c->abi_version != OKV_ABI_VERSION) return OKV_E_INVALID;
+  if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1) return OKV_E_INVALID;
+  if (c->num_q_heads % c->num_kv_heads != 0) return OKV_E_INVALID;
+  if (!is_pow2(c->head_dim) || c->head_dim % 4 != 0) return OKV_E_INVALID;
+  if (c->block < 8 || c->block % 8 != 0 || c->head_dim % c->block != 0) return OKV_E_INVALID;
+  if (c->max_tokens < 1 || c->max_tokens % 32 != 0) return OKV_E_INVALID;
+  if (c->quant != OKV_QUANT_SYM3 && c->quant != OKV_QUANT_ASYM3) return OKV_E_INVALID;
+  if (c->in_dtype != OKV_DT_F32 && c->in_dtype != OKV_DT_BF16) return OKV_E_INVALID;
+  if (c->rotation != OKV_ROT_SIGN && c->rotation != OKV_ROT_SO4) return OKV_E_INVALID;
+  if (c->quant == OKV_QUANT_SYM3) {
+    if (c->scale_dtype != OKV_DT_F32 && c->scale_dtype != OKV_DT_F16) {
+      return c->scale_dtype == OKV_DT_E4M3 ? OKV_E_UNSUPPORTED : OKV_E_INVALID;
+    }
+    if (!std::isfinite(c->eps) || c->eps < 0.0f) return OKV_E_INVALID;
+  } else {
+    if (c->scale_dtype != OKV_DT_E4M3) {
+      return (c->scale_dtype == OKV_DT_F32 || c->scale_dtype == OKV_DT_F16) ? OKV_E_UNSUPPORTED
+                                                                            : OKV_E_INVALID;
+    }
+  }
+  // valid, but only these are built
+  if (c->head_dim != 128 && c->head_dim != 256) return OKV_E_UNSUPPORTED;
+  if (c->block % 32 != 0) return OKV_E_UNSUPPORTED;
+  // index arithmetic in the kernels uses 32-bit token counts
+  if (static_cast<int64_t>(c->max_tokens) * c->head_dim > (int64_t{1} << 40)) return OKV_E_UNSUPPORTED;
+  return OKV_OK;
+}
+
+void layout_of(const okv_config& c, okv_layout_info* li) {
+  const uint64_t units = static_cast<uint64_t>(c.batch) * c.num_kv_heads;
+  const uint64_t rows = units * static_cast<uint64_t>(c.max_tokens);
+  li->k_codes_bytes = rows * (3u * c.head_dim / 8);
+  li->v_codes_bytes = rows * (3u * c.head_dim / 8);
+  li->k_meta_bytes = rows * static_cast<uint64_t>(c.head_dim / c.block) * meta_entry_bytes(c);
+  li->v_meta_bytes = li->k_meta_bytes;
+}
+
+struct TimingSlot {
+  hipEvent_t e0, e1, e2;
+};
+
+}  // namespace
+
+struct okv_handle {
+  okv_config cfg;
+  int device = 0;
+  float* d_rot = nullptr;
+  float* d_ws = nullptr;
+  int32_t len = 0;
+  int32_t splits = 0;  // 0 = automatic
+  bool timing = false;
+  std::vector<TimingSlot> slots;
+  int recorded = 0;
+};
+
+namespace {
+
+int choose_splits(const okv_handle* h, int32_t T) {
+  const int ntiles = (T + okv::kTile - 1) / okv::kTile;
+  int s = h->splits;
+  if (s <= 0) {
+    const int units = h->cfg.batch * h->cfg.num_q_heads;
+    s = (kTargetGroups + units - 1) / units;
+  }
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > ntiles) s = ntiles;
+  if (s < 1) s = 1;
+  // no empty split: recompute the count from the tiles each split gets
+  const int tps = (ntiles + s - 1) / s;
+  return (ntiles + tps - 1) / tps;
+}
+
+void free_timing(okv_handle* h) {
+  for (auto& t : h->slots) {
+    (void)hipEventDestroy(t.e0);
+    (void)hipEventDestroy(t.e1);
+    (void)hipEventDestroy(t.e2);
+  }
+  h->slots.clear();
+  h->recorded = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* okv_strerror(int status) {
+  switch (status) {
+    case OKV_OK: return "ok";
+    case OKV_E_INVALID: return "invalid argument or configuration";
+    case OKV_E_ALIGN: return "pointer not 16-byte aligned";
+    case OKV_E_CAPACITY: return "cache capacity exceeded";
+    case OKV_E_UNSUPPORTED: return "configuration not supported by this build";
+    case OKV_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int okv_layout(const okv_config* cfg, okv_layout_info* info) {
+  if (info == nullptr) return OKV_E_INVALID;
+  const int st = validate_shape(cfg);
+  if (st != OKV_OK) return st;
+  layout_of(*cfg, info);
+  return OKV_OK;
+}
+
+int okv_create(const okv_config* cfg, okv_handle** out) {
+  if (out == nullptr) return OKV_E_INVALID;
+  *out = nullptr;
+  int st = validate_shape(cfg);
+  if (st != OKV_OK) return st;
+  if (cfg->rot_params == nullptr) return OKV_E_INVALID;
+  if (!cfg->k_codes || !cfg->v_codes || !cfg->k_meta || !cfg->v_meta) return OKV_E_INVALID;
+  if (!aligned16(cfg->k_codes) || !aligned16(cfg->v_codes) || !aligned16(cfg->k_meta) ||
+      !aligned16(cfg->v_meta)) {
+    return OKV_E_ALIGN;
+  }
+  const int d = cfg->head_dim;
+  const size_t nrot = cfg->rotation == OKV_ROT_SIGN ? static_cast<size_t>(d) : static_cast<size_t>(4) * d;
+  const float* rp = cfg->rot_params;
+  if (cfg->rotation == OKV_ROT_SIGN) {
+    for (int i = 0; i < d; ++i) {
+      if (rp[i] != 1.0f && rp[i] != -1.0f) return OKV_E_INVALID;
+    }
+  } else {
+    for (int r = 0; r < d / 4; ++r) {
+      const float* R = rp + 16 * r;
+      for (int a = 0; a < 4; ++a) {
+        for (int c = 0; c < 4; ++c) {
+          double dot = 0.0;
+          for (int k = 0; k < 4; ++k) dot += static_cast<double>(R[4 * k + a]) * R[4 * k + c];
+          if (!(std::fabs(dot - (a == c ? 1.0 : 0.0)) <= 1e-3)) return OKV_E_INVALID;
+        }
+      }
+    }
+  }
+
+  okv_handle* h = new (std::nothrow) okv_handle();
+  if (h == nullptr) return OKV_E_HIP;
+  h->cfg = *cfg;
+  h->cfg.rot_params = nullptr;  // the host copy is not kept
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return OKV_E_HIP;
+  }
+  const size_t ws_floats = static_cast<size_t>(cfg->batch) * cfg->num_q_heads * kMaxSplits * (d + 2);
+  if (hipMalloc(&h->d_rot, nrot * sizeof(float)) != hipSuccess ||
+      hipMemcpy(h->d_rot, rp, nrot * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMalloc(&h->d_ws, ws_floats * sizeof(float)) != hipSuccess) {
+    if (h->d_rot) (void)hipFree(h->d_rot);
+    if (h->d_ws) (void)hipFree(h->d_ws);
+    delete h;
+    return OKV_E_HIP;
+  }
+  *out = h;
+  return OKV_OK;
+}
+
+int okv_destroy(okv_handle* h) {
+  if (h == nullptr) return OKV_OK;
+  int st = OKV_OK;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->device);
+  free_timing(h);
+  if (h->d_rot && hipFree(h->d_rot) != hipSuccess) st = OKV_E_HIP;
+  if (h->d_ws && hipFree(h->d_ws) != hipSuccess) st = OKV_E_HIP;
+  (void)hipSetDevice(prev);
+  delete h;
+  return st;
+}
+
+int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* hip_stream) {
+  if (h == nullptr || k == nullptr || v == nullptr) return OKV_E_INVALID;
+  if (n_new < 1) return OKV_E_INVALID;
+  if (!aligned16(k) || !aligned16(v)) return OKV_E_ALIGN;
+  const okv_config& c = h->cfg;
+  if (static_cast<int64_t>(h->len) + n_new > c.max_tokens) return OKV_E_CAPACITY;
+  okv::WriteParams p{};
+  p.k = k;
+  p.v = v;
+  p.k_codes = static_cast<uint8_t*>(c.k_codes);
+  p.v_codes = static_cast<uint8_t*>(c.v_codes);
+  p.k_meta = c.k_meta;
+  p.v_meta = c.v_meta;
+  p.rot = h->d_rot;
+  p.n_new = n_new;
+  p.len = h->len;
+  p.hkv = c.num_kv_heads;
+  p.tcap = c.max_tokens;
+  p.ntile_cap = c.max_tokens / okv::kTile;
+  p.tile0 = h->len / okv::kTile;
+  p.block = c.block;
+  p.quant = c.quant;
+  p.scale_dtype = c.scale_dtype;
+  p.rotation = c.rotation;
+  p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  p.eps = c.eps;
+  const int tile1 = (h->len + n_new - 1) / okv::kTile;
+  const int ntiles = tile1 - p.tile0 + 1;
+  if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
+  if (okv::launch_write(p, ntiles, c.batch, c.head_dim, static_cast<hipStream_t>(hip_stream)) != hipSuccess) {
+    return OKV_E_HIP;
+  }
+  h->len += n_new;
+  return OKV_OK;
+}
+
+int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) {
+  if (h == nullptr || q == nullptr || out == nullptr) return OKV_E_INVALID;
+  if (!aligned16(q) || !aligned16(out)) return OKV_E_ALIGN;
+  if (h->len < 1) return OKV_E_INVALID;
+  const okv_config& c = h->cfg;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int nsplit = choose_splits(h, h->len);
+  okv::DecodeParams p{};
+  p.k_codes = static_cast<const uint8_t*>(c.k_codes);
+  p.v_codes = static_cast<const uint8_t*>(c.v_codes);
+  p.k_meta = c.k_meta;
+  p.v_meta = c.v_meta;
+  p.q = q;
+  p.rot = h->d_rot;
+  p.ws = h->d_ws;
+  p.hq = c.num_q_heads;
+  p.hkv = c.num_kv_heads;
+  p.tcap = c.max_tokens;
+  p.ntile_cap = c.max_tokens / okv::kTile;
+  p.T = h->len;
+  const int ntiles = (h->len + okv::kTile - 1) / okv::kTile;
+  p.tiles_per_split = (ntiles + nsplit - 1) / nsplit;
+  p.nsplit = nsplit;
+  p.block = c.block;
+  p.quant = c.quant;
+  p.scale_dtype = c.scale_dtype;
+  p.rotation = c.rotation;
+  p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  okv::ReduceParams r{};
+  r.ws = h->d_ws;
+  r.rot = h->d_rot;
+  r.out = out;
+  r.hq = c.num_q_heads;
+  r.nsplit = nsplit;
+  r.rotation = c.rotation;
+  if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
+  TimingSlot* ts = nullptr;
+  if (h->timing && h->recorded < static_cast<int>(h->slots.size())) ts = &h->slots[h->recorded++];
+  if (ts && hipEventRecord(ts->e0, s) != hipSuccess) return OKV_E_HIP;
+  if (okv::launch_decode(p, c.batch, c.head_dim, s) != hipSuccess) return OKV_E_HIP;
+  if (ts && hipEventRecord(ts->e1, s) != hipSuccess) return OKV_E_HIP;
+  if (okv::launch_reduce(r, c.batch, c.head_dim, s) != hipSuccess) return OKV_E_HIP;
+  if (ts && hipEventRecord(ts->e2, s) != hipSuccess) return OKV_E_HIP;
+  return OKV_OK;
+}
+
+int okv_get_len(const okv_handle* h, int32_t* len) {
+  if (h == nullptr || len == nullptr) return OKV_E_INVALID;
+  *len = h->len;
+  return OKV_OK;
+}
+
+int okv_set_len(okv_handle* h, int32_t len) {
+  if (h == nullptr || len < 0 || len > h->cfg.max_tokens) return OKV_E_INVALID;
+  h->len = len;
+  return OKV_OK;
+}
+
+int okv_set_splits(okv_handle* h, int32_t num_splits) {
+  if (h == nullptr || num_splits < 0 || num_splits > kMaxSplits) return OKV_E_INVALID;
+  h->splits = num_splits;
+  return OKV_OK;
+}
+
+int okv_max_splits(const okv_handle* h, int32_t* n) {
+  if (h == nullptr || n == nullptr) return OKV_E_INVALID;
+  *n = kMaxSplits;
+  return OKV_OK;
+}
+
+int okv_get_splits(const okv_handle* h, int32_t* n) {
+  if (h == nullptr || n == nullptr) return OKV_E_INVALID;
+  *n = h->len > 0 ? choose_splits(h, h->len) : 0;
+  return OKV_OK;
+}
+
+int okv_timing_enable(okv_handle* h, int32_t enable) {
+  if (h == nullptr) return OKV_E_INVALID;
+  if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
+  if (enable && h->slots.empty()) {
+    h->slots.resize(kTimingSlots);
+    for (auto& t : h->slots) {
+      if (hipEventCreate(&t.e0) != hipSuccess || hipEventCreate(&t.e1) != hipSuccess ||
+          hipEventCreate(&t.e2) != hipSuccess) {
+        return OKV_E_HIP;
+      }
+    }
+  }
+  if (!enable) free_timing(h);
+  h->timing = enable != 0;
+  h->recorded = 0;
+  return OKV_OK;
+}
+
+int okv_timing_read(okv_handle* h, int32_t* calls, double* attn_ms, double* reduce_ms) {
+  if (h == nullptr || calls == nullptr || attn_ms == nullptr || reduce_ms == nullptr) return OKV_E_INVALID;
+  double a = 0.0, r = 0.0;
+  for (int i = 0; i < h->recorded; ++i) {
+    TimingSlot& t = h->slots[i];
+    float x = 0.0f, y = 0.0f;
+    if (hipEventSynchronize(t.e2) != hipSuccess) return OKV_E_HIP;
+    if (hipEventElapsedTime(&x, t.e0, t.e1) != hipSuccess) return OKV_E_HIP;
+    if (hipEventElapsedTime(&y, t.e1, t.e2) != hipSuccess) return OKV_E_HIP;
+    a += x;
+    r += y;
+  }
+  *calls = h->recorded;
+  *attn_ms = a;
+  *reduce_ms = r;
+  h->recorded = 0;
+  return OKV_OK;
+}
+
+}  // extern "C"

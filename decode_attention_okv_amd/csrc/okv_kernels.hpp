@@ -1,0 +1,53 @@
+// Internal interface between the host runtime (okv_host.cpp) and the HIP kernels.
+// Not installed; the public interface is include/okv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace okv {
+
+constexpr int kTile = 32;   // tokens per value tile
+constexpr int kGroup = 32;  // codes per 12-byte packed group
+
+enum : int { kQuantSym = 0, kQuantAsym = 1 };
+enum : int { kScaleF32 = 0, kScaleF16 = 1, kScaleE4M3 = 3 };
+enum : int { kRotSign = 0, kRotSo4 = 1 };
+
+struct WriteParams {
+  const void* k;         // [B][n_new][Hkv][D] input type
+  const void* v;
+  uint8_t* k_codes;      // [B][Hkv][tcap][3D/8]
+  uint8_t* v_codes;      // [B][Hkv][tcap/32][D][12]
+  void* k_meta;          // [B][Hkv][tcap][D/m] (x2 bytes for E4M3 pairs)
+  void* v_meta;
+  const float* rot;      // device: D signs or (D/4) 4x4 matrices
+  int n_new, len, hkv, tcap, ntile_cap, tile0;
+  int block, quant, scale_dtype, rotation, in_bf16;
+  float eps;
+};
+
+struct DecodeParams {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const void* k_meta;
+  const void* v_meta;
+  const void* q;         // [B][Hq][D] input type
+  const float* rot;
+  float* ws;             // [B][Hq][nsplit][D + 2]: acc[D], m (log2 units), l
+  int hq, hkv, tcap, ntile_cap, T, tiles_per_split, nsplit;
+  int block, quant, scale_dtype, rotation, in_bf16;
+};
+
+struct ReduceParams {
+  const float* ws;
+  const float* rot;
+  float* out;            // [B][Hq][D] float32
+  int hq, nsplit, rotation;
+};
+
+hipError_t launch_write(const WriteParams& p, int ntiles, int batch, int d, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s);
+
+}  // namespace okv

@@ -1,0 +1,186 @@
+/*
+ * okv -- Hadamard-rotated 3-bit KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library libokv.so.  Plain pointers and sizes only; every device
+ * pointer is memory the caller allocated on the GPU the handle lives on.
+ *
+ * The method (pages: "Orthogonally mixed 3-bit KV cache", Mathematical statement,
+ * Key formulas and Implementation notes; "Orthogonal Invariance in Activation
+ * Space: Fast Walsh-Hadamard Transforms for KV Quantization", Sections 2.3, 3.1-3.4
+ * and 4.3; "Hardware-Fused Fast Hadamard Transforms Enable Lossless 3-Bit KV-Cache
+ * Compression at 128K Context Without Perplexity Drift", third paragraph):
+ *
+ *   write:  k1 = U k, v1 = U v; one scale per block of m values; 3-bit codes;
+ *           8 codes in 3 bytes; only codes and scales are stored.
+ *   decode: q1 = U q; logits from q1 and the dequantised rotated keys, unpacked
+ *           and scaled inside the dot product; softmax; weighted sum of the
+ *           dequantised rotated values; y = U^T y1.
+ *
+ *   U = H_d D  (OKV_ROT_SIGN: random signs D, then the normalised Walsh-Hadamard
+ *               transform H_d)  or  U = B H_d  (OKV_ROT_SO4: H_d, then the
+ *               block-diagonal SO(4) matrix B = diag(R_1 .. R_{d/4})).
+ *
+ * Quantisers (per block of m rotated values y):
+ *   OKV_QUANT_SYM3:  s = (max|y| + eps) / 3 rounded to float32 then to the scale
+ *                    type; c = clip(round_half_even(y / s), -3, 3); stored code
+ *                    u = c + 4 (0..7); y_hat = s (u - 4).
+ *   OKV_QUANT_ASYM3: s = (max - min) / 7, z = min, both stored as OCP FP8 E4M3
+ *                    (round-half-even, saturating at 448); u = clip(round_half_even(
+ *                    (y - z) / s), 0, 7); y_hat = s u + z.
+ * Every float32 step of the write path is rounded to nearest-even in a fixed order
+ * (butterfly stages of stride 1, 2, 4, ..., d/2, then one multiply by
+ * RN32(1/sqrt d); SO(4) rows as ((R0 x0 + R1 x1) + R2 x2) + R3 x3 without fused
+ * multiply-adds), so codes and scales are reproducible bit for bit.
+ *
+ * Packing: 32 codes e[0..31] form a 12-byte group of three little-endian 32-bit
+ * words W0 W1 W2.  For k = 0,1,2 and byte b = 0..3: bits 0-2 of byte b of W_k hold
+ * e[8k+b] and bits 3-5 hold e[8k+4+b].  Bits 6-7 of byte b of W0 hold the low two
+ * bits of e[24+b], bits 6-7 of byte b of W1 the low two bits of e[28+b]; bit 6 of
+ * byte b of W2 holds bit 2 of e[24+b] and bit 7 holds bit 2 of e[28+b].
+ *
+ * Cache layouts (caller-owned device buffers, row-major, contiguous):
+ *   k_codes  uint8 [batch][num_kv_heads][max_tokens][3*head_dim/8]
+ *            token-major rows; dims 32g..32g+31 are group g (bytes 12g..12g+11).
+ *   v_codes  uint8 [batch][num_kv_heads][max_tokens/32][head_dim][12]
+ *            32-token tiles; in tile t, dim j is one group holding the codes of
+ *            tokens 32t .. 32t+31 (token 32t+i is code i).  Token slots of a
+ *            tile that are not yet written hold code 0.
+ *   k_meta, v_meta  [batch][num_kv_heads][max_tokens][head_dim/block] of the
+ *            scale type (float32 or IEEE half) for OKV_QUANT_SYM3, and
+ *            uint8 [batch][num_kv_heads][max_tokens][head_dim/block][2] holding the
+ *            E4M3 (scale, zero-point) pair for OKV_QUANT_ASYM3.
+ *   k, v     [batch][n_new][num_kv_heads][head_dim] in the input type.
+ *   q        [batch][num_q_heads][head_dim] in the input type.
+ *   out      float32 [batch][num_q_heads][head_dim].
+ *   Query head j attends with key/value head j / (num_q_heads / num_kv_heads).
+ *
+ * Ownership: the caller owns every tensor buffer (cache, inputs, outputs) and
+ * keeps the cache buffers alive until okv_destroy.  The handle owns a device copy
+ * of the rotation parameters, the split-K workspace and the host-side sequence
+ * length (uniform over the batch).
+ *
+ * Errors: every call returns an okv_status.  Arguments are checked before any
+ * GPU work is queued; on error nothing is launched and no state changes.  No C++
+ * exception crosses this interface.  Calls do not synchronise; they queue work on
+ * the given HIP stream (NULL = the default stream).  A handle must be used from
+ * one stream at a time.
+ */
+#ifndef OKV_H
+#define OKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OKV_ABI_VERSION 1
+
+typedef enum okv_status {
+  OKV_OK = 0,
+  OKV_E_INVALID = 1,      /* bad configuration or argument */
+  OKV_E_ALIGN = 2,        /* a pointer is not 16-byte aligned */
+  OKV_E_CAPACITY = 3,     /* len + n_new > max_tokens */
+  OKV_E_UNSUPPORTED = 4,  /* a valid combination this build does not implement */
+  OKV_E_HIP = 5           /* HIP runtime or launch error */
+} okv_status;
+
+typedef enum okv_quant { OKV_QUANT_SYM3 = 0, OKV_QUANT_ASYM3 = 1 } okv_quant;
+
+typedef enum okv_dtype {
+  OKV_DT_F32 = 0,
+  OKV_DT_F16 = 1,
+  OKV_DT_BF16 = 2,
+  OKV_DT_E4M3 = 3
+} okv_dtype;
+
+typedef enum okv_rotation { OKV_ROT_SIGN = 0, OKV_ROT_SO4 = 1 } okv_rotation;
+
+typedef struct okv_config {
+  int32_t abi_version;   /* must be OKV_ABI_VERSION */
+  int32_t batch;         /* sequences, >= 1 */
+  int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* >= 1 */
+  int32_t head_dim;      /* d: power of two, 4 | d; this build: 128 or 256 */
+  int32_t max_tokens;    /* cache capacity per sequence, multiple of 32 */
+  int32_t block;         /* quantisation block m: m | d, 8 | m; this build: 32 or 64 */
+  int32_t quant;         /* okv_quant */
+  int32_t scale_dtype;   /* OKV_DT_F32 or OKV_DT_F16 (SYM3); OKV_DT_E4M3 (ASYM3) */
+  int32_t in_dtype;      /* OKV_DT_F32 or OKV_DT_BF16: type of k, v and q */
+  int32_t rotation;      /* okv_rotation */
+  float eps;             /* SYM3 scale offset, finite, >= 0 (1e-6 is usual) */
+  /* Host pointer, copied at okv_create.  OKV_ROT_SIGN: head_dim values, each +1
+   * or -1 (the diagonal of D).  OKV_ROT_SO4: (head_dim/4) row-major 4x4 float32
+   * matrices R_i (rotation matrices: R^T R = I within 1e-3). */
+  const float* rot_params;
+  /* Caller-owned device buffers (layouts above), 16-byte aligned. */
+  void* k_codes;
+  void* v_codes;
+  void* k_meta;
+  void* v_meta;
+} okv_config;
+
+typedef struct okv_handle okv_handle;
+
+/* Sizes in bytes of the four cache buffers a configuration needs (shape fields,
+ * quant, scale_dtype are read; the pointers are not).  Returns OKV_E_INVALID or
+ * OKV_E_UNSUPPORTED for configurations okv_create would reject. */
+typedef struct okv_layout_info {
+  uint64_t k_codes_bytes;
+  uint64_t v_codes_bytes;
+  uint64_t k_meta_bytes;
+  uint64_t v_meta_bytes;
+} okv_layout_info;
+
+/* Validate cfg (host only, no GPU touched on failure), copy the rotation
+ * parameters to the current device, allocate the split-K workspace there and
+ * return a handle with sequence length 0.  The current HIP device at this call is
+ * the device of the handle. */
+int okv_create(const okv_config* cfg, okv_handle** out);
+
+/* Append n_new tokens to every sequence: rotate k and v with U, quantise, pack,
+ * and store codes and scales at positions len .. len+n_new-1 (the idea card,
+ * Implementation notes: "On every new token compute k1 = U(k) and v1 = U(v) ...
+ * store only packed codes and scales").  k, v: device, [batch][n_new][kv][d] in
+ * the input type, 16-byte aligned.  Asynchronous on hip_stream; len advances by
+ * n_new at once (host side). */
+int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* hip_stream);
+
+/* One decode step: for every (sequence, query head) attend over all len cached
+ * tokens and write the float32 output (the idea card, Implementation notes: read
+ * path).  q: device [batch][num_q_heads][d] in the input type; out: device
+ * float32 [batch][num_q_heads][d]; both 16-byte aligned.  OKV_E_INVALID when the
+ * cache is empty.  Asynchronous on hip_stream. */
+int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream);
+
+/* Free the handle's device memory (not the caller's buffers).  NULL is OK. */
+int okv_destroy(okv_handle* h);
+
+/* ---- auxiliary calls (not part of the method) ---- */
+
+const char* okv_strerror(int status);
+int okv_layout(const okv_config* cfg, okv_layout_info* info);
+/* Current sequence length of the handle. */
+int okv_get_len(const okv_handle* h, int32_t* len);
+/* Set the sequence length to 0..max_tokens (e.g. 0 to reuse the buffers); the
+ * cache contents below the new length are taken as written. */
+int okv_set_len(okv_handle* h, int32_t len);
+/* Split-K count of okv_decode_attn: 0 chooses automatically (default), otherwise
+ * 1 .. okv_max_splits. */
+int okv_set_splits(okv_handle* h, int32_t num_splits);
+int okv_max_splits(const okv_handle* h, int32_t* n);
+/* Split count the next okv_decode_attn call will use at the current length. */
+int okv_get_splits(const okv_handle* h, int32_t* n);
+/* Kernel timing: when enabled, okv_decode_attn records HIP events on its stream
+ * around its attention kernel and its reduce kernel.  okv_timing_read waits for the
+ * recorded calls, returns how many were recorded since the last read and the
+ * summed kernel milliseconds, then clears the record. */
+int okv_timing_enable(okv_handle* h, int32_t enable);
+int okv_timing_read(okv_handle* h, int32_t* calls, double* attn_ms, double* reduce_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OKV_H */

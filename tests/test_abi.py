@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports what include/okv.h declares and rejects bad
+arguments on the host (CPU only: no call here reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_okv_amd as okv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "okv.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(okv_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert {"okv_create", "okv_write", "okv_decode_attn", "okv_destroy"} <= set(names)
+    for n in names:
+        assert hasattr(okv.lib, n), n
+    assert set(names) == set(okv.EXPORTS)
+
+
+def base(**kw):
+    args = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=1024, block=32,
+                quant="sym", scale_dtype="f16", in_dtype="bf16", rotation="sign",
+                rot_params=[1.0] * 128, k_codes=4096, v_codes=8192, k_meta=16384, v_meta=32768)
+    args.update(kw)
+    return okv.make_config(**args)
+
+
+def test_layout_sizes():
+    st, lay = okv.okv_layout(base())
+    assert st == okv.OKV_OK
+    rows = 2 * 2 * 1024
+    assert lay.k_codes_bytes == rows * 48 and lay.v_codes_bytes == rows * 48
+    assert lay.k_meta_bytes == rows * 4 * 2
+    st, lay = okv.okv_layout(base(quant="asym", scale_dtype="e4m3", block=64))
+    assert st == okv.OKV_OK and lay.k_meta_bytes == rows * 2 * 2
+    st, lay = okv.okv_layout(base(scale_dtype="f32", head_dim=256, rot_params=[1.0] * 256))
+    assert st == okv.OKV_OK and lay.k_codes_bytes == rows * 96 and lay.k_meta_bytes == rows * 8 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(abi_version=99), okv.OKV_E_INVALID),
+    (dict(batch=0), okv.OKV_E_INVALID),
+    (dict(num_q_heads=7), okv.OKV_E_INVALID),            # Hq mod Hkv != 0
+    (dict(head_dim=96), okv.OKV_E_INVALID),              # not a power of two
+    (dict(block=24), okv.OKV_E_INVALID),                 # does not divide d
+    (dict(block=12), okv.OKV_E_INVALID),                 # 8 does not divide m
+    (dict(max_tokens=1000), okv.OKV_E_INVALID),          # not a multiple of 32
+    (dict(quant=5), okv.OKV_E_INVALID),
+    (dict(in_dtype="f16"), okv.OKV_E_INVALID),
+    (dict(rotation=3), okv.OKV_E_INVALID),
+    (dict(eps=-1.0), okv.OKV_E_INVALID),
+    (dict(eps=float("nan")), okv.OKV_E_INVALID),
+    (dict(scale_dtype="bf16"), okv.OKV_E_INVALID),
+    (dict(scale_dtype="e4m3"), okv.OKV_E_UNSUPPORTED),   # symmetric with FP8 scales: not built
+    (dict(quant="asym", scale_dtype="f16"), okv.OKV_E_UNSUPPORTED),
+    (dict(head_dim=64, rot_params=[1.0] * 64), okv.OKV_E_UNSUPPORTED),
+    (dict(block=16), okv.OKV_E_UNSUPPORTED),
+])
+def test_rejections(kw, status):
+    cfg = base(**{k: v for k, v in kw.items() if k != "abi_version"})
+    if "abi_version" in kw:
+        cfg.abi_version = kw["abi_version"]
+    assert okv.okv_layout(cfg)[0] == status
+    st, h = okv.okv_create(cfg)
+    assert st == status and not h.value
+
+
+def test_create_rejects_bad_pointers_and_params_before_gpu():
+    st, h = okv.okv_create(base(k_codes=0))
+    assert st == okv.OKV_E_INVALID
+    st, h = okv.okv_create(base(v_meta=32768 + 4))
+    assert st == okv.OKV_E_ALIGN
+    st, h = okv.okv_create(base(rot_params=[1.0] * 127 + [0.5]))
+    assert st == okv.OKV_E_INVALID                       # a sign that is not +-1
+    cfg = base()
+    cfg.rot_params = None
+    assert okv.okv_create(cfg)[0] == okv.OKV_E_INVALID
+    import numpy as np
+    bad = np.tile(np.eye(4, dtype=np.float32) * 2, (32, 1, 1)).ravel()
+    assert okv.okv_create(base(rotation="so4", rot_params=bad))[0] == okv.OKV_E_INVALID
+    assert okv.lib.okv_create(ctypes.byref(base()), None) == okv.OKV_E_INVALID
+
+
+def test_null_handle_calls():
+    null = ctypes.c_void_p()
+    assert okv.okv_destroy(null) == okv.OKV_OK
+    assert okv.okv_write(null, 16, 16, 1, 0) == okv.OKV_E_INVALID
+    assert okv.okv_decode_attn(null, 16, 16, 0) == okv.OKV_E_INVALID
+    assert okv.okv_get_len(null)[0] == okv.OKV_E_INVALID
+    assert okv.okv_set_splits(null, 4) == okv.OKV_E_INVALID
+    assert okv.okv_timing_read(null)[0] == okv.OKV_E_INVALID
+    assert okv.okv_strerror(okv.OKV_E_CAPACITY) == "cache capacity exceeded"

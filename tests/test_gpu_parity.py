@@ -1,0 +1,156 @@
+"""GPU parity of libokv against the CPU oracle at sizes the oracle finishes quickly.
+
+Codes, scales and zero-points: byte-exact.  Decode output: max |y - y_ref| <=
+2e-3 * RMS(y_ref) over each decode call.  Every call goes through the C ABI.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import okv_synth
+from okv_parity import (compare_unit, decode_ref_unit, exact_ties, free_gpu, make_cache, out_error,
+                        params_of, round_up, say, unit_inputs)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+REDUCED = {
+    # name: (overrides, token count, write chunks)
+    "tiny_d128_t256": (dict(), 256, [100, 1, 155]),
+    "gqa_h32kv8_t32k": (dict(), 1000, [1000]),
+    "mha_b4h32_t128k": (dict(batch=2, hq=8, hkv=8), 777, [500, 277]),
+    "gqa_b16h64kv8_t128k_asym": (dict(batch=2), 1500, [1500]),
+    "so4_d256_b32_t8k": (dict(batch=2), 600, [64, 536]),
+}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_case(wl, t, chunks, splits=0, steps=0):
+    """Write t tokens in `chunks`, decode, then `steps` x (append 1, decode).
+    Checks every unit's bytes and every decode output against the oracle."""
+    _need_gpu()
+    p32, u = params_of(wl)
+    cache = make_cache(wl, round_up(t + steps + 1, 32), p32)
+    if splits:
+        cache.set_splits(splits)
+    k, v = okv_synth.kv_tokens(wl, 0, t, device="cuda")
+    pos = 0
+    for n in chunks:
+        say(wl.name, "okv_write", pos, n)
+        cache.write(k[:, pos:pos + n].contiguous(), v[:, pos:pos + n].contiguous())
+        pos += n
+    assert pos == t and cache.length == t
+    errs = []
+    k_all, v_all = k, v
+    for step in range(steps + 1):
+        if step:
+            kn, vn = okv_synth.kv_tokens(wl, t + step - 1, 1, device="cuda", step=step)
+            say(wl.name, "okv_write append", t + step - 1)
+            cache.write(kn, vn)
+            k_all = torch.cat([k_all, kn], 1)
+            v_all = torch.cat([v_all, vn], 1)
+        tt = t + step
+        q = okv_synth.queries(wl, step, device="cuda")
+        say(wl.name, "okv_decode_attn", "T", tt, "splits", cache.splits())
+        out = cache.decode_attn(q)
+        torch.cuda.synchronize()
+        out_h = out.cpu().numpy()
+        q_h = okv_synth.host_f32(q)
+        y_ref = np.zeros_like(out_h, dtype=np.float64)
+        ties = 0
+        for b in range(wl.batch):
+            for h in range(wl.hkv):
+                kh, vh = unit_inputs(k_all, v_all, b, h)
+                import oracle
+                ref = oracle.write_unit(kh, vh, wl, p32)
+                if step == 0 or step == steps:
+                    mism = compare_unit(cache, wl, b, h, tt, ref)
+                    assert all(x == 0 for x in mism.values()), (b, h, mism)
+                    ties += exact_ties(ref, wl)
+                y_ref[b, h * wl.group:(h + 1) * wl.group] = decode_ref_unit(wl, q_h, b, h, ref, tt, u)
+        err, worst = out_error(out_h, y_ref)
+        say(wl.name, f"T={tt} max_err/rms={err:.3e} worst_head={worst:.3e} exact_ties={ties}")
+        errs.append(err)
+        assert err <= TOL, (tt, err)
+    cache.close()
+    free_gpu()
+    return errs
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_write_decode_reduced(name):
+    over, t, chunks = REDUCED[name]
+    wl = okv_synth.workload(name).with_(**over)
+    run_case(wl, t, chunks, steps=2 if name == "gqa_h32kv8_t32k" else 0)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_split_count_invariance(splits):
+    wl = okv_synth.workload("mha_b4h32_t128k").with_(batch=1, hq=4, hkv=4)
+    run_case(wl, 1111, [1111], splits=splits)
+
+
+@pytest.mark.parametrize("t,chunks", [(1, [1]), (32, [32]), (33, [1, 31, 1]), (64, [20, 20, 24]),
+                                      (97, [97])])
+def test_small_lengths(t, chunks):
+    wl = okv_synth.workload("gqa_b16h64kv8_t128k_asym").with_(batch=1, hq=16, hkv=2)
+    run_case(wl, t, chunks)
+    wl = okv_synth.workload("tiny_d128_t256")
+    run_case(wl, t, chunks)
+
+
+def test_degenerate_inputs():
+    # all-zero keys: every logit is equal, the output is the mean of the values;
+    # constant values: H_d of a constant vector is one spike per vector
+    _need_gpu()
+    import oracle
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=4, hkv=1)
+    p32, u = params_of(wl)
+    t = 70
+    cache = make_cache(wl, 96, p32)
+    k = torch.zeros((1, t, 1, wl.d), dtype=torch.bfloat16, device="cuda")
+    v = torch.full((1, t, 1, wl.d), 0.5, dtype=torch.bfloat16, device="cuda")
+    v[0, ::3] = -2.0
+    say("degenerate okv_write")
+    cache.write(k, v)
+    q = okv_synth.queries(wl, 0, device="cuda")
+    out = cache.decode_attn(q).cpu().numpy()
+    kh, vh = unit_inputs(k, v, 0, 0)
+    ref = oracle.write_unit(kh, vh, wl, p32)
+    assert all(x == 0 for x in compare_unit(cache, wl, 0, 0, t, ref).values())
+    y_ref = decode_ref_unit(wl, okv_synth.host_f32(q), 0, 0, ref, t, u)
+    err, _ = out_error(out[0], y_ref)
+    assert err <= TOL
+    cache.close()
+
+
+def test_error_paths():
+    _need_gpu()
+    import decode_attention_okv_amd as okv
+    wl = okv_synth.workload("tiny_d128_t256")
+    p32, _ = params_of(wl)
+    cache = make_cache(wl, 64, p32)
+    q = okv_synth.queries(wl, 0, device="cuda")
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    say("error paths")
+    assert okv.okv_decode_attn(cache.handle, q.data_ptr(), out.data_ptr()) == okv.OKV_E_INVALID
+    k, v = okv_synth.kv_tokens(wl, 0, 65, device="cuda")
+    assert okv.okv_write(cache.handle, k.data_ptr(), v.data_ptr(), 65) == okv.OKV_E_CAPACITY
+    assert okv.okv_write(cache.handle, k.data_ptr() + 4, v.data_ptr(), 1) == okv.OKV_E_ALIGN
+    assert okv.okv_write(cache.handle, k.data_ptr(), v.data_ptr(), 0) == okv.OKV_E_INVALID
+    assert cache.length == 0
+    cache.write(k[:, :64].contiguous(), v[:, :64].contiguous())
+    assert okv.okv_write(cache.handle, k.data_ptr(), v.data_ptr(), 1) == okv.OKV_E_CAPACITY
+    assert okv.okv_decode_attn(cache.handle, q.data_ptr() + 4, out.data_ptr()) == okv.OKV_E_ALIGN
+    assert okv.okv_decode_attn(cache.handle, q.data_ptr(), out.data_ptr()) == okv.OKV_OK
+    torch.cuda.synchronize()
+    assert np.isfinite(out.cpu().numpy()).all()
+    cache.close()
+    assert okv.okv_destroy(ctypes.c_void_p()) == okv.OKV_OK
