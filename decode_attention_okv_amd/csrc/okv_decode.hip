@@ -17,6 +17,8 @@
 //
 // Both quantisers are handled in one centred form: x_hat = s (u - 4) + o with
 // o = 0 (symmetric codes) or o = z + 4 s (asymmetric codes; exact in float32).
+#include <hip/hip_ext.h>
+
 #include "okv_device.hpp"
 
 namespace okv {
@@ -24,17 +26,11 @@ namespace okv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWStride = 36;          // floats per row of the per-wave weight buffer
+constexpr float kWMax = 4194303.0f;   // value weights: 22-bit fixed point per step (2^22 - 1)
 constexpr int kQMax = 8000000;        // |q| fixed-point limit: three balanced int8 digits
 constexpr int kMaxSplitsDev = 256;    // must match the host's split-K capacity
 
 enum : int { kFmtSymF32 = 0, kFmtSymF16 = 1, kFmtAsym = 2 };
-
-template <int FMT>
-__device__ __forceinline__ uint32_t load_meta_raw(const void* meta, size_t i) {
-  if constexpr (FMT == kFmtSymF32) return reinterpret_cast<const uint32_t*>(meta)[i];
-  else return reinterpret_cast<const uint16_t*>(meta)[i];
-}
 
 // (scale, offset) of a block from its raw metadata bits.
 template <int FMT>
@@ -61,6 +57,26 @@ __device__ __forceinline__ float swz_xor4(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
 }
 
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float swz_xor16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+// Maximum over the 64 lanes, returned wave-uniform (DPP / swizzle within each half,
+// then the two halves through readlane).
+__device__ __forceinline__ float wave_max_fast(float v) {
+  v = fmaxf(v, dpp_xor1(v));
+  v = fmaxf(v, dpp_xor2(v));
+  v = fmaxf(v, swz_xor4(v));
+  v = fmaxf(v, dpp_ror8(v));
+  v = fmaxf(v, swz_xor16(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  return fmaxf(a, b);
+}
+
 // Unnormalised in-place FWHT of D floats in shared memory.
 template <int D>
 __device__ __forceinline__ void lds_fwht(float* x) {
@@ -76,19 +92,33 @@ __device__ __forceinline__ void lds_fwht(float* x) {
   }
 }
 
-template <int D>
-struct TileRaw {
+// Raw loads of one compute step: NT consecutive 32-token tiles.
+template <int D, int NT>
+struct StepRaw {
   static constexpr int NG = D / 32;
-  static constexpr int IPL = kTile / (64 / NG);
-  static constexpr int DPL = D / 64;
+  static constexpr int IPL = NT * kTile / (64 / NG);   // key items per lane
+  static constexpr int DPL = D / 64;                   // value dims per lane (per tile)
   uint32_t kw[IPL][3];
   uint32_t km[IPL];
-  uint32_t vw[DPL][3];
+  uint32_t vw[NT][DPL][3];
   uint32_t vm[IPL];
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, `bytes` valid bytes (loads past them return 0)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t buf_meta(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (FMT == kFmtSymF32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 // One workgroup = one (split, query head, sequence); its four waves take the split's
-// 32-token tiles in turn, each wave double-buffering the raw loads of its next tile.
+// steps of NT 32-token tiles in turn, each wave double-buffering the raw loads of
+// its next step.
 //  * keys: lane (token slot, 32-dim group g) unpacks its group to byte lanes and
 //    takes int8 dot products against q in 24-bit fixed point (three balanced int8
 //    digits, each centred by its digit sum: exact in int32); the block scale is
@@ -96,25 +126,31 @@ struct TileRaw {
 //    lanes;
 //  * softmax in base 2; the running maximum is raised only when a logit exceeds it
 //    by more than 8, so weights stay <= 256 and rescaling is rare;
-//  * values: each lane owns D/64 dims of the dim-major value tile, weights
-//    w = p s come from a per-wave shared buffer; codes are centred per tile.
-template <int D, int FMT, int BLOCK>
+//  * values: each lane owns D/64 dims of the dim-major value tiles; the step's
+//    weights w = p s become 22-bit integers relative to the step maximum, stored as
+//    three byte planes in LDS, and meet the codes in unsigned int8 dot products
+//    (exact in int32); one float multiply-add per dim and step.
+template <int D, int FMT, int BLOCK, int NT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) {
-  using Raw = TileRaw<D>;
+  using Raw = StepRaw<D, NT>;
+  constexpr int STEP = NT * kTile;      // tokens per compute step
   constexpr int NG = Raw::NG;           // 32-dim groups per key row
   constexpr int TPR = 64 / NG;          // token slots covered by the 64 lanes per round
-  constexpr int IPL = Raw::IPL;         // key items per lane per tile
+  constexpr int IPL = Raw::IPL;         // key items per lane per step
   constexpr int LPG = 64 / NG;          // lanes per 32-dim value group
   constexpr int DPL = Raw::DPL;         // value dims per lane
   constexpr int GPB = BLOCK / 32;       // 32-dim groups per quantisation block
   constexpr int NBLK = D / BLOCK;
+  constexpr int ROWB = 3 * D / 8;       // bytes of a key code row
+  constexpr int MB = FMT == kFmtSymF32 ? 4 : 2;   // metadata bytes per block
+  static_assert(D <= 256, "one thread per q element");
 
   __shared__ float q_s[D];
-  __shared__ float q_t[D];
-  __shared__ int32_t qi_s[D];
-  __shared__ int32_t qg_s[NG][4];
+  __shared__ __align__(16) uint8_t qd_s[3][D];    // q digit planes (hi, mid, lo)
+  __shared__ int32_t qsum_s[NG][4];               // per group: sum of q, of hi, mid, lo
   __shared__ float red_s[4];
-  __shared__ __align__(16) float wbuf[4][NBLK][kWStride];
+  __shared__ __align__(16) uint8_t wq[4][NBLK][3][STEP];  // per-wave weight planes (lo, mid, hi)
+  __shared__ int32_t wsum_s[4][NBLK];
   __shared__ float cm_s[4], cl_s[4];
   __shared__ float cacc_s[4][D];
   __shared__ float cob_s[4][NBLK];
@@ -123,86 +159,81 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int hk = hq / (p.hq / p.hkv);
   const size_t unit = static_cast<size_t>(b) * p.hkv + hk;
 
-  // ---- q1 = U q in float32, then 24-bit fixed point
+  // ---- q1 = U q in float32, then 24-bit fixed point as three balanced int8 digits
   const size_t qoff = (static_cast<size_t>(b) * p.hq + hq) * D;
-  for (int j = tid; j < D; j += 256) {
-    float x = p.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qoff + j])
-                        : reinterpret_cast<const float*>(p.q)[qoff + j];
-    if (p.rotation == kRotSign) x *= p.rot[j];
-    q_s[j] = x;
+  if (tid < D) {
+    float x = p.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qoff + tid])
+                        : reinterpret_cast<const float*>(p.q)[qoff + tid];
+    if (p.rotation == kRotSign) x *= p.rot[tid];
+    q_s[tid] = x;
   }
   __syncthreads();
   lds_fwht<D>(q_s);
   const float cn = rsqrtf(static_cast<float>(D));
-  for (int j = tid; j < D; j += 256) {
-    float y;
+  float yq = 0.0f;
+  if (tid < D) {
     if (p.rotation == kRotSo4) {
-      const float* R = p.rot + 16 * (j >> 2) + 4 * (j & 3);
-      const float* xs = q_s + (j & ~3);
-      y = R[0] * xs[0] + R[1] * xs[1] + R[2] * xs[2] + R[3] * xs[3];
+      const float* R = p.rot + 16 * (tid >> 2) + 4 * (tid & 3);
+      const float* xs = q_s + (tid & ~3);
+      yq = R[0] * xs[0] + R[1] * xs[1] + R[2] * xs[2] + R[3] * xs[3];
     } else {
-      y = q_s[j];
+      yq = q_s[tid];
     }
-    q_t[j] = y * cn;
+    yq *= cn;
   }
-  __syncthreads();
-  float amax_q = 0.0f;
-  for (int j = tid; j < D; j += 256) amax_q = fmaxf(amax_q, fabsf(q_t[j]));
-  amax_q = wave_max(amax_q);
+  float amax_q = wave_max(fabsf(yq));
   if (lane == 0) red_s[wave] = amax_q;
   __syncthreads();
   amax_q = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-  {
+  if (tid < D) {
     const float inv = amax_q > 0.0f ? static_cast<float>(kQMax) / amax_q : 0.0f;
-    for (int j = tid; j < D; j += 256) {
-      int qi = static_cast<int>(__builtin_rintf(q_t[j] * inv));
-      qi = qi > kQMax ? kQMax : (qi < -kQMax ? -kQMax : qi);
-      qi_s[j] = qi;
+    int qi = static_cast<int>(__builtin_rintf(yq * inv));
+    qi = qi > kQMax ? kQMax : (qi < -kQMax ? -kQMax : qi);
+    const int lo = ((qi + 128) & 255) - 128;
+    const int q2 = (qi - lo) >> 8;
+    const int mi = ((q2 + 128) & 255) - 128;
+    const int hi = (q2 - mi) >> 8;
+    qd_s[0][tid] = static_cast<uint8_t>(hi);
+    qd_s[1][tid] = static_cast<uint8_t>(mi);
+    qd_s[2][tid] = static_cast<uint8_t>(lo);
+    // group sums over the 32 consecutive threads of the group
+    int s0 = qi, s1 = hi, s2 = mi, s3 = lo;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      s0 += __shfl_xor(s0, m, 64);
+      s1 += __shfl_xor(s1, m, 64);
+      s2 += __shfl_xor(s2, m, 64);
+      s3 += __shfl_xor(s3, m, 64);
     }
-    __syncthreads();
-    if (tid < NG) {
-      // per group: sum of q and of each of its three digits
-      int sq = 0, sh = 0, sm = 0, sl = 0;
-      for (int j = 0; j < 32; ++j) {
-        const int qi = qi_s[32 * tid + j];
-        const int l = ((qi + 128) & 255) - 128;
-        const int q2 = (qi - l) >> 8;
-        const int m = ((q2 + 128) & 255) - 128;
-        const int h = (q2 - m) >> 8;
-        sq += qi; sh += h; sm += m; sl += l;
-      }
-      qg_s[tid][0] = sq; qg_s[tid][1] = sh; qg_s[tid][2] = sm; qg_s[tid][3] = sl;
+    if ((tid & 31) == 0) {
+      qsum_s[tid >> 5][0] = s0; qsum_s[tid >> 5][1] = s1; qsum_s[tid >> 5][2] = s2; qsum_s[tid >> 5][3] = s3;
     }
-    __syncthreads();
   }
+  __syncthreads();
   const float c_logit = (amax_q > 0.0f ? amax_q / static_cast<float>(kQMax) : 0.0f) * kLog2e * cn;
 
   // per-lane q digits of key group g (dim 32g + 4k + byte)
   const int g = lane % NG;
   uint32_t qh[8], qm[8], ql[8];
+  {
+    const uint4* ph = reinterpret_cast<const uint4*>(&qd_s[0][32 * g]);
+    const uint4* pm = reinterpret_cast<const uint4*>(&qd_s[1][32 * g]);
+    const uint4* pl = reinterpret_cast<const uint4*>(&qd_s[2][32 * g]);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint32_t hv = 0, mv = 0, lv = 0;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int qi = qi_s[32 * g + 4 * k + bb];
-      const int l = ((qi + 128) & 255) - 128;
-      const int q2 = (qi - l) >> 8;
-      const int m = ((q2 + 128) & 255) - 128;
-      const int h = (q2 - m) >> 8;
-      hv |= (static_cast<uint32_t>(h) & 0xFFu) << (8 * bb);
-      mv |= (static_cast<uint32_t>(m) & 0xFFu) << (8 * bb);
-      lv |= (static_cast<uint32_t>(l) & 0xFFu) << (8 * bb);
+    for (int c = 0; c < 2; ++c) {
+      const uint4 a = ph[c], bm = pm[c], l4 = pl[c];
+      qh[4 * c] = a.x; qh[4 * c + 1] = a.y; qh[4 * c + 2] = a.z; qh[4 * c + 3] = a.w;
+      qm[4 * c] = bm.x; qm[4 * c + 1] = bm.y; qm[4 * c + 2] = bm.z; qm[4 * c + 3] = bm.w;
+      ql[4 * c] = l4.x; ql[4 * c + 1] = l4.y; ql[4 * c + 2] = l4.z; ql[4 * c + 3] = l4.w;
     }
-    qh[k] = hv; qm[k] = mv; ql[k] = lv;
   }
-  const float qsum_f = static_cast<float>(qg_s[g][0]);
-  const int h_init = -4 * qg_s[g][1], m_init = -4 * qg_s[g][2], l_init = -4 * qg_s[g][3];
+  const float qsum_f = static_cast<float>(qsum_s[g][0]);
+  const int h_init = -4 * qsum_s[g][1], m_init = -4 * qsum_s[g][2], l_init = -4 * qsum_s[g][3];
   const int blk_k = g / GPB;
   const bool wlane = (g % GPB) == 0;    // lane computes value weights of block blk_k
 
@@ -220,46 +251,47 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int ntiles = (T + kTile - 1) / kTile;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(t_begin + p.tiles_per_split, ntiles);
-  const uint8_t* kc = p.k_codes + unit * p.tcap * (3 * D / 8);
-  const uint8_t* vc = p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12;
-  const size_t mrow0 = unit * p.tcap;
+  // buffer resources of this (sequence, KV head): rows past T read as zero
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_codes + unit * p.tcap * ROWB, static_cast<uint32_t>(T) * ROWB);
+  const __amdgpu_buffer_rsrc_t rkm = make_rsrc(
+      reinterpret_cast<const uint8_t*>(p.k_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
+  const __amdgpu_buffer_rsrc_t rvm = make_rsrc(
+      reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12,
+                                              static_cast<uint32_t>(ntiles) * D * 12);
+  const uint32_t koff = static_cast<uint32_t>((lane / NG) * ROWB + 12 * g);
+  const uint32_t moff = static_cast<uint32_t>(((lane / NG) * NBLK + blk_k) * MB);
 
-  auto load_tile = [&](Raw& r, int tile) {
-    const int base = tile * kTile;
+  // step `st` covers tiles NT st .. NT st + NT - 1
+  auto load_step = [&](Raw& r, int st) {
+    const uint32_t sk = static_cast<uint32_t>(st) * STEP * ROWB;
+    const uint32_t sm = static_cast<uint32_t>(st) * STEP * NBLK * MB;
 #pragma unroll
     for (int it = 0; it < IPL; ++it) {
-      const int pos = base + lane / NG + it * TPR;
-      r.kw[it][0] = r.kw[it][1] = r.kw[it][2] = 0u;
-      r.km[it] = 0u;
-      r.vm[it] = 0u;
-      if (pos < T) {
-        const uint3 w = *reinterpret_cast<const uint3*>(kc + static_cast<size_t>(pos) * (3 * D / 8) + 12 * g);
-        r.kw[it][0] = w.x; r.kw[it][1] = w.y; r.kw[it][2] = w.z;
-        const size_t mi = (mrow0 + pos) * NBLK + blk_k;
-        r.km[it] = load_meta_raw<FMT>(p.k_meta, mi);
-        if (wlane) r.vm[it] = load_meta_raw<FMT>(p.v_meta, mi);
-      }
+      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, koff + it * TPR * ROWB, sk, 0);
+      r.kw[it][0] = w[0]; r.kw[it][1] = w[1]; r.kw[it][2] = w[2];
+      r.km[it] = buf_meta<FMT>(rkm, moff + it * TPR * NBLK * MB, sm);
+      r.vm[it] = buf_meta<FMT>(rvm, moff + it * TPR * NBLK * MB, sm);
     }
-    const uint8_t* vt = vc + static_cast<size_t>(tile) * D * 12;
 #pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      const uint3 w = *reinterpret_cast<const uint3*>(vt + 12 * vdim[dd]);
-      r.vw[dd][0] = w.x; r.vw[dd][1] = w.y; r.vw[dd][2] = w.z;
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint32_t sv = static_cast<uint32_t>(NT * st + tt) * D * 12;
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, 12 * vdim[dd], sv, 0);
+        r.vw[tt][dd][0] = w[0]; r.vw[tt][dd][1] = w[1]; r.vw[tt][dd][2] = w[2];
+      }
     }
   };
 
-  Raw cur, nxt;
-  int tile = t_begin + wave;
-  if (tile < t_end) load_tile(cur, tile);
-  for (; tile < t_end; tile += 4) {
-    if (tile + 4 < t_end) load_tile(nxt, tile + 4);
-    const int base = tile * kTile;
+  auto compute_step = [&](const Raw& r, int st) {
+    const int base = st * STEP;
     // ---- keys
     float L[IPL];
 #pragma unroll
     for (int it = 0; it < IPL; ++it) {
       uint32_t dw[8];
-      g32_to_bytes(cur.kw[it][0], cur.kw[it][1], cur.kw[it][2], dw);
+      g32_to_bytes(r.kw[it][0], r.kw[it][1], r.kw[it][2], dw);
       int ah = h_init, am = m_init, al = l_init;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -269,21 +301,20 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       }
       const int comb = (ah << 16) + (am << 8) + al;   // sum_j q_j (u_j - 4), exact
       float s, o;
-      meta_decode<FMT>(cur.km[it], s, o);
+      meta_decode<FMT>(r.km[it], s, o);
       float val = s * static_cast<float>(comb);
       if constexpr (FMT == kFmtAsym) val = __builtin_fmaf(o, qsum_f, val);
       val += dpp_xor1(val);
       val += dpp_xor2(val);
       if constexpr (NG == 8) val += swz_xor4(val);
-      const int pos = base + lane / NG + it * TPR;
-      L[it] = pos < T ? val * c_logit : -INFINITY;
+      L[it] = base + lane / NG + it * TPR < T ? val * c_logit : -INFINITY;
     }
     // ---- online softmax (base 2)
     float tmax = L[0];
 #pragma unroll
     for (int it = 1; it < IPL; ++it) tmax = fmaxf(tmax, L[it]);
     if (__any(tmax > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, wave_max(tmax));
+      const float m_new = fmaxf(m_run, wave_max_fast(tmax));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) acc[dd] *= alpha;
@@ -298,53 +329,95 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
 #pragma unroll
       for (int it = 0; it < IPL; ++it) l_run += pr[it];
     }
-    // ---- value weights w = p s_v (one lane per token and block)
-    if (wlane) {
+    // ---- value weights w = p s_v (one lane per token and block), as 22-bit
+    // integers relative to the step's largest weight
+    float wv[IPL];
+    float wmax = 0.0f;
 #pragma unroll
-      for (int it = 0; it < IPL; ++it) {
-        float s, o;
-        meta_decode<FMT>(cur.vm[it], s, o);
-        const bool valid = base + lane / NG + it * TPR < T;
-        const float w = valid ? pr[it] * s : 0.0f;
-        if constexpr (FMT == kFmtAsym) ob += valid ? pr[it] * o : 0.0f;
-        wbuf[wave][blk_k][lane / NG + it * TPR] = w;
+    for (int it = 0; it < IPL; ++it) {
+      float sv, ov;
+      meta_decode<FMT>(r.vm[it], sv, ov);   // zero past T
+      wv[it] = wlane ? pr[it] * sv : 0.0f;
+      if constexpr (FMT == kFmtAsym) ob += wlane ? pr[it] * ov : 0.0f;
+      wmax = fmaxf(wmax, wv[it]);
+    }
+    wmax = wave_max_fast(wmax);
+    const float winv = wmax > 0.0f ? kWMax * __builtin_amdgcn_rcpf(wmax) : 0.0f;
+    const float wsig = wmax * (1.0f / kWMax);
+    int wsum = 0;
+#pragma unroll
+    for (int it = 0; it < IPL; ++it) {
+      const uint32_t wi = static_cast<uint32_t>(__builtin_rintf(wv[it] * winv));
+      wsum += static_cast<int>(wi);
+      if (wlane) {
+        const int slot = lane / NG + it * TPR;
+        wq[wave][blk_k][0][slot] = static_cast<uint8_t>(wi);
+        wq[wave][blk_k][1][slot] = static_cast<uint8_t>(wi >> 8);
+        wq[wave][blk_k][2][slot] = static_cast<uint8_t>(wi >> 16);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // sum of the block's integer weights: lanes of equal g
+#pragma unroll
+    for (int mk = NG; mk < 64; mk <<= 1) wsum += __shfl_xor(wsum, mk, 64);
+    if (lane < NG && wlane) wsum_s[wave][blk_k] = wsum;
+    // the weights are read back by other lanes of this wave: LDS operations of a
+    // wave execute in order, so only compiler reordering has to be prevented
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- values: acc[j] += sum_t w_t (u_tj - 4)
-    float w[kTile];
-    {
-      const float4* wr = reinterpret_cast<const float4*>(&wbuf[wave][blk_v][0]);
+    // ---- values: acc[j] += wsig * sum_t w_t (u_tj - 4), w_t = sum_d 256^d digit_d,t;
+    // byte b of pl[d][k] is digit d of token 4k + b of the tile
+    const int wcen = 4 * wsum_s[wave][blk_v];
+    int ai[DPL];
 #pragma unroll
-      for (int i = 0; i < kTile / 4; ++i) {
-        const float4 v4 = wr[i];
-        w[4 * i] = v4.x; w[4 * i + 1] = v4.y; w[4 * i + 2] = v4.z; w[4 * i + 3] = v4.w;
+    for (int dd = 0; dd < DPL; ++dd) ai[dd] = -wcen;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      uint32_t pl[3][8];
+#pragma unroll
+      for (int dg = 0; dg < 3; ++dg) {
+        const uint4* wr = reinterpret_cast<const uint4*>(&wq[wave][blk_v][dg][kTile * tt]);
+        const uint4 x0 = wr[0], x1 = wr[1];
+        pl[dg][0] = x0.x; pl[dg][1] = x0.y; pl[dg][2] = x0.z; pl[dg][3] = x0.w;
+        pl[dg][4] = x1.x; pl[dg][5] = x1.y; pl[dg][6] = x1.z; pl[dg][7] = x1.w;
+      }
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        uint32_t dw[8];
+        g32_to_bytes(r.vw[tt][dd][0], r.vw[tt][dd][1], r.vw[tt][dd][2], dw);
+        uint32_t a0 = 0, a1 = 0, a2 = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          a0 = __builtin_amdgcn_udot4(dw[k], pl[0][k], a0, false);
+          a1 = __builtin_amdgcn_udot4(dw[k], pl[1][k], a1, false);
+          a2 = __builtin_amdgcn_udot4(dw[k], pl[2][k], a2, false);
+        }
+        // one tile's sum w u <= 7 * 32 * 2^22 < 2^30, and every partial sum lies in
+        // [-4 sum(w), 3 sum(w)] with 4 sum(w) <= 4 * 64 * 2^22 = 2^30: exact in int32
+        ai[dd] += 65536 * static_cast<int>(a2) + 256 * static_cast<int>(a1) + static_cast<int>(a0);
       }
     }
-    float wsum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) wsum += w[i];
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      uint32_t dw[8];
-      g32_to_bytes_opaque(cur.vw[dd][0], cur.vw[dd][1], cur.vw[dd][2], dw);
-      float t = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kTile; ++i) {
-        const uint32_t x = dw[i >> 2];
-        float u;
-        if ((i & 3) == 0) u = static_cast<float>(x & 0xFFu);
-        else if ((i & 3) == 1) u = static_cast<float>((x >> 8) & 0xFFu);
-        else if ((i & 3) == 2) u = static_cast<float>((x >> 16) & 0xFFu);
-        else u = static_cast<float>(x >> 24);
-        t = __builtin_fmaf(w[i], u, t);
-      }
-      acc[dd] += __builtin_fmaf(-4.0f, wsum, t);
-    }
+    for (int dd = 0; dd < DPL; ++dd) acc[dd] = __builtin_fmaf(wsig, static_cast<float>(ai[dd]), acc[dd]);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
-    cur = nxt;
+  };
+
+  // steps of NT tiles; the four waves take steps in turn; two register buffers
+  // alternate so that the loads of step s+4 are in flight while step s is computed
+  // (past the split's end the prefetch reloads its last step)
+  const int s_begin = t_begin / NT;
+  const int s_end = (t_end + NT - 1) / NT;
+  Raw ra, rb;
+  int st = s_begin + wave;
+  if (st < s_end) load_step(ra, st);
+  while (st < s_end) {
+    load_step(rb, min(st + 4, s_end - 1));
+    compute_step(ra, st);
+    st += 4;
+    if (st >= s_end) break;
+    load_step(ra, min(st + 4, s_end - 1));
+    compute_step(rb, st);
+    st += 4;
   }
 
   // ---- combine the four waves
@@ -452,23 +525,23 @@ __global__ __launch_bounds__(256) void reduce_kernel(const ReduceParams p) {
 }
 
 template <int D, int FMT, int BLOCK>
-void launch_decode_t(const DecodeParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_valu_kernel<D, FMT, BLOCK>), grid, dim3(256), 0, s, p);
+void launch_decode_t(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL((decode_valu_kernel<D, FMT, BLOCK, kStepTiles>), grid, dim3(256), 0, s, e0, e1, 0, p);
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_decode_d(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   int fmt;
   if (p.quant == kQuantAsym) fmt = kFmtAsym;
   else fmt = p.scale_dtype == kScaleF32 ? kFmtSymF32 : kFmtSymF16;
   if (p.block == 32) {
-    if (fmt == kFmtSymF32) launch_decode_t<D, kFmtSymF32, 32>(p, grid, s);
-    else if (fmt == kFmtSymF16) launch_decode_t<D, kFmtSymF16, 32>(p, grid, s);
-    else launch_decode_t<D, kFmtAsym, 32>(p, grid, s);
+    if (fmt == kFmtSymF32) launch_decode_t<D, kFmtSymF32, 32>(p, grid, s, e0, e1);
+    else if (fmt == kFmtSymF16) launch_decode_t<D, kFmtSymF16, 32>(p, grid, s, e0, e1);
+    else launch_decode_t<D, kFmtAsym, 32>(p, grid, s, e0, e1);
   } else if (p.block == 64) {
-    if (fmt == kFmtSymF32) launch_decode_t<D, kFmtSymF32, 64>(p, grid, s);
-    else if (fmt == kFmtSymF16) launch_decode_t<D, kFmtSymF16, 64>(p, grid, s);
-    else launch_decode_t<D, kFmtAsym, 64>(p, grid, s);
+    if (fmt == kFmtSymF32) launch_decode_t<D, kFmtSymF32, 64>(p, grid, s, e0, e1);
+    else if (fmt == kFmtSymF16) launch_decode_t<D, kFmtSymF16, 64>(p, grid, s, e0, e1);
+    else launch_decode_t<D, kFmtAsym, 64>(p, grid, s, e0, e1);
   } else {
     return hipErrorInvalidValue;
   }
@@ -477,19 +550,21 @@ hipError_t launch_decode_d(const DecodeParams& p, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1) {
   if (p.nsplit < 1 || p.nsplit > kMaxSplitsDev) return hipErrorInvalidValue;
   const dim3 grid(p.nsplit, p.hq, batch);
-  if (d == 128) return launch_decode_d<128>(p, grid, s);
-  if (d == 256) return launch_decode_d<256>(p, grid, s);
+  if (d == 128) return launch_decode_d<128>(p, grid, s, e0, e1);
+  if (d == 256) return launch_decode_d<256>(p, grid, s, e0, e1);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s) {
+hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1) {
   if (p.nsplit < 1 || p.nsplit > kMaxSplitsDev) return hipErrorInvalidValue;
   const dim3 grid(p.hq, batch);
-  if (d == 128) hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(256), 0, s, p);
-  else if (d == 256) hipLaunchKernelGGL(reduce_kernel<256>, grid, dim3(256), 0, s, p);
+  if (d == 128) hipExtLaunchKernelGGL(reduce_kernel<128>, grid, dim3(256), 0, s, e0, e1, 0, p);
+  else if (d == 256) hipExtLaunchKernelGGL(reduce_kernel<256>, grid, dim3(256), 0, s, e0, e1, 0, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

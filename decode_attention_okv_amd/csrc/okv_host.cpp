@@ -16,7 +16,7 @@
 namespace {
 
 constexpr int kMaxSplits = 256;      // split-K workspace capacity per (sequence, query head)
-constexpr int kTargetGroups = 4096;  // workgroups the automatic split count aims for
+constexpr int kTargetGroups = 2048;  // workgroups the automatic split count aims for
 constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -69,7 +69,7 @@ void layout_of(const okv_config& c, okv_layout_info* li) {
 }
 
 struct TimingSlot {
-  hipEvent_t e0, e1, e2;
+  hipEvent_t e0, e1, e2, e3;  // attention kernel start/end, reduce kernel start/end
 };
 
 }  // namespace
@@ -88,7 +88,9 @@ struct okv_handle {
 
 namespace {
 
-int choose_splits(const okv_handle* h, int32_t T) {
+// Split count and tiles per split for a cache of T tokens: every split holds a
+// whole number of decode steps (kStepTiles tiles) and none is empty.
+int choose_splits(const okv_handle* h, int32_t T, int* tiles_per_split) {
   const int ntiles = (T + okv::kTile - 1) / okv::kTile;
   int s = h->splits;
   if (s <= 0) {
@@ -98,8 +100,9 @@ int choose_splits(const okv_handle* h, int32_t T) {
   if (s > kMaxSplits) s = kMaxSplits;
   if (s > ntiles) s = ntiles;
   if (s < 1) s = 1;
-  // no empty split: recompute the count from the tiles each split gets
-  const int tps = (ntiles + s - 1) / s;
+  int tps = (ntiles + s - 1) / s;
+  tps = (tps + okv::kStepTiles - 1) / okv::kStepTiles * okv::kStepTiles;
+  if (tiles_per_split) *tiles_per_split = tps;
   return (ntiles + tps - 1) / tps;
 }
 
@@ -108,6 +111,7 @@ void free_timing(okv_handle* h) {
     (void)hipEventDestroy(t.e0);
     (void)hipEventDestroy(t.e1);
     (void)hipEventDestroy(t.e2);
+    (void)hipEventDestroy(t.e3);
   }
   h->slots.clear();
   h->recorded = 0;
@@ -245,7 +249,8 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   if (h->len < 1) return OKV_E_INVALID;
   const okv_config& c = h->cfg;
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const int nsplit = choose_splits(h, h->len);
+  int tps = 0;
+  const int nsplit = choose_splits(h, h->len, &tps);
   okv::DecodeParams p{};
   p.k_codes = static_cast<const uint8_t*>(c.k_codes);
   p.v_codes = static_cast<const uint8_t*>(c.v_codes);
@@ -259,8 +264,7 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   p.tcap = c.max_tokens;
   p.ntile_cap = c.max_tokens / okv::kTile;
   p.T = h->len;
-  const int ntiles = (h->len + okv::kTile - 1) / okv::kTile;
-  p.tiles_per_split = (ntiles + nsplit - 1) / nsplit;
+  p.tiles_per_split = tps;
   p.nsplit = nsplit;
   p.block = c.block;
   p.quant = c.quant;
@@ -277,11 +281,14 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
   TimingSlot* ts = nullptr;
   if (h->timing && h->recorded < static_cast<int>(h->slots.size())) ts = &h->slots[h->recorded++];
-  if (ts && hipEventRecord(ts->e0, s) != hipSuccess) return OKV_E_HIP;
-  if (okv::launch_decode(p, c.batch, c.head_dim, s) != hipSuccess) return OKV_E_HIP;
-  if (ts && hipEventRecord(ts->e1, s) != hipSuccess) return OKV_E_HIP;
-  if (okv::launch_reduce(r, c.batch, c.head_dim, s) != hipSuccess) return OKV_E_HIP;
-  if (ts && hipEventRecord(ts->e2, s) != hipSuccess) return OKV_E_HIP;
+  if (okv::launch_decode(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr, ts ? ts->e1 : nullptr) !=
+      hipSuccess) {
+    return OKV_E_HIP;
+  }
+  if (okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr) !=
+      hipSuccess) {
+    return OKV_E_HIP;
+  }
   return OKV_OK;
 }
 
@@ -311,7 +318,7 @@ int okv_max_splits(const okv_handle* h, int32_t* n) {
 
 int okv_get_splits(const okv_handle* h, int32_t* n) {
   if (h == nullptr || n == nullptr) return OKV_E_INVALID;
-  *n = h->len > 0 ? choose_splits(h, h->len) : 0;
+  *n = h->len > 0 ? choose_splits(h, h->len, nullptr) : 0;
   return OKV_OK;
 }
 
@@ -322,7 +329,7 @@ int okv_timing_enable(okv_handle* h, int32_t enable) {
     h->slots.resize(kTimingSlots);
     for (auto& t : h->slots) {
       if (hipEventCreate(&t.e0) != hipSuccess || hipEventCreate(&t.e1) != hipSuccess ||
-          hipEventCreate(&t.e2) != hipSuccess) {
+          hipEventCreate(&t.e2) != hipSuccess || hipEventCreate(&t.e3) != hipSuccess) {
         return OKV_E_HIP;
       }
     }
@@ -339,9 +346,9 @@ int okv_timing_read(okv_handle* h, int32_t* calls, double* attn_ms, double* redu
   for (int i = 0; i < h->recorded; ++i) {
     TimingSlot& t = h->slots[i];
     float x = 0.0f, y = 0.0f;
-    if (hipEventSynchronize(t.e2) != hipSuccess) return OKV_E_HIP;
+    if (hipEventSynchronize(t.e3) != hipSuccess) return OKV_E_HIP;
     if (hipEventElapsedTime(&x, t.e0, t.e1) != hipSuccess) return OKV_E_HIP;
-    if (hipEventElapsedTime(&y, t.e1, t.e2) != hipSuccess) return OKV_E_HIP;
+    if (hipEventElapsedTime(&y, t.e2, t.e3) != hipSuccess) return OKV_E_HIP;
     a += x;
     r += y;
   }

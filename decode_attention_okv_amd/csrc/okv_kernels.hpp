@@ -9,6 +9,7 @@ namespace okv {
 
 constexpr int kTile = 32;   // tokens per value tile
 constexpr int kGroup = 32;  // codes per 12-byte packed group
+constexpr int kStepTiles = 2;  // tiles per decode compute step: splits hold whole steps
 
 enum : int { kQuantSym = 0, kQuantAsym = 1 };
 enum : int { kScaleF32 = 0, kScaleF16 = 1, kScaleE4M3 = 3 };
@@ -47,7 +48,11 @@ struct ReduceParams {
 };
 
 hipError_t launch_write(const WriteParams& p, int ntiles, int batch, int d, hipStream_t s);
-hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s);
-hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s);
+// ev0/ev1 (may be null): events recorded at the start and the end of the kernel's
+// own dispatch (hipExtLaunchKernelGGL), so their elapsed time is the kernel time.
+hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 }  // namespace okv

@@ -173,7 +173,8 @@ int okv_max_splits(const okv_handle* h, int32_t* n);
 /* Split count the next okv_decode_attn call will use at the current length. */
 int okv_get_splits(const okv_handle* h, int32_t* n);
 /* Kernel timing: when enabled, okv_decode_attn records HIP events on its stream
- * around its attention kernel and its reduce kernel.  okv_timing_read waits for the
+ * attached to the dispatch of its attention kernel and of its reduce kernel (so the
+ * elapsed times are the kernels' own).  okv_timing_read waits for the
  * recorded calls, returns how many were recorded since the last read and the
  * summed kernel milliseconds, then clears the record. */
 int okv_timing_enable(okv_handle* h, int32_t enable);
