@@ -80,8 +80,8 @@ def cpu_baseline(wl, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mha_b4h32_t128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0)
@@ -157,14 +157,12 @@ def main():
     torch.cuda.synchronize()
     step_ms_total = ts.elapsed_time(te)
     assert torch.isfinite(out).all()
-    # kernel durations: the same K decode calls again (cache rolled back to the
-    # length the timed region started from), with events attached to the kernels'
-    # own dispatches
-    cache.set_length(T0 + W)
+    # attention-kernel duration: K more decode calls back to back at the final
+    # length, with HIP events attached to the kernel's own dispatch
+    t_fin = T0 + steps
     cache.timing(True)
-    for i in range(W, steps):
-        cache.write(*news[i])
-        cache.decode_attn(qs[i], out)
+    for i in range(K):
+        cache.decode_attn(qs[W + i], out)
     torch.cuda.synchronize()
     ncalls, attn_ms, red_ms = cache.timing_read()
     cache.timing(False)
@@ -173,7 +171,7 @@ def main():
     lens = [T0 + i + 1 for i in range(W, steps)]
     tot_bytes = sum(sum(algorithmic_decode_bytes(wl, t)) for t in lens)
     value = tot_bytes / (step_ms_total * 1e-3) / 1e9
-    kern_bytes = sum(algorithmic_decode_bytes(wl, t)[0] + algorithmic_decode_bytes(wl, t)[1] for t in lens)
+    kern_bytes = K * (algorithmic_decode_bytes(wl, t_fin)[0] + algorithmic_decode_bytes(wl, t_fin)[1])
     achieved = kern_bytes / (attn_ms * 1e-3) / 1e9
     write_tok_s = wl.batch * T0 / (prefill_ms * 1e-3)
 

@@ -1,13 +1,13 @@
 // Read path: decode attention directly over the packed 3-bit cache.
 //
-// Pages: "Orthogonally mixed 3-bit KV cache", Implementation notes (q1 = U(q);
-// unpack and scale keys inside the attention dot product; logits from q1 and the
-// reconstructed transformed keys; softmax; multiply by the reconstructed
-// transformed values; rotate the output back with U.T; never materialise full
-// K/V) and Key formulas (softmax(QK^T / sqrt d) V); "Orthogonal Invariance in
-// Activation Space", Section 2.3 (rotating q and rotating the output back leaves
-// attention unchanged) and Section 4.3 (dequantisation fused into the attention
-// kernel).
+// Pages: "Orthogonally mixed 3-bit KV cache", Implementation notes (the read
+// path: the query is rotated by U, the packed keys are decoded and scaled inside
+// the dot product, the softmax weights multiply the decoded rotated values and U^T
+// maps the result back; full-precision K/V never exist in memory) and Key
+// formulas (attention as softmax of the scaled logits times V); "Orthogonal
+// Invariance in Activation Space", Section 2.3 (rotating q together with k, and
+// rotating the output back, leaves attention unchanged) and Section 4.3
+// (dequantisation fused into the attention kernel).
 //
 // Split-K: the token range of each (sequence, query head) is cut into splits; one
 // workgroup per split produces (m, l, acc[D]) with m the running maximum of the

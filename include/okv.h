@@ -139,12 +139,11 @@ typedef struct okv_layout_info {
  * the device of the handle. */
 int okv_create(const okv_config* cfg, okv_handle** out);
 
-/* Append n_new tokens to every sequence: rotate k and v with U, quantise, pack,
- * and store codes and scales at positions len .. len+n_new-1 (the idea card,
- * Implementation notes: "On every new token compute k1 = U(k) and v1 = U(v) ...
- * store only packed codes and scales").  k, v: device, [batch][n_new][kv][d] in
- * the input type, 16-byte aligned.  Asynchronous on hip_stream; len advances by
- * n_new at once (host side). */
+/* Append n_new tokens to every sequence: rotate each new key and value vector by
+ * U, quantise it blockwise, pack the codes and store codes and scales at positions
+ * len .. len+n_new-1 (the write path of the idea card's Implementation notes).
+ * k, v: device, [batch][n_new][kv][d] in the input type, 16-byte aligned.
+ * Asynchronous on hip_stream; len advances by n_new at once (host side). */
 int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* hip_stream);
 
 /* One decode step: for every (sequence, query head) attend over all len cached

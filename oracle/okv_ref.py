@@ -80,9 +80,9 @@ def c_norm_f32(d: int) -> np.float32:
 def fwht_f32(x) -> np.ndarray:
     """Normalised fast Walsh-Hadamard transform of the last axis, in float32.
 
-    The idea card, Implementation notes, asks for the "recursive butterfly";
-    H_{2n} = [[H_n, H_n], [H_n, -H_n]] transforms both halves first and combines
-    them last.  READING (fp32 evaluation order): butterfly stages of stride
+    The idea card, Implementation notes, computes the transform by the recursive
+    butterfly scheme; the recursion H_{2n} = [[H_n, H_n], [H_n, -H_n]] transforms
+    both halves first and combines them last.  READING (fp32 evaluation order): butterfly stages of stride
     h = 1, 2, 4, ..., d/2 in that order; in a stage every pair (i, i + h) with
     i & h == 0 becomes (a + b, a - b), each a single float32 rounding; after the
     last stage one multiply by c_d = RN32(1/sqrt(d)) (normalisation, OIQ report
@@ -105,9 +105,9 @@ def rotate_f32(x, rotation: str, params32) -> np.ndarray:
     """y = U x in float32, the write path's rotation (bit specification).
 
     'sign' (OIQ report Section 3.2): multiply by the signs (exact), then fwht_f32.
-    'so4'  (idea card, Implementation notes: "normalized fast Walsh-Hadamard
-    transform ... then apply a block-diagonal collection of SO(4) matrices"):
-    fwht_f32, then for each 4-block r of the output
+    'so4'  (idea card, Implementation notes: the normalised transform first, the
+    block-diagonal SO(4) rotations after it): fwht_f32, then for each 4-block r
+    of the output
     y_r = ((R_r0 x_0 + R_r1 x_1) + R_r2 x_2) + R_r3 x_3, every product and sum
     rounded separately (READING: this order, no fused multiply-add).
     """
@@ -285,8 +285,8 @@ def meta_values(meta, spec):
 
 def dequantize(u, meta, spec) -> np.ndarray:
     """x_hat (float64) from stored codes and metadata (idea card, Key formulas:
-    x_hat = s clip(round(x/s), ...); news item, third paragraph: scale and
-    zero-point)."""
+    the reconstruction is the scale times the clipped rounded code; news item,
+    third paragraph: scale and zero-point)."""
     u = np.asarray(u).astype(np.float64)
     d = u.shape[-1]
     m = spec.block
@@ -302,8 +302,9 @@ def dequantize(u, meta, spec) -> np.ndarray:
 def _g32_positions() -> np.ndarray:
     """Bit index (0..95, little-endian over the 12 bytes) of bit q of code i.
 
-    READING: the idea card (Implementation notes) says only "pack the codes into
-    bytes"; the layout chosen here keeps 8 codes per 32-bit word in byte lanes:
+    READING: the idea card (Implementation notes) only says that the codes are
+    packed into bytes; the layout chosen here keeps 8 codes per 32-bit word in
+    byte lanes:
       codes 0..23: word k = i // 8, r = i % 8, byte b = r % 4, field f = r // 4,
                    bits 8b + 3f .. 8b + 3f + 2 of word k;
       codes 24..27 (b = i - 24): bits 0-1 -> bits 8b+6, 8b+7 of word 0,
@@ -396,9 +397,9 @@ def unpack_vtiles(v, t: int) -> np.ndarray:
 def write_unit(k, v, spec, params32):
     """Rotate, quantise and pack the keys and values of one (sequence, KV head).
 
-    The idea card, Implementation notes: on every new token compute k1 = U(k),
-    v1 = U(v), one scale per block, round to signed 3-bit integers, pack, store
-    only codes and scales.  k, v: (T, d) float32 (exact widening of the inputs).
+    The idea card, Implementation notes (write path): each new key and value
+    vector is rotated by U, given one scale per block, rounded to signed 3-bit
+    codes and packed; only codes and scales are kept.  k, v: (T, d) float32 (exact widening of the inputs).
     Returns a dict: k_codes (T, 3d/8) uint8, v_codes (ceil(T/32), d, 12) uint8,
     k_meta / v_meta (T, d/m) scales or (T, d/m, 2) E4M3 bytes, plus the code
     arrays k_u / v_u (T, d) and the rotated float32 vectors k_rot / v_rot.
@@ -437,10 +438,11 @@ def attend_unit(q, k_codes, k_meta, v_codes, v_meta, t: int, spec, u_mat) -> np.
     """Decode attention of the query heads q (G, d) of one KV head over its t
     cached tokens, from the packed cache.
 
-    The idea card, Implementation notes: q1 = U(q); logits from q1 and the
-    reconstructed transformed keys; softmax; multiply by the reconstructed
-    transformed values; rotate the output back with U^T.  The OIQ report,
-    Section 2.3, gives why this equals attention on the unrotated vectors.
+    The idea card, Implementation notes (read path): the query is rotated by U,
+    logits come from it and the decoded rotated keys, the softmax weights
+    multiply the decoded rotated values, and U^T maps the result back.  The OIQ
+    report, Section 2.3, explains why this equals attention on the unrotated
+    vectors.
     Returns (G, d) float64.
     """
     d = spec.d
