@@ -20,7 +20,8 @@ __all__ = [
     "OkvError", "OkvConfig", "OkvLayout", "lib", "LIB_PATH", "EXPORTS",
     "okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror", "okv_layout",
     "okv_get_len", "okv_set_len", "okv_set_splits", "okv_get_splits", "okv_max_splits",
-    "okv_timing_enable", "okv_timing_read", "make_config", "OkvCache",
+    "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel", "okv_get_decode_kernel",
+    "DECODE_KERNEL", "make_config", "OkvCache",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libokv.so")
@@ -30,10 +31,12 @@ OKV_OK, OKV_E_INVALID, OKV_E_ALIGN, OKV_E_CAPACITY, OKV_E_UNSUPPORTED, OKV_E_HIP
 QUANT = {"sym": 0, "asym": 1}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 ROTATION = {"sign": 0, "so4": 1}
+DECODE_KERNEL = {"auto": 0, "per_head": 1, "grouped": 2}
 
 EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror",
            "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
-           "okv_get_splits", "okv_timing_enable", "okv_timing_read")
+           "okv_get_splits", "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel",
+           "okv_get_decode_kernel")
 
 
 class OkvConfig(ctypes.Structure):
@@ -83,6 +86,8 @@ def _load():
         "okv_get_splits": (i32, [vp, P(i32)]),
         "okv_timing_enable": (i32, [vp, i32]),
         "okv_timing_read": (i32, [vp, P(i32), P(ctypes.c_double), P(ctypes.c_double)]),
+        "okv_set_decode_kernel": (i32, [vp, i32]),
+        "okv_get_decode_kernel": (i32, [vp, P(i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(so, name)
@@ -173,6 +178,15 @@ def okv_timing_read(h):
     n, a, r = ctypes.c_int32(), ctypes.c_double(), ctypes.c_double()
     st = lib.okv_timing_read(h, ctypes.byref(n), ctypes.byref(a), ctypes.byref(r))
     return st, n.value, a.value, r.value
+
+
+def okv_set_decode_kernel(h, kind: int) -> int:
+    return lib.okv_set_decode_kernel(h, kind)
+
+
+def okv_get_decode_kernel(h):
+    n = ctypes.c_int32()
+    return lib.okv_get_decode_kernel(h, ctypes.byref(n)), n.value
 
 
 def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block=32,
@@ -282,6 +296,15 @@ class OkvCache:
         st, n = okv_get_splits(self.handle)
         _check(st, "okv_get_splits")
         return n
+
+    def set_decode_kernel(self, kind: str) -> None:
+        """"auto", "per_head" or "grouped" (see okv_set_decode_kernel)."""
+        _check(okv_set_decode_kernel(self.handle, DECODE_KERNEL[kind]), "okv_set_decode_kernel")
+
+    def decode_kernel(self) -> str:
+        st, n = okv_get_decode_kernel(self.handle)
+        _check(st, "okv_get_decode_kernel")
+        return {v: k for k, v in DECODE_KERNEL.items()}[n]
 
     def timing(self, on: bool) -> None:
         _check(okv_timing_enable(self.handle, on), "okv_timing_enable")

@@ -19,78 +19,13 @@
 // o = 0 (symmetric codes) or o = z + 4 s (asymmetric codes; exact in float32).
 #include <hip/hip_ext.h>
 
-#include "okv_device.hpp"
+#include "okv_decode_common.hpp"
 
 namespace okv {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kWMax = 4194303.0f;   // value weights: 22-bit fixed point per step (2^22 - 1)
-constexpr int kQMax = 8000000;        // |q| fixed-point limit: three balanced int8 digits
-constexpr int kMaxSplitsDev = 256;    // must match the host's split-K capacity
-
-enum : int { kFmtSymF32 = 0, kFmtSymF16 = 1, kFmtAsym = 2 };
-
-// (scale, offset) of a block from its raw metadata bits.
-template <int FMT>
-__device__ __forceinline__ void meta_decode(uint32_t raw, float& s, float& o) {
-  if constexpr (FMT == kFmtSymF32) {
-    s = __uint_as_float(raw);
-    o = 0.0f;
-  } else if constexpr (FMT == kFmtSymF16) {
-    s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(raw)));
-    o = 0.0f;
-  } else {
-    s = e4m3_decode(raw & 0xFFu);
-    o = e4m3_decode(raw >> 8) + 4.0f * s;
-  }
-}
-
-__device__ __forceinline__ float dpp_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float swz_xor4(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
-}
-
-__device__ __forceinline__ float dpp_ror8(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float swz_xor16(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-}
-
-// Maximum over the 64 lanes, returned wave-uniform (DPP / swizzle within each half,
-// then the two halves through readlane).
-__device__ __forceinline__ float wave_max_fast(float v) {
-  v = fmaxf(v, dpp_xor1(v));
-  v = fmaxf(v, dpp_xor2(v));
-  v = fmaxf(v, swz_xor4(v));
-  v = fmaxf(v, dpp_ror8(v));
-  v = fmaxf(v, swz_xor16(v));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  return fmaxf(a, b);
-}
-
-// Unnormalised in-place FWHT of D floats in shared memory.
-template <int D>
-__device__ __forceinline__ void lds_fwht(float* x) {
-#pragma unroll
-  for (int hs = 1; hs < D; hs <<= 1) {
-    for (int pidx = threadIdx.x; pidx < D / 2; pidx += blockDim.x) {
-      const int i = (pidx / hs) * 2 * hs + (pidx % hs);
-      const float a = x[i], c = x[i + hs];
-      x[i] = a + c;
-      x[i + hs] = a - c;
-    }
-    __syncthreads();
-  }
-}
+using namespace dec;
 
 // Raw loads of one compute step: NT consecutive 32-token tiles.
 template <int D, int NT>
@@ -103,18 +38,6 @@ struct StepRaw {
   uint32_t vw[NT][DPL][3];
   uint32_t vm[IPL];
 };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer: stride 0, `bytes` valid bytes (loads past them return 0)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t buf_meta(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (FMT == kFmtSymF32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-  else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
 
 // One workgroup = one (split, query head, sequence); its four waves take the split's
 // steps of NT 32-token tiles in turn, each wave double-buffering the raw loads of
@@ -251,7 +174,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int ntiles = (T + kTile - 1) / kTile;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(t_begin + p.tiles_per_split, ntiles);
-  // buffer resources of this (sequence, KV head): rows past T read as zero
+  // buffer resources of this (sequence, KV head); offsets carry the step base in the
+  // vector offset (the range check covers it), so rows past T read as zero
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_codes + unit * p.tcap * ROWB, static_cast<uint32_t>(T) * ROWB);
   const __amdgpu_buffer_rsrc_t rkm = make_rsrc(
       reinterpret_cast<const uint8_t*>(p.k_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
@@ -268,17 +192,17 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     const uint32_t sm = static_cast<uint32_t>(st) * STEP * NBLK * MB;
 #pragma unroll
     for (int it = 0; it < IPL; ++it) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, koff + it * TPR * ROWB, sk, 0);
+      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, sk + koff + it * TPR * ROWB, 0, 0);
       r.kw[it][0] = w[0]; r.kw[it][1] = w[1]; r.kw[it][2] = w[2];
-      r.km[it] = buf_meta<FMT>(rkm, moff + it * TPR * NBLK * MB, sm);
-      r.vm[it] = buf_meta<FMT>(rvm, moff + it * TPR * NBLK * MB, sm);
+      r.km[it] = buf_meta<FMT>(rkm, sm + moff + it * TPR * NBLK * MB, 0);
+      r.vm[it] = buf_meta<FMT>(rvm, sm + moff + it * TPR * NBLK * MB, 0);
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       const uint32_t sv = static_cast<uint32_t>(NT * st + tt) * D * 12;
 #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, 12 * vdim[dd], sv, 0);
+        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, sv + 12 * vdim[dd], 0, 0);
         r.vw[tt][dd][0] = w[0]; r.vw[tt][dd][1] = w[1]; r.vw[tt][dd][2] = w[2];
       }
     }

@@ -1,0 +1,91 @@
+// Helpers shared by the decode kernels (included by okv_decode.hip and
+// okv_decode_mfma.hip only).
+#pragma once
+
+#include "okv_device.hpp"
+
+namespace okv {
+namespace dec {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kWMax = 4194303.0f;   // value weights: 22-bit fixed point per step (2^22 - 1)
+constexpr int kQMax = 8000000;        // |q| fixed-point limit: three balanced int8 digits
+constexpr int kMaxSplitsDev = 256;    // must match the host's split-K capacity
+
+enum : int { kFmtSymF32 = 0, kFmtSymF16 = 1, kFmtAsym = 2 };
+
+// (scale, offset) of a block from its raw metadata bits.
+template <int FMT>
+__device__ __forceinline__ void meta_decode(uint32_t raw, float& s, float& o) {
+  if constexpr (FMT == kFmtSymF32) {
+    s = __uint_as_float(raw);
+    o = 0.0f;
+  } else if constexpr (FMT == kFmtSymF16) {
+    s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(raw)));
+    o = 0.0f;
+  } else {
+    // v_cvt_f32_fp8 decodes OCP E4M3FN on gfx950 (byte 0: scale, byte 1: zero-point)
+    s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(raw), 0);
+    o = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(raw), 1) + 4.0f * s;
+  }
+}
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float swz_xor4(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+}
+
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float swz_xor16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+// Maximum over the 64 lanes, returned wave-uniform (DPP / swizzle within each half,
+// then the two halves through readlane).
+__device__ __forceinline__ float wave_max_fast(float v) {
+  v = fmaxf(v, dpp_xor1(v));
+  v = fmaxf(v, dpp_xor2(v));
+  v = fmaxf(v, swz_xor4(v));
+  v = fmaxf(v, dpp_ror8(v));
+  v = fmaxf(v, swz_xor16(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  return fmaxf(a, b);
+}
+
+// Unnormalised in-place FWHT of D floats in shared memory.
+template <int D>
+__device__ __forceinline__ void lds_fwht(float* x) {
+#pragma unroll
+  for (int hs = 1; hs < D; hs <<= 1) {
+    for (int pidx = threadIdx.x; pidx < D / 2; pidx += blockDim.x) {
+      const int i = (pidx / hs) * 2 * hs + (pidx % hs);
+      const float a = x[i], c = x[i + hs];
+      x[i] = a + c;
+      x[i + hs] = a - c;
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, `bytes` valid bytes (loads past them return 0)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t buf_meta(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (FMT == kFmtSymF32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+}  // namespace dec
+}  // namespace okv

@@ -1,0 +1,643 @@
+// Decode attention for query groups: G query heads share one key/value head, so
+// the packed keys and values of a (sequence, KV head) are streamed once for all G
+// heads and both contractions run on int8 MFMA (v_mfma_i32_16x16x64_i8).  A wave
+// works on steps of 64 tokens (two 32-token value tiles):
+//
+//  * Q.K: A = key codes of 16 tokens (rows) x 64 dims, B = 16 columns (head h,
+//    block b) holding one int8 digit of q_h restricted to block b (zero elsewhere).
+//    A lane decodes one whole 32-code key group and feeds two instructions; the
+//    (head, block) columns keep the per-block scales separable.  Three instruction
+//    chains take the three balanced digits of the 24-bit fixed-point query and
+//    combine exactly in int32.
+//  * P.V: A = the step's weights p s as 21-bit integers in three 7-bit digits, rows
+//    (head, block); B = value codes of 64 tokens x 16 dims, decoded once per step
+//    into LDS; C = int32 [rows x dims].  Only rows whose block holds the 16 dims are
+//    kept, scaled back to float once per step.
+//
+// Block metadata is decoded once per (token, block) into LDS as floats.  With the
+// asymmetric quantiser the zero-point enters directly (s u + z); with the symmetric
+// one the codes are centred (s (u - 4)) through the integer accumulators.
+//
+// Method: "Orthogonally mixed 3-bit KV cache" (idea card), Implementation notes,
+// read path, and Key formulas; "Orthogonal Invariance in Activation Space",
+// Sections 2.3 and 4.3.  Split partials go to the same workspace, merged by the
+// same reduce kernel as the per-head path.
+#include <hip/hip_ext.h>
+
+#include "okv_decode_common.hpp"
+#include "okv_kernels.hpp"
+
+namespace okv {
+
+namespace {
+
+using namespace dec;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kStep = 64;                 // tokens per wave step (two value tiles)
+constexpr int kW7 = (1 << 21) - 1;        // P.V weights: 21-bit integers per step and row
+
+__device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
+__device__ __forceinline__ int xor16i(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
+__device__ __forceinline__ int xor32i(int v) { return __shfl_xor(v, 32, 64); }
+
+__device__ __forceinline__ v4i mfma64(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// a * 2^sa + b * 2^sb + c in wrapping int32 arithmetic (the true value fits).
+template <int SA, int SB>
+__device__ __forceinline__ int combine3(int a, int b, int c) {
+  return static_cast<int>((static_cast<uint32_t>(a) << SA) + (static_cast<uint32_t>(b) << SB) +
+                          static_cast<uint32_t>(c));
+}
+
+// Balanced base-256 digits: q = 65536 hi + 256 mi + lo, each in [-128, 127].
+__device__ __forceinline__ void digits_q(int q, int& hi, int& mi, int& lo) {
+  lo = ((q + 128) & 255) - 128;
+  const int q2 = (q - lo) >> 8;
+  mi = ((q2 + 128) & 255) - 128;
+  hi = (q2 - mi) >> 8;
+}
+
+// Byte b of the result = the low byte of x_b.
+__device__ __forceinline__ uint32_t bytes4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  return (x3 << 24) | (x2 << 16) | (x1 << 8) | x0;   // v_lshl_or_b32 chain
+}
+
+// 16-byte slot of chunk c (16 tokens) in a 64-byte LDS row r: rotating the chunk
+// order by bits 2-3 of the row spreads 16 consecutive rows over all 64 banks.
+__device__ __forceinline__ int slot16(int c, int r) { return (c ^ (r >> 2)) & 3; }
+
+template <int MDW>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+  if constexpr (MDW == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (MDW == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < MDW / 4; ++i) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+      w[4 * i] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
+    }
+  }
+}
+
+// Scale s (and zero-point z) of block `bb` from a token's raw metadata row `w`.
+template <int FMT>
+__device__ __forceinline__ void meta_entry(const uint32_t* w, int bb, float& s, float& z) {
+  if constexpr (FMT == kFmtSymF32) {
+    s = __uint_as_float(w[bb]);
+    z = 0.0f;
+  } else if constexpr (FMT == kFmtSymF16) {
+    const uint32_t x = w[bb >> 1];
+    s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>((bb & 1) ? (x >> 16) : x)));
+    z = 0.0f;
+  } else {
+    // v_cvt_pk_f32_fp8 decodes two OCP E4M3FN bytes on gfx950: entry = (scale, zero-point)
+    const int x = static_cast<int>(w[bb >> 1]);
+    const auto f = (bb & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(x, true) : __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+    s = f[0];
+    z = f[1];
+  }
+}
+
+template <int NQ, int DPL, int MDW>
+struct StepRaw {
+  uint32_t kw[4][NQ][3];  // token 16 hf + (lane % 16) of the step, key group 4 qd + lane / 16
+  uint32_t vw[2][DPL][3]; // value tile tt of the step, dims lane + 64 k
+  uint32_t km[MDW];       // key metadata row of token `lane` of the step
+  uint32_t vm[MDW];       // value metadata row of token `lane`
+};
+
+// One workgroup = one (split, KV head, sequence) and all G query heads of that KV
+// head; its four waves take the split's 64-token steps in turn.
+template <int D, int FMT, int BLOCK, int G>
+__global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams p) {
+  constexpr int NQ = D / 128;          // quads of four 32-dim groups (128 dims each)
+  constexpr int BPQ = 128 / BLOCK;     // quantisation blocks per quad
+  constexpr int NBLK = D / BLOCK;
+  static_assert(G * BPQ == 16, "one 16-column (head, block) set per quad");
+  constexpr int ROWB = 3 * D / 8;
+  constexpr int MB = FMT == kFmtSymF32 ? 4 : 2;      // bytes per metadata entry
+  constexpr int MDW = NBLK * MB / 4;                 // metadata dwords per token
+  constexpr int NBQ = 8;               // 16-dim output blocks per quad
+  constexpr int DPL = D / 64;          // value groups per lane and tile
+  constexpr int UPB = 4 / BPQ;         // useful P.V rows per lane and 16-dim block
+  constexpr int NU = G * D / 256;      // query elements per thread in the prologue
+  constexpr int UB0 = 4 * 128 * 64;    // per-wave value rows of one quad
+  constexpr int UB1 = 4 * G * D * 4;   // wave partials in the final combine
+  constexpr int UB = UB0 > UB1 ? UB0 : UB1;
+  static_assert(G * D * 7 <= UB, "prologue buffers fit the shared region");
+  constexpr bool ASYM = FMT == kFmtAsym;
+  constexpr int NS = ASYM ? 2 : 1;     // decoded metadata floats per entry: s (, z)
+  constexpr int MST = kStep + 4;       // padded LDS row of one block's metadata floats
+  using Raw = StepRaw<NQ, DPL, MDW>;
+
+  // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
+  __shared__ __align__(16) uint8_t u_s[UB];
+  __shared__ __align__(16) uint8_t wq_s[4][NQ][3][16][kStep];   // weight digits per row
+  __shared__ __align__(16) float mf_s[4][2][NBLK][NS][MST];     // [key/value][block][s, z][token]
+  __shared__ int32_t wsum_s[4][NQ][16];
+  __shared__ float wsig_s[4][NQ][16];
+  __shared__ float alpha_s[4][G];
+  __shared__ float cm_s[4][G], cl_s[4][G];
+  __shared__ float cob_s[4][G][NBLK];
+  __shared__ int32_t qds_s[G][NBLK][4];              // per (head, block): sum q, hi, mid, lo
+  __shared__ uint32_t qam_s[G];                      // per head: max |q1| (float bits)
+
+  const int split = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const size_t unit = static_cast<size_t>(b) * p.hkv + hk;
+
+  // ---- q1 = U q for the G heads of the group; 24-bit fixed point per head
+  float(*q_s)[D] = reinterpret_cast<float(*)[D]>(u_s);
+  uint8_t(*qd_s)[G][D] = reinterpret_cast<uint8_t(*)[G][D]>(u_s + G * D * 4);
+  const size_t qoff = (static_cast<size_t>(b) * p.hq + static_cast<size_t>(hk) * G) * D;
+  for (int e = tid; e < G * D; e += 256) {
+    const int jd = e % D;
+    float x = p.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qoff + e])
+                        : reinterpret_cast<const float*>(p.q)[qoff + e];
+    if (p.rotation == kRotSign) x *= p.rot[jd];
+    q_s[e / D][jd] = x;
+  }
+  if (tid < G) qam_s[tid] = 0u;
+  __syncthreads();
+  for (int hs = 1; hs < D; hs <<= 1) {
+    for (int e = tid; e < G * D / 2; e += 256) {
+      const int h = e / (D / 2), pi = e % (D / 2);
+      const int i = (pi / hs) * 2 * hs + (pi % hs);
+      const float a = q_s[h][i], c = q_s[h][i + hs];
+      q_s[h][i] = a + c;
+      q_s[h][i + hs] = a - c;
+    }
+    __syncthreads();
+  }
+  const float cn = rsqrtf(static_cast<float>(D));
+  float yq[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    // a wave's 64 consecutive elements belong to one head (64 | D)
+    const int e = tid + 256 * u, h = e / D, jd = e % D;
+    float y;
+    if (p.rotation == kRotSo4) {
+      const float* R = p.rot + 16 * (jd >> 2) + 4 * (jd & 3);
+      const float* xs = &q_s[h][jd & ~3];
+      y = R[0] * xs[0] + R[1] * xs[1] + R[2] * xs[2] + R[3] * xs[3];
+    } else {
+      y = q_s[h][jd];
+    }
+    yq[u] = y * cn;
+    const float am = wave_max_fast(fabsf(yq[u]));
+    if (lane == 0) atomicMax(&qam_s[h], __float_as_uint(am));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int e = tid + 256 * u, h = e / D, jd = e % D;
+    const float am = __uint_as_float(qam_s[h]);
+    const float inv = am > 0.0f ? static_cast<float>(kQMax) / am : 0.0f;
+    int qi = static_cast<int>(__builtin_rintf(yq[u] * inv));
+    qi = qi > kQMax ? kQMax : (qi < -kQMax ? -kQMax : qi);
+    int hi, mi, lo;
+    digits_q(qi, hi, mi, lo);
+    qd_s[0][h][jd] = static_cast<uint8_t>(hi);
+    qd_s[1][h][jd] = static_cast<uint8_t>(mi);
+    qd_s[2][h][jd] = static_cast<uint8_t>(lo);
+    // block sums over the BLOCK consecutive lanes of the block
+    int s0 = qi, s1 = hi, s2 = mi, s3 = lo;
+#pragma unroll
+    for (int m = 1; m < BLOCK; m <<= 1) {
+      s0 += __shfl_xor(s0, m, 64);
+      s1 += __shfl_xor(s1, m, 64);
+      s2 += __shfl_xor(s2, m, 64);
+      s3 += __shfl_xor(s3, m, 64);
+    }
+    if (jd % BLOCK == 0) {
+      qds_s[h][jd / BLOCK][0] = s0;
+      qds_s[h][jd / BLOCK][1] = s1;
+      qds_s[h][jd / BLOCK][2] = s2;
+      qds_s[h][jd / BLOCK][3] = s3;
+    }
+  }
+  __syncthreads();
+
+  // ---- lane roles
+  const int j = lane & 15;             // QK column (head, block) / P.V row or dim
+  const int lq = lane >> 4;            // k-chunk of the MFMA operands
+  const int h = j / BPQ;               // head of this lane's QK column
+  const int bq = j % BPQ;              // block (within a quad) of this lane's QK column
+  const float am_h = __uint_as_float(qam_s[h]);
+  // base-2 logit per integer unit (kept positive: a zero query has all-zero logits)
+  const float c_logit = fmaxf((am_h / static_cast<float>(kQMax)) * kLog2e * cn, 1.0e-30f);
+  // QK B operands: digit d of q_h at dims 32 (4 qd + lq) + 16 c + e (e < 16), zero
+  // outside the column's block
+  v4i qb[NQ][2][3];
+  int cinit[NQ][3];
+  float qsum_f[NQ];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const int blk = qd * BPQ + bq;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int dim0 = 32 * (4 * qd + lq) + 16 * c;
+      const bool in_blk = dim0 / BLOCK == blk;       // 16 dims never straddle a block
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&qd_s[d][h][dim0]);
+        qb[qd][c][d] = in_blk ? v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                                    static_cast<int>(w.w)}
+                              : v4i{0, 0, 0, 0};
+      }
+    }
+    // symmetric codes are centred (u - 4) by the accumulator's initial value
+#pragma unroll
+    for (int d = 0; d < 3; ++d) cinit[qd][d] = ASYM ? 0 : -4 * qds_s[h][blk][1 + d];
+    qsum_f[qd] = static_cast<float>(qds_s[h][blk][0]);
+  }
+  __syncthreads();   // u_s is reused for value rows below
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float ob[NQ];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) ob[qd] = 0.0f;
+  float acc[NQ][NBQ][UPB];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb)
+#pragma unroll
+      for (int u = 0; u < UPB; ++u) acc[qd][nb][u] = 0.0f;
+
+  const int T = p.T;
+  const int ntiles = (T + kTile - 1) / kTile;
+  const int t_begin = split * p.tiles_per_split;   // even: splits hold whole steps
+  const int t_end = min(t_begin + p.tiles_per_split, ntiles);
+  // buffer resources of this (sequence, KV head); offsets carry the step base in the
+  // vector offset, so rows past T (and tiles past the last) read as zero
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_codes + unit * p.tcap * ROWB, static_cast<uint32_t>(T) * ROWB);
+  const __amdgpu_buffer_rsrc_t rkm = make_rsrc(
+      reinterpret_cast<const uint8_t*>(p.k_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
+  const __amdgpu_buffer_rsrc_t rvm = make_rsrc(
+      reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12,
+                                              static_cast<uint32_t>(ntiles) * D * 12);
+  const uint32_t koff = static_cast<uint32_t>(j * ROWB + 12 * lq);
+  uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
+  float(*mf)[NBLK][NS][MST] = mf_s[wave];
+
+  auto load_step = [&](Raw& r, int st) {
+    const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
+#pragma unroll
+    for (int hf = 0; hf < 4; ++hf) {
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 48 * qd), 0, 0);
+        r.kw[hf][qd][0] = w[0]; r.kw[hf][qd][1] = w[1]; r.kw[hf][qd][2] = w[2];
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * 12;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, tv + 12 * lane + 768 * k, 0, 0);
+        r.vw[tt][k][0] = w[0]; r.vw[tt][k][1] = w[1]; r.vw[tt][k][2] = w[2];
+      }
+    }
+    load_row<MDW>(rkm, (tok0 + lane) * (NBLK * MB), r.km);
+    load_row<MDW>(rvm, (tok0 + lane) * (NBLK * MB), r.vm);
+  };
+
+  auto compute_step = [&](const Raw& r, int st) {
+    const int base = st * kStep;
+    const bool tail = base + kStep > T;            // wave-uniform
+    // ---- metadata of token `lane`: decode once, to LDS as floats [block][s, z][token]
+#pragma unroll
+    for (int bb = 0; bb < NBLK; ++bb) {
+      float s, z;
+      meta_entry<FMT>(r.km, bb, s, z);
+      mf[0][bb][0][lane] = s;
+      if constexpr (ASYM) mf[0][bb][1][lane] = z;
+      meta_entry<FMT>(r.vm, bb, s, z);
+      mf[1][bb][0][lane] = s;
+      if constexpr (ASYM) mf[1][bb][1][lane] = z;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+    // ---- logits (integer units of c_logit): lane holds head h, tokens 16 hf + 4 lq + rr
+    float L[4][4];
+#pragma unroll
+    for (int hf = 0; hf < 4; ++hf) {
+      float val[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        uint32_t dk[8];
+        g32_to_bytes(r.kw[hf][qd][0], r.kw[hf][qd][1], r.kw[hf][qd][2], dk);
+        const v4i a0 = {static_cast<int>(dk[0]), static_cast<int>(dk[1]), static_cast<int>(dk[2]),
+                        static_cast<int>(dk[3])};
+        const v4i a1 = {static_cast<int>(dk[4]), static_cast<int>(dk[5]), static_cast<int>(dk[6]),
+                        static_cast<int>(dk[7])};
+        v4i c[3];
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          c[d] = v4i{cinit[qd][d], cinit[qd][d], cinit[qd][d], cinit[qd][d]};
+          c[d] = mfma64(a0, qb[qd][0][d], c[d]);
+          c[d] = mfma64(a1, qb[qd][1][d], c[d]);
+        }
+        const int blk = qd * BPQ + bq;
+        const float4 s4 = *reinterpret_cast<const float4*>(&mf[0][blk][0][16 * hf + 4 * lq]);
+        float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (ASYM) z4 = *reinterpret_cast<const float4*>(&mf[0][blk][NS - 1][16 * hf + 4 * lq]);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+        const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          // sum over the block of q (u - 4) (symmetric) or q u (asymmetric), exact
+          const int comb = combine3<16, 8>(c[0][rr], c[1][rr], c[2][rr]);
+          float v = __builtin_fmaf(sv[rr], static_cast<float>(comb), val[rr]);
+          if constexpr (ASYM) v = __builtin_fmaf(zv[rr], qsum_f[qd], v);
+          val[rr] = v;
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float v = val[rr];
+        v += dpp_xor1(v);                 // sum over the head's blocks (adjacent columns)
+        if constexpr (BPQ == 4) v += dpp_xor2(v);
+        L[hf][rr] = v;
+      }
+    }
+    if (tail) {
+#pragma unroll
+      for (int hf = 0; hf < 4; ++hf)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (base + 16 * hf + 4 * lq + rr >= T) L[hf][rr] = -INFINITY;
+    }
+    // ---- online softmax per head (base 2), lazy maximum
+    float tmax = L[0][0];
+#pragma unroll
+    for (int hf = 0; hf < 4; ++hf)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) tmax = fmaxf(tmax, L[hf][rr]);
+    tmax = fmaxf(tmax, swz_xor16(tmax));
+    tmax = fmaxf(tmax, xor32f(tmax));
+    tmax *= c_logit;                      // finite: every step holds a valid token
+    if (__any(tmax > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) ob[qd] *= alpha;
+      m_run = m_new;
+      if (lq == 0 && bq == 0) alpha_s[wave][h] = alpha;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
+      // P.V row 4 lq + u BPQ + (block) belongs to head (4 lq + u BPQ) / BPQ
+#pragma unroll
+      for (int u = 0; u < UPB; ++u) {
+        const float al = alpha_s[wave][(4 * lq + u * BPQ) / BPQ];
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+          for (int nb = 0; nb < NBQ; ++nb) acc[qd][nb][u] *= al;
+      }
+    }
+    float pr[4][4];
+#pragma unroll
+    for (int hf = 0; hf < 4; ++hf)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        pr[hf][rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[hf][rr], c_logit, -m_run));
+        l_run += pr[hf][rr];
+      }
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      // ---- weights w = p s_v of row (h, bq) as 21-bit integers, 7-bit digits
+      const int blk = qd * BPQ + bq;
+      float w[4][4];
+      float wm = 0.0f;
+#pragma unroll
+      for (int hf = 0; hf < 4; ++hf) {
+        const float4 s4 = *reinterpret_cast<const float4*>(&mf[1][blk][0][16 * hf + 4 * lq]);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+        float zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (ASYM) {
+          const float4 z4 = *reinterpret_cast<const float4*>(&mf[1][blk][NS - 1][16 * hf + 4 * lq]);
+          zv[0] = z4.x; zv[1] = z4.y; zv[2] = z4.z; zv[3] = z4.w;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          w[hf][rr] = pr[hf][rr] * sv[rr];          // zero past T (scale reads as zero)
+          if constexpr (ASYM) ob[qd] = __builtin_fmaf(pr[hf][rr], zv[rr], ob[qd]);
+          wm = fmaxf(wm, w[hf][rr]);
+        }
+      }
+      wm = fmaxf(wm, swz_xor16(wm));
+      wm = fmaxf(wm, xor32f(wm));
+      // w winv + 1/2 stays below kW7 (rcp is within an ulp), so truncation rounds
+      const float winv = wm > 1.0e-30f ? static_cast<float>(kW7 - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
+      int ws = 0;
+#pragma unroll
+      for (int hf = 0; hf < 4; ++hf) {
+        uint32_t wi[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          wi[rr] = static_cast<uint32_t>(__builtin_fmaf(w[hf][rr], winv, 0.5f));
+          if constexpr (!ASYM) ws += static_cast<int>(wi[rr]);
+        }
+        uint8_t* row = &wq_s[wave][qd][0][j][0];
+        const int off = 16 * slot16(hf, j) + 4 * lq;
+        *reinterpret_cast<uint32_t*>(row + off) =
+            bytes4(wi[0] >> 14, wi[1] >> 14, wi[2] >> 14, wi[3] >> 14);
+        *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) =
+            bytes4(__builtin_amdgcn_ubfe(wi[0], 7, 7), __builtin_amdgcn_ubfe(wi[1], 7, 7),
+                   __builtin_amdgcn_ubfe(wi[2], 7, 7), __builtin_amdgcn_ubfe(wi[3], 7, 7));
+        *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) =
+            bytes4(wi[0] & 127u, wi[1] & 127u, wi[2] & 127u, wi[3] & 127u);
+      }
+      if constexpr (!ASYM) {
+        ws += xor16i(ws);
+        ws += xor32i(ws);
+      }
+      if (lq == 0) {
+        wsum_s[wave][qd][j] = 4 * ws;             // centring of (u - 4); zero when asymmetric
+        wsig_s[wave][qd][j] = wm * (1.0f / static_cast<float>(kW7 - 1));
+      }
+      // ---- value rows of this quad: [dim][64 tokens] bytes, 16-byte chunks rotated
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int rrow = lane + 64 * kk;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          uint32_t dv[8];
+          const uint32_t* g = r.vw[tt][2 * qd + kk];
+          g32_to_bytes(g[0], g[1], g[2], dv);
+          *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt, rrow)) =
+              make_uint4(dv[0], dv[1], dv[2], dv[3]);
+          *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt + 1, rrow)) =
+              make_uint4(dv[4], dv[5], dv[6], dv[7]);
+        }
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
+      // ---- P.V: rows (head, block), K = the step's 64 tokens, 16 dims per instruction
+      v4i a[3];
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        const uint4 x = *reinterpret_cast<const uint4*>(&wq_s[wave][qd][d][j][16 * slot16(lq, j)]);
+        a[d] = v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
+      }
+      int wcen[BPQ][UPB];
+      float wsg[BPQ][UPB];
+#pragma unroll
+      for (int bb = 0; bb < BPQ; ++bb)
+#pragma unroll
+        for (int u = 0; u < UPB; ++u) {
+          const int prow = 4 * lq + u * BPQ + bb;
+          wcen[bb][u] = ASYM ? 0 : wsum_s[wave][qd][prow];
+          wsg[bb][u] = wsig_s[wave][qd][prow];
+        }
+#pragma unroll
+      for (int nb = 0; nb < NBQ; ++nb) {
+        const int bqn = (16 * nb) / BLOCK;          // block (within the quad) of these dims
+        const int rrow = 16 * nb + j;
+        const uint4 x = *reinterpret_cast<const uint4*>(vrow + rrow * 64 + 16 * slot16(lq, rrow));
+        const v4i bv = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
+        const v4i z = {0, 0, 0, 0};
+        const v4i e0 = mfma64(a[0], bv, z);
+        const v4i e1 = mfma64(a[1], bv, z);
+        const v4i e2 = mfma64(a[2], bv, z);
+#pragma unroll
+        for (int u = 0; u < UPB; ++u) {
+          const int rr = u * BPQ + bqn;             // C row 4 lq + rr = (head, block bqn)
+          const int ai = combine3<14, 7>(e0[rr], e1[rr], e2[rr]) - wcen[bqn][u];
+          acc[qd][nb][u] = __builtin_fmaf(wsg[bqn][u], static_cast<float>(ai), acc[qd][nb][u]);
+        }
+      }
+      // the next quad or step overwrites this wave's LDS rows
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+
+  // (past the split's end the prefetch reloads its last step)
+  const int s_begin = t_begin / 2;
+  const int s_end = (t_end + 1) / 2;
+  Raw ra, rb;
+  int st = s_begin + wave;
+  if (st < s_end) load_step(ra, st);
+  while (st < s_end) {
+    load_step(rb, min(st + 4, s_end - 1));
+    compute_step(ra, st);
+    st += 4;
+    if (st >= s_end) break;
+    load_step(ra, min(st + 4, s_end - 1));
+    compute_step(rb, st);
+    st += 4;
+  }
+
+  // ---- combine the four waves; partials per query head
+  l_run += swz_xor16(l_run);
+  l_run += xor32f(l_run);
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    ob[qd] += swz_xor16(ob[qd]);
+    ob[qd] += xor32f(ob[qd]);
+  }
+  __syncthreads();   // every wave is done with its value rows
+  float* cacc = reinterpret_cast<float*>(u_s);      // [4][G][D]
+  if (lq == 0 && bq == 0) {
+    cm_s[wave][h] = m_run;
+    cl_s[wave][h] = l_run;
+  }
+  if (lq == 0) {
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) cob_s[wave][h][qd * BPQ + bq] = ob[qd];
+  }
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb)
+#pragma unroll
+      for (int u = 0; u < UPB; ++u) {
+        const int hh = (4 * lq + u * BPQ) / BPQ;
+        cacc[(wave * G + hh) * D + 128 * qd + 16 * nb + j] = acc[qd][nb][u];
+      }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D, dim = e % D;
+    const float mx = fmaxf(fmaxf(cm_s[0][hh], cm_s[1][hh]), fmaxf(cm_s[2][hh], cm_s[3][hh]));
+    float a = 0.0f, l = 0.0f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        const float al = __builtin_amdgcn_exp2f(cm_s[wv][hh] - mx);
+        a += al * (cacc[(wv * G + hh) * D + dim] + cob_s[wv][hh][dim / BLOCK]);
+        l += al * cl_s[wv][hh];
+      }
+    }
+    const size_t hq = static_cast<size_t>(hk) * G + hh;
+    float* out = p.ws + ((static_cast<size_t>(b) * p.hq + hq) * p.nsplit + split) * (D + 2);
+    out[dim] = a;
+    if (dim == 0) {
+      out[D] = mx;
+      out[D + 1] = l;
+    }
+  }
+}
+
+template <int D, int FMT, int BLOCK, int G>
+void launch_t(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL((decode_grouped_kernel<D, FMT, BLOCK, G>), grid, dim3(256), 0, s, e0, e1, 0, p);
+}
+
+template <int D, int BLOCK, int G>
+void launch_fmt(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.quant == kQuantAsym) launch_t<D, kFmtAsym, BLOCK, G>(p, grid, s, e0, e1);
+  else if (p.scale_dtype == kScaleF32) launch_t<D, kFmtSymF32, BLOCK, G>(p, grid, s, e0, e1);
+  else launch_t<D, kFmtSymF16, BLOCK, G>(p, grid, s, e0, e1);
+}
+
+template <int D>
+bool launch_d(const DecodeParams& p, int group, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.block == 32 && group == 4) {
+    launch_fmt<D, 32, 4>(p, grid, s, e0, e1);
+    return true;
+  }
+  if (p.block == 64 && group == 8) {
+    launch_fmt<D, 64, 8>(p, grid, s, e0, e1);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+bool grouped_decode_supported(int d, int block, int group) {
+  return (d == 128 || d == 256) && ((block == 32 && group == 4) || (block == 64 && group == 8));
+}
+
+hipError_t launch_decode_grouped(const DecodeParams& p, int batch, int d, hipStream_t s, hipEvent_t e0,
+                                 hipEvent_t e1) {
+  if (p.nsplit < 1 || p.nsplit > kMaxSplitsDev) return hipErrorInvalidValue;
+  if (p.hkv < 1 || p.hq % p.hkv != 0 || p.tiles_per_split % 2 != 0) return hipErrorInvalidValue;
+  const int group = p.hq / p.hkv;
+  if (!grouped_decode_supported(d, p.block, group)) return hipErrorInvalidValue;
+  const dim3 grid(p.nsplit, p.hkv, batch);
+  bool ok = false;
+  if (d == 128) ok = launch_d<128>(p, group, grid, s, e0, e1);
+  else ok = launch_d<256>(p, group, grid, s, e0, e1);
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace okv

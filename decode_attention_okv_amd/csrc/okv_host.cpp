@@ -54,8 +54,11 @@ int validate_shape(const okv_config* c) {
   // valid, but only these are built
   if (c->head_dim != 128 && c->head_dim != 256) return OKV_E_UNSUPPORTED;
   if (c->block % 32 != 0) return OKV_E_UNSUPPORTED;
-  // index arithmetic in the kernels uses 32-bit token counts
-  if (static_cast<int64_t>(c->max_tokens) * c->head_dim > (int64_t{1} << 40)) return OKV_E_UNSUPPORTED;
+  // the kernels address one (sequence, KV head) slice of a cache buffer with 32-bit
+  // byte offsets (buffer resources): the packed codes of a slice stay below 4 GiB
+  if (static_cast<int64_t>(c->max_tokens) * (3 * c->head_dim / 8) >= (int64_t{1} << 32)) {
+    return OKV_E_UNSUPPORTED;
+  }
   return OKV_OK;
 }
 
@@ -81,6 +84,7 @@ struct okv_handle {
   float* d_ws = nullptr;
   int32_t len = 0;
   int32_t splits = 0;  // 0 = automatic
+  int32_t kernel = OKV_DECODE_AUTO;
   bool timing = false;
   std::vector<TimingSlot> slots;
   int recorded = 0;
@@ -88,13 +92,25 @@ struct okv_handle {
 
 namespace {
 
+bool grouped_built(const okv_config& c) {
+  return okv::grouped_decode_supported(c.head_dim, c.block, c.num_q_heads / c.num_kv_heads);
+}
+
+// OKV_DECODE_PER_HEAD or OKV_DECODE_GROUPED: the kernel okv_decode_attn launches.
+int decode_kernel_of(const okv_handle* h) {
+  if (h->kernel == OKV_DECODE_PER_HEAD) return OKV_DECODE_PER_HEAD;
+  return grouped_built(h->cfg) ? OKV_DECODE_GROUPED : OKV_DECODE_PER_HEAD;
+}
+
 // Split count and tiles per split for a cache of T tokens: every split holds a
 // whole number of decode steps (kStepTiles tiles) and none is empty.
 int choose_splits(const okv_handle* h, int32_t T, int* tiles_per_split) {
   const int ntiles = (T + okv::kTile - 1) / okv::kTile;
   int s = h->splits;
   if (s <= 0) {
-    const int units = h->cfg.batch * h->cfg.num_q_heads;
+    // workgroups per split: one per query head, or one per KV head when grouped
+    const int heads = decode_kernel_of(h) == OKV_DECODE_GROUPED ? h->cfg.num_kv_heads : h->cfg.num_q_heads;
+    const int units = h->cfg.batch * heads;
     s = (kTargetGroups + units - 1) / units;
   }
   if (s > kMaxSplits) s = kMaxSplits;
@@ -281,10 +297,12 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
   TimingSlot* ts = nullptr;
   if (h->timing && h->recorded < static_cast<int>(h->slots.size())) ts = &h->slots[h->recorded++];
-  if (okv::launch_decode(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr, ts ? ts->e1 : nullptr) !=
-      hipSuccess) {
-    return OKV_E_HIP;
-  }
+  const hipError_t le = decode_kernel_of(h) == OKV_DECODE_GROUPED
+                           ? okv::launch_decode_grouped(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
+                                                        ts ? ts->e1 : nullptr)
+                           : okv::launch_decode(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
+                                                ts ? ts->e1 : nullptr);
+  if (le != hipSuccess) return OKV_E_HIP;
   if (okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr) !=
       hipSuccess) {
     return OKV_E_HIP;
@@ -319,6 +337,22 @@ int okv_max_splits(const okv_handle* h, int32_t* n) {
 int okv_get_splits(const okv_handle* h, int32_t* n) {
   if (h == nullptr || n == nullptr) return OKV_E_INVALID;
   *n = h->len > 0 ? choose_splits(h, h->len, nullptr) : 0;
+  return OKV_OK;
+}
+
+int okv_set_decode_kernel(okv_handle* h, int32_t kind) {
+  if (h == nullptr) return OKV_E_INVALID;
+  if (kind != OKV_DECODE_AUTO && kind != OKV_DECODE_PER_HEAD && kind != OKV_DECODE_GROUPED) {
+    return OKV_E_INVALID;
+  }
+  if (kind == OKV_DECODE_GROUPED && !grouped_built(h->cfg)) return OKV_E_UNSUPPORTED;
+  h->kernel = kind;
+  return OKV_OK;
+}
+
+int okv_get_decode_kernel(const okv_handle* h, int32_t* kind) {
+  if (h == nullptr || kind == nullptr) return OKV_E_INVALID;
+  *kind = decode_kernel_of(h);
   return OKV_OK;
 }
 

@@ -55,4 +55,11 @@ hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s,
 hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
+// Grouped decode (one workgroup per KV head serves its whole query group on MFMA):
+// built for head_dim 128/256 with (group 4, block 32) or (group 8, block 64).  Grid
+// (nsplit, hkv, batch); writes the same workspace as launch_decode.
+bool grouped_decode_supported(int d, int block, int group);
+hipError_t launch_decode_grouped(const DecodeParams& p, int batch, int d, hipStream_t s,
+                                 hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
 }  // namespace okv

@@ -103,7 +103,8 @@ typedef struct okv_config {
   int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads */
   int32_t num_kv_heads;  /* >= 1 */
   int32_t head_dim;      /* d: power of two, 4 | d; this build: 128 or 256 */
-  int32_t max_tokens;    /* cache capacity per sequence, multiple of 32 */
+  int32_t max_tokens;    /* cache capacity per sequence, multiple of 32; this build:
+                          * max_tokens * 3 * head_dim / 8 < 2^32 */
   int32_t block;         /* quantisation block m: m | d, 8 | m; this build: 32 or 64 */
   int32_t quant;         /* okv_quant */
   int32_t scale_dtype;   /* OKV_DT_F32 or OKV_DT_F16 (SYM3); OKV_DT_E4M3 (ASYM3) */
@@ -178,6 +179,23 @@ int okv_get_splits(const okv_handle* h, int32_t* n);
  * summed kernel milliseconds, then clears the record. */
 int okv_timing_enable(okv_handle* h, int32_t enable);
 int okv_timing_read(okv_handle* h, int32_t* calls, double* attn_ms, double* reduce_ms);
+
+/* Attention kernel of okv_decode_attn.  OKV_DECODE_PER_HEAD: one workgroup per
+ * (split, sequence, query head) reads the packed cache of its KV head.
+ * OKV_DECODE_GROUPED: one workgroup per (split, sequence, KV head) reads the packed
+ * cache once for the whole query group and computes Q.K and P.V on int8 matrix
+ * cores; built for query group 4 with block 32 and query group 8 with block 64.
+ * OKV_DECODE_AUTO (default) takes the grouped kernel where it is built, else the
+ * per-head one.  okv_set_decode_kernel returns OKV_E_UNSUPPORTED for
+ * OKV_DECODE_GROUPED on other configurations; okv_get_decode_kernel reports the
+ * kernel the next call will use (PER_HEAD or GROUPED). */
+typedef enum okv_decode_kernel {
+  OKV_DECODE_AUTO = 0,
+  OKV_DECODE_PER_HEAD = 1,
+  OKV_DECODE_GROUPED = 2
+} okv_decode_kernel;
+int okv_set_decode_kernel(okv_handle* h, int32_t kind);
+int okv_get_decode_kernel(const okv_handle* h, int32_t* kind);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,11 @@ def base(**kw):
     return okv.make_config(**args)
 
 
+def test_largest_slice_is_accepted():
+    st, lay = okv.okv_layout(base(max_tokens=89478464))               # 2^32 - 1024 bytes
+    assert st == okv.OKV_OK and lay.k_codes_bytes == 2 * 2 * 89478464 * 48   # batch 2 x 2 KV heads
+
+
 def test_layout_sizes():
     st, lay = okv.okv_layout(base())
     assert st == okv.OKV_OK
@@ -62,6 +67,9 @@ def test_layout_sizes():
     (dict(quant="asym", scale_dtype="f16"), okv.OKV_E_UNSUPPORTED),
     (dict(head_dim=64, rot_params=[1.0] * 64), okv.OKV_E_UNSUPPORTED),
     (dict(block=16), okv.OKV_E_UNSUPPORTED),
+    # one (sequence, KV head) slice of packed codes must stay below 4 GiB
+    (dict(max_tokens=89478496), okv.OKV_E_UNSUPPORTED),              # 48 B rows: 2^32 + 512
+    (dict(max_tokens=44739264, head_dim=256, rot_params=[1.0] * 256), okv.OKV_E_UNSUPPORTED),
 ])
 def test_rejections(kw, status):
     cfg = base(**{k: v for k, v in kw.items() if k != "abi_version"})
@@ -96,4 +104,6 @@ def test_null_handle_calls():
     assert okv.okv_get_len(null)[0] == okv.OKV_E_INVALID
     assert okv.okv_set_splits(null, 4) == okv.OKV_E_INVALID
     assert okv.okv_timing_read(null)[0] == okv.OKV_E_INVALID
+    assert okv.okv_set_decode_kernel(null, 0) == okv.OKV_E_INVALID
+    assert okv.okv_get_decode_kernel(null)[0] == okv.OKV_E_INVALID
     assert okv.okv_strerror(okv.OKV_E_CAPACITY) == "cache capacity exceeded"

@@ -86,10 +86,11 @@ def check_units(cache, wl, units, k_all, v_all, p32, u, qsteps):
             assert err <= TOL
 
 
-def prefill_and_step(wl, steps=1):
+def prefill_and_step(wl, steps=1, also_per_head=False):
     """Prefill wl.tokens tokens in one okv_write, then `steps` x (append one token,
-    decode), as the benchmark does.  Returns the cache, all keys/values and the
-    decode calls [(t, q, out_host)]."""
+    decode), as the benchmark does (automatic kernel and split count).  With
+    also_per_head, the last query is decoded once more with the per-head kernel.
+    Returns the cache, all keys/values and the decode calls [(t, q, out_host)]."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     p32, u = params_of(wl)
@@ -107,9 +108,15 @@ def prefill_and_step(wl, steps=1):
         ks.append(kn)
         vs.append(vn)
         q = okv_synth.queries(wl, i, device="cuda")
-        say(wl.name, "okv_decode_attn T", cache.length, "splits", cache.splits())
+        say(wl.name, "okv_decode_attn", cache.decode_kernel(), "T", cache.length, "splits", cache.splits())
         out = cache.decode_attn(q)
         calls.append((cache.length, q, out))
+    if also_per_head and calls:
+        cache.set_decode_kernel("per_head")
+        t, q, _ = calls[-1]
+        say(wl.name, "okv_decode_attn per_head T", t, "splits", cache.splits())
+        calls.append((t, q, cache.decode_attn(q)))
+        cache.set_decode_kernel("auto")
     torch.cuda.synchronize()
     calls = [(t, q, o.cpu().numpy()) for t, q, o in calls]
     k_all = torch.cat(ks, 1) if steps else k
@@ -124,7 +131,7 @@ def prefill_and_step(wl, steps=1):
 ])
 def test_fullsize_prefill_decode(name, units):
     wl = okv_synth.workload(name)
-    cache, k, v, p32, u, calls = prefill_and_step(wl, steps=1)
+    cache, k, v, p32, u, calls = prefill_and_step(wl, steps=1, also_per_head=wl.group > 1)
     check_random_tokens(cache, wl, k, v, p32)
     check_units(cache, wl, units, k, v, p32, u, calls)
     cache.close()

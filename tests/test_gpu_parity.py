@@ -32,7 +32,14 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def run_case(wl, t, chunks, splits=0, steps=0):
+def expected_kernel(wl, kernel):
+    if kernel != "auto":
+        return kernel
+    grouped = wl.d in (128, 256) and (wl.group, wl.block) in ((4, 32), (8, 64))
+    return "grouped" if grouped else "per_head"
+
+
+def run_case(wl, t, chunks, splits=0, steps=0, kernel="auto"):
     """Write t tokens in `chunks`, decode, then `steps` x (append 1, decode).
     Checks every unit's bytes and every decode output against the oracle."""
     _need_gpu()
@@ -40,6 +47,8 @@ def run_case(wl, t, chunks, splits=0, steps=0):
     cache = make_cache(wl, round_up(t + steps + 1, 32), p32)
     if splits:
         cache.set_splits(splits)
+    cache.set_decode_kernel(kernel)
+    assert cache.decode_kernel() == expected_kernel(wl, kernel)
     k, v = okv_synth.kv_tokens(wl, 0, t, device="cuda")
     pos = 0
     for n in chunks:
@@ -58,7 +67,7 @@ def run_case(wl, t, chunks, splits=0, steps=0):
             v_all = torch.cat([v_all, vn], 1)
         tt = t + step
         q = okv_synth.queries(wl, step, device="cuda")
-        say(wl.name, "okv_decode_attn", "T", tt, "splits", cache.splits())
+        say(wl.name, "okv_decode_attn", cache.decode_kernel(), "T", tt, "splits", cache.splits())
         out = cache.decode_attn(q)
         torch.cuda.synchronize()
         out_h = out.cpu().numpy()
@@ -84,29 +93,41 @@ def run_case(wl, t, chunks, splits=0, steps=0):
     return errs
 
 
-@pytest.mark.parametrize("name", list(REDUCED))
-def test_write_decode_reduced(name):
+# every workload with the automatic kernel choice; the grouped workloads also
+# with the per-head kernel forced
+REDUCED_CASES = [(n, "auto") for n in REDUCED] + [
+    (n, "per_head") for n in ("gqa_h32kv8_t32k", "gqa_b16h64kv8_t128k_asym", "so4_d256_b32_t8k")]
+
+
+@pytest.mark.parametrize("name,kernel", REDUCED_CASES)
+def test_write_decode_reduced(name, kernel):
     over, t, chunks = REDUCED[name]
     wl = okv_synth.workload(name).with_(**over)
-    run_case(wl, t, chunks, steps=2 if name == "gqa_h32kv8_t32k" else 0)
+    run_case(wl, t, chunks, steps=2 if name == "gqa_h32kv8_t32k" else 0, kernel=kernel)
 
 
 @pytest.mark.parametrize("splits", [1, 3, 16])
 def test_split_count_invariance(splits):
     wl = okv_synth.workload("mha_b4h32_t128k").with_(batch=1, hq=4, hkv=4)
     run_case(wl, 1111, [1111], splits=splits)
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=8, hkv=2)
+    run_case(wl, 1111, [1111], splits=splits, kernel="grouped")
 
 
 @pytest.mark.parametrize("t,chunks", [(1, [1]), (32, [32]), (33, [1, 31, 1]), (64, [20, 20, 24]),
                                       (97, [97])])
 def test_small_lengths(t, chunks):
     wl = okv_synth.workload("gqa_b16h64kv8_t128k_asym").with_(batch=1, hq=16, hkv=2)
-    run_case(wl, t, chunks)
+    run_case(wl, t, chunks, kernel="grouped")
+    run_case(wl, t, chunks, kernel="per_head")
+    wl = okv_synth.workload("so4_d256_b32_t8k").with_(batch=1, hq=4, hkv=1)
+    run_case(wl, t, chunks, kernel="grouped")
     wl = okv_synth.workload("tiny_d128_t256")
     run_case(wl, t, chunks)
 
 
-def test_degenerate_inputs():
+@pytest.mark.parametrize("kernel", ["grouped", "per_head"])
+def test_degenerate_inputs(kernel):
     # all-zero keys: every logit is equal, the output is the mean of the values;
     # constant values: H_d of a constant vector is one spike per vector
     _need_gpu()
@@ -115,10 +136,11 @@ def test_degenerate_inputs():
     p32, u = params_of(wl)
     t = 70
     cache = make_cache(wl, 96, p32)
+    cache.set_decode_kernel(kernel)
     k = torch.zeros((1, t, 1, wl.d), dtype=torch.bfloat16, device="cuda")
     v = torch.full((1, t, 1, wl.d), 0.5, dtype=torch.bfloat16, device="cuda")
     v[0, ::3] = -2.0
-    say("degenerate okv_write")
+    say("degenerate okv_write", kernel)
     cache.write(k, v)
     q = okv_synth.queries(wl, 0, device="cuda")
     out = cache.decode_attn(q).cpu().numpy()
@@ -140,6 +162,9 @@ def test_error_paths():
     q = okv_synth.queries(wl, 0, device="cuda")
     out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
     say("error paths")
+    assert okv.okv_set_decode_kernel(cache.handle, okv.DECODE_KERNEL["grouped"]) == okv.OKV_E_UNSUPPORTED
+    assert okv.okv_set_decode_kernel(cache.handle, 7) == okv.OKV_E_INVALID
+    assert cache.decode_kernel() == "per_head"
     assert okv.okv_decode_attn(cache.handle, q.data_ptr(), out.data_ptr()) == okv.OKV_E_INVALID
     k, v = okv_synth.kv_tokens(wl, 0, 65, device="cuda")
     assert okv.okv_write(cache.handle, k.data_ptr(), v.data_ptr(), 65) == okv.OKV_E_CAPACITY
