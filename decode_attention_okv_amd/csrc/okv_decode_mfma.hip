@@ -46,11 +46,14 @@ __device__ __forceinline__ v4i mfma64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// a * 2^sa + b * 2^sb + c in wrapping int32 arithmetic (the true value fits).
+// a * 2^sa + b * 2^sb + c in wrapping int32 arithmetic (the true value fits).  The
+// empty asm keeps the two shift-adds apart, so each maps to one v_lshl_add_u32
+// instead of two shifts and an add3.
 template <int SA, int SB>
 __device__ __forceinline__ int combine3(int a, int b, int c) {
-  return static_cast<int>((static_cast<uint32_t>(a) << SA) + (static_cast<uint32_t>(b) << SB) +
-                          static_cast<uint32_t>(c));
+  uint32_t t = (static_cast<uint32_t>(b) << SB) + static_cast<uint32_t>(c);
+  asm("" : "+v"(t));
+  return static_cast<int>((static_cast<uint32_t>(a) << SA) + t);
 }
 
 // Balanced base-256 digits: q = 65536 hi + 256 mi + lo, each in [-128, 127].
@@ -134,7 +137,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   static_assert(G * D * 7 <= UB, "prologue buffers fit the shared region");
   constexpr bool ASYM = FMT == kFmtAsym;
   constexpr int NS = ASYM ? 2 : 1;     // decoded metadata floats per entry: s (, z)
-  constexpr int MST = kStep + 4;       // padded LDS row of one block's metadata floats
+  // padded LDS row of one block's metadata floats: consecutive blocks start 16 banks
+  // apart, so the four-token reads of a quad's blocks never share a bank
+  constexpr int MST = ASYM ? 72 : 80;
   using Raw = StepRaw<NQ, DPL, MDW>;
 
   // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
@@ -293,30 +298,53 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
   float(*mf)[NBLK][NS][MST] = mf_s[wave];
 
-  auto load_step = [&](Raw& r, int st) {
+  // key groups of 16-token group hf
+  auto load_k = [&](Raw& r, int st, int hf) {
     const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
 #pragma unroll
-    for (int hf = 0; hf < 4; ++hf) {
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 48 * qd), 0, 0);
-        r.kw[hf][qd][0] = w[0]; r.kw[hf][qd][1] = w[1]; r.kw[hf][qd][2] = w[2];
-      }
+    for (int qd = 0; qd < NQ; ++qd) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 48 * qd), 0, 0);
+      r.kw[hf][qd][0] = w[0]; r.kw[hf][qd][1] = w[1]; r.kw[hf][qd][2] = w[2];
     }
+  };
+  // value groups of quad qd (dims 128 qd + lane + 64 kk) of both tiles
+  auto load_v = [&](Raw& r, int st, int qd) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * 12;
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) {
+      for (int k = 2 * qd; k < 2 * qd + 2; ++k) {
         const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, tv + 12 * lane + 768 * k, 0, 0);
         r.vw[tt][k][0] = w[0]; r.vw[tt][k][1] = w[1]; r.vw[tt][k][2] = w[2];
       }
     }
+  };
+  // value rows of quad qd to LDS: [dim][64 tokens] bytes, 16-byte chunks rotated
+  auto decode_v = [&](const Raw& r, int qd) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int rrow = lane + 64 * kk;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t dv[8];
+        const uint32_t* g = r.vw[tt][2 * qd + kk];
+        g32_to_bytes(g[0], g[1], g[2], dv);
+        *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt, rrow)) =
+            make_uint4(dv[0], dv[1], dv[2], dv[3]);
+        *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt + 1, rrow)) =
+            make_uint4(dv[4], dv[5], dv[6], dv[7]);
+      }
+    }
+  };
+  auto load_m = [&](Raw& r, int st) {
+    const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
     load_row<MDW>(rkm, (tok0 + lane) * (NBLK * MB), r.km);
     load_row<MDW>(rvm, (tok0 + lane) * (NBLK * MB), r.vm);
   };
 
-  auto compute_step = [&](const Raw& r, int st) {
+  // one step from the raw data in `r`; each part of `r` is refilled with step `nx`
+  // as soon as it has been consumed
+  auto compute_step = [&](Raw& r, int st, int nx) {
     const int base = st * kStep;
     const bool tail = base + kStep > T;            // wave-uniform
     // ---- metadata of token `lane`: decode once, to LDS as floats [block][s, z][token]
@@ -330,6 +358,10 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       mf[1][bb][0][lane] = s;
       if constexpr (ASYM) mf[1][bb][1][lane] = z;
     }
+    load_m(r, nx);
+    // values of the first quad go to LDS at once, so their registers refill early
+    decode_v(r, 0);
+    load_v(r, nx, 0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
     // ---- logits (integer units of c_logit): lane holds head h, tokens 16 hf + 4 lq + rr
@@ -341,6 +373,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       for (int qd = 0; qd < NQ; ++qd) {
         uint32_t dk[8];
         g32_to_bytes(r.kw[hf][qd][0], r.kw[hf][qd][1], r.kw[hf][qd][2], dk);
+        if (qd == NQ - 1) load_k(r, nx, hf);
         const v4i a0 = {static_cast<int>(dk[0]), static_cast<int>(dk[1]), static_cast<int>(dk[2]),
                         static_cast<int>(dk[3])};
         const v4i a1 = {static_cast<int>(dk[4]), static_cast<int>(dk[5]), static_cast<int>(dk[6]),
@@ -472,20 +505,10 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
         wsum_s[wave][qd][j] = 4 * ws;             // centring of (u - 4); zero when asymmetric
         wsig_s[wave][qd][j] = wm * (1.0f / static_cast<float>(kW7 - 1));
       }
-      // ---- value rows of this quad: [dim][64 tokens] bytes, 16-byte chunks rotated
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int rrow = lane + 64 * kk;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          uint32_t dv[8];
-          const uint32_t* g = r.vw[tt][2 * qd + kk];
-          g32_to_bytes(g[0], g[1], g[2], dv);
-          *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt, rrow)) =
-              make_uint4(dv[0], dv[1], dv[2], dv[3]);
-          *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt + 1, rrow)) =
-              make_uint4(dv[4], dv[5], dv[6], dv[7]);
-        }
+      if (qd > 0) {
+        // the previous quad's P.V is done with the value rows
+        decode_v(r, qd);
+        load_v(r, nx, qd);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_wave_barrier();
@@ -529,21 +552,19 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
     }
   };
 
-  // (past the split's end the prefetch reloads its last step)
+  // (past the split's end the prefetch reloads the wave's last step, from L2)
   const int s_begin = t_begin / 2;
   const int s_end = (t_end + 1) / 2;
-  Raw ra, rb;
+  Raw r;
   int st = s_begin + wave;
-  if (st < s_end) load_step(ra, st);
-  while (st < s_end) {
-    load_step(rb, min(st + 4, s_end - 1));
-    compute_step(ra, st);
-    st += 4;
-    if (st >= s_end) break;
-    load_step(ra, min(st + 4, s_end - 1));
-    compute_step(rb, st);
-    st += 4;
+  if (st < s_end) {
+    load_m(r, st);
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) load_v(r, st, qd);
+#pragma unroll
+    for (int hf = 0; hf < 4; ++hf) load_k(r, st, hf);
   }
+  for (; st < s_end; st += 4) compute_step(r, st, min(st + 4, s_end - 1));
 
   // ---- combine the four waves; partials per query head
   l_run += swz_xor16(l_run);

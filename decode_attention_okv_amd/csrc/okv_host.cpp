@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kMaxSplits = 256;      // split-K workspace capacity per (sequence, query head)
 constexpr int kTargetGroups = 2048;  // workgroups the automatic split count aims for
+constexpr int kMinSplitTiles = 32;   // automatic splits keep >= 4 two-tile steps per wave
 constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -112,6 +113,8 @@ int choose_splits(const okv_handle* h, int32_t T, int* tiles_per_split) {
     const int heads = decode_kernel_of(h) == OKV_DECODE_GROUPED ? h->cfg.num_kv_heads : h->cfg.num_q_heads;
     const int units = h->cfg.batch * heads;
     s = (kTargetGroups + units - 1) / units;
+    const int cap = ntiles / kMinSplitTiles;   // short caches: fewer, longer splits
+    if (s > cap) s = cap;
   }
   if (s > kMaxSplits) s = kMaxSplits;
   if (s > ntiles) s = ntiles;
