@@ -36,7 +36,7 @@ DECODE_KERNEL = {"auto": 0, "per_head": 1, "grouped": 2}
 EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror",
            "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
            "okv_get_splits", "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel",
-           "okv_get_decode_kernel")
+           "okv_get_decode_kernel", "okv_last_hip_error")
 
 
 class OkvConfig(ctypes.Structure):
@@ -70,6 +70,15 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m decode_attention_okv_amd.build`")
+    # One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64.so.7.  With
+    # torch loaded first, the dynamic linker resolves libokv's libamdhip64.so.7 to that
+    # same runtime, so tensors and handles share one device context.  Loaded the other
+    # way round, the process would hold two HIP runtimes, and the second one to start
+    # can fail to find the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     so = ctypes.CDLL(LIB_PATH)
     vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
     sig = {
@@ -78,6 +87,7 @@ def _load():
         "okv_decode_attn": (i32, [vp, vp, vp, vp]),
         "okv_destroy": (i32, [vp]),
         "okv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "okv_last_hip_error": (ctypes.c_char_p, []),
         "okv_layout": (i32, [P(OkvConfig), P(OkvLayout)]),
         "okv_get_len": (i32, [vp, P(i32)]),
         "okv_set_len": (i32, [vp, i32]),
@@ -102,7 +112,10 @@ lib = _load()
 class OkvError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {lib.okv_strerror(status).decode()} (status {status})")
+        msg = f"{where}: {lib.okv_strerror(status).decode()} (status {status})"
+        if status == OKV_E_HIP:
+            msg += f": {lib.okv_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 def _check(status: int, where: str) -> None:

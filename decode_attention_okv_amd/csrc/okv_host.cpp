@@ -22,6 +22,15 @@ constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// last HIP error that made a call on this thread fail (okv_last_hip_error)
+thread_local hipError_t g_last_hip = hipSuccess;
+
+bool hip_ok(hipError_t e) {
+  if (e == hipSuccess) return true;
+  g_last_hip = e;
+  return false;
+}
+
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 int meta_entry_bytes(const okv_config& c) {
@@ -195,14 +204,14 @@ int okv_create(const okv_config* cfg, okv_handle** out) {
   if (h == nullptr) return OKV_E_HIP;
   h->cfg = *cfg;
   h->cfg.rot_params = nullptr;  // the host copy is not kept
-  if (hipGetDevice(&h->device) != hipSuccess) {
+  if (!hip_ok(hipGetDevice(&h->device))) {
     delete h;
     return OKV_E_HIP;
   }
   const size_t ws_floats = static_cast<size_t>(cfg->batch) * cfg->num_q_heads * kMaxSplits * (d + 2);
-  if (hipMalloc(&h->d_rot, nrot * sizeof(float)) != hipSuccess ||
-      hipMemcpy(h->d_rot, rp, nrot * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMalloc(&h->d_ws, ws_floats * sizeof(float)) != hipSuccess) {
+  if (!hip_ok(hipMalloc(&h->d_rot, nrot * sizeof(float))) ||
+      !hip_ok(hipMemcpy(h->d_rot, rp, nrot * sizeof(float), hipMemcpyHostToDevice)) ||
+      !hip_ok(hipMalloc(&h->d_ws, ws_floats * sizeof(float)))) {
     if (h->d_rot) (void)hipFree(h->d_rot);
     if (h->d_ws) (void)hipFree(h->d_ws);
     delete h;
@@ -219,8 +228,8 @@ int okv_destroy(okv_handle* h) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->device);
   free_timing(h);
-  if (h->d_rot && hipFree(h->d_rot) != hipSuccess) st = OKV_E_HIP;
-  if (h->d_ws && hipFree(h->d_ws) != hipSuccess) st = OKV_E_HIP;
+  if (h->d_rot && !hip_ok(hipFree(h->d_rot))) st = OKV_E_HIP;
+  if (h->d_ws && !hip_ok(hipFree(h->d_ws))) st = OKV_E_HIP;
   (void)hipSetDevice(prev);
   delete h;
   return st;
@@ -254,8 +263,8 @@ int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* 
   p.eps = c.eps;
   const int tile1 = (h->len + n_new - 1) / okv::kTile;
   const int ntiles = tile1 - p.tile0 + 1;
-  if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
-  if (okv::launch_write(p, ntiles, c.batch, c.head_dim, static_cast<hipStream_t>(hip_stream)) != hipSuccess) {
+  if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
+  if (!hip_ok(okv::launch_write(p, ntiles, c.batch, c.head_dim, static_cast<hipStream_t>(hip_stream)))) {
     return OKV_E_HIP;
   }
   h->len += n_new;
@@ -297,7 +306,7 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   r.hq = c.num_q_heads;
   r.nsplit = nsplit;
   r.rotation = c.rotation;
-  if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
+  if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
   TimingSlot* ts = nullptr;
   if (h->timing && h->recorded < static_cast<int>(h->slots.size())) ts = &h->slots[h->recorded++];
   const hipError_t le = decode_kernel_of(h) == OKV_DECODE_GROUPED
@@ -305,9 +314,8 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
                                                         ts ? ts->e1 : nullptr)
                            : okv::launch_decode(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
                                                 ts ? ts->e1 : nullptr);
-  if (le != hipSuccess) return OKV_E_HIP;
-  if (okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr) !=
-      hipSuccess) {
+  if (!hip_ok(le)) return OKV_E_HIP;
+  if (!hip_ok(okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr))) {
     return OKV_E_HIP;
   }
   return OKV_OK;
@@ -343,6 +351,10 @@ int okv_get_splits(const okv_handle* h, int32_t* n) {
   return OKV_OK;
 }
 
+const char* okv_last_hip_error(void) {
+  return g_last_hip == hipSuccess ? "none" : hipGetErrorString(g_last_hip);
+}
+
 int okv_set_decode_kernel(okv_handle* h, int32_t kind) {
   if (h == nullptr) return OKV_E_INVALID;
   if (kind != OKV_DECODE_AUTO && kind != OKV_DECODE_PER_HEAD && kind != OKV_DECODE_GROUPED) {
@@ -361,12 +373,12 @@ int okv_get_decode_kernel(const okv_handle* h, int32_t* kind) {
 
 int okv_timing_enable(okv_handle* h, int32_t enable) {
   if (h == nullptr) return OKV_E_INVALID;
-  if (hipSetDevice(h->device) != hipSuccess) return OKV_E_HIP;
+  if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
   if (enable && h->slots.empty()) {
     h->slots.resize(kTimingSlots);
     for (auto& t : h->slots) {
-      if (hipEventCreate(&t.e0) != hipSuccess || hipEventCreate(&t.e1) != hipSuccess ||
-          hipEventCreate(&t.e2) != hipSuccess || hipEventCreate(&t.e3) != hipSuccess) {
+      if (!hip_ok(hipEventCreate(&t.e0)) || !hip_ok(hipEventCreate(&t.e1)) ||
+          !hip_ok(hipEventCreate(&t.e2)) || !hip_ok(hipEventCreate(&t.e3))) {
         return OKV_E_HIP;
       }
     }
@@ -383,9 +395,9 @@ int okv_timing_read(okv_handle* h, int32_t* calls, double* attn_ms, double* redu
   for (int i = 0; i < h->recorded; ++i) {
     TimingSlot& t = h->slots[i];
     float x = 0.0f, y = 0.0f;
-    if (hipEventSynchronize(t.e3) != hipSuccess) return OKV_E_HIP;
-    if (hipEventElapsedTime(&x, t.e0, t.e1) != hipSuccess) return OKV_E_HIP;
-    if (hipEventElapsedTime(&y, t.e2, t.e3) != hipSuccess) return OKV_E_HIP;
+    if (!hip_ok(hipEventSynchronize(t.e3))) return OKV_E_HIP;
+    if (!hip_ok(hipEventElapsedTime(&x, t.e0, t.e1))) return OKV_E_HIP;
+    if (!hip_ok(hipEventElapsedTime(&y, t.e2, t.e3))) return OKV_E_HIP;
     a += x;
     r += y;
   }

@@ -160,6 +160,9 @@ int okv_destroy(okv_handle* h);
 /* ---- auxiliary calls (not part of the method) ---- */
 
 const char* okv_strerror(int status);
+/* Text of the HIP runtime error behind the last OKV_E_HIP returned on the calling
+ * thread ("none" if there was none).  Static storage; not cleared by later calls. */
+const char* okv_last_hip_error(void);
 int okv_layout(const okv_config* cfg, okv_layout_info* info);
 /* Current sequence length of the handle. */
 int okv_get_len(const okv_handle* h, int32_t* len);
