@@ -8,9 +8,10 @@
 // hardware-fused transforms, third paragraph (asymmetric unsigned 3-bit codes per
 // 64-element sub-block with an FP8 scale and zero-point).
 //
-// Every float32 operation here is rounded on its own, in a fixed order, so the
-// result matches the bit specification exactly: contraction into fused
-// multiply-adds is disabled for this file.
+// Every float32 operation of the transform and the statistics is rounded on its
+// own, in a fixed order, so the result matches the bit specification exactly:
+// contraction into fused multiply-adds is disabled for this file (the explicit
+// fmaf calls below only serve the code rounding, where their exactness is used).
 #pragma clang fp contract(off)
 
 #include "okv_device.hpp"
@@ -19,64 +20,116 @@ namespace okv {
 
 namespace {
 
-// One workgroup owns one 32-token tile of one (sequence, KV head): it computes the
-// new tokens of the tile, rewrites the key rows of those tokens and the whole value
-// tile (old codes kept, unwritten slots zero).  Key and value vectors are spread
-// over D/8 lanes, 8 consecutive elements per lane.
-template <int D>
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
+
+// Distance from a half-integer below which the fast code rounding defers to the exact
+// one: the approximate quotient is within ~2e-6 of the exact one for |q| <= 8.
+constexpr float kNear = 0.5f - 0x1.0p-17f;
+
+// Four codes (integer-valued floats 0..7) as the bytes of one word.
+__device__ __forceinline__ uint32_t bytes_of(const float* u) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(u[0], 0, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(u[1], 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(u[2], 2, w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(u[3], 3, w);
+}
+
+// 32 codes as byte lanes (byte b of d[k] = code 4k+b) -> the 12-byte group.
+__device__ __forceinline__ void pack_g32(const uint32_t d[8], uint32_t& w0, uint32_t& w1, uint32_t& w2) {
+  w0 = d[0] | (d[1] << 3) | ((d[6] & 0x03030303u) << 6);
+  w1 = d[2] | (d[3] << 3) | ((d[7] & 0x03030303u) << 6);
+  w2 = d[4] | (d[5] << 3) | ((d[6] & 0x04040404u) << 4) | ((d[7] & 0x04040404u) << 5);
+}
+
+// Bits of a 12-byte group that hold the codes of tokens 0 .. n-1.
+__device__ __forceinline__ void keep_mask(int n, uint32_t& m0, uint32_t& m1, uint32_t& m2) {
+  m0 = m1 = m2 = 0u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int sh = 8 * b;
+    if (b < n) m0 |= 0x07u << sh;
+    if (4 + b < n) m0 |= 0x38u << sh;
+    if (24 + b < n) { m0 |= 0xC0u << sh; m2 |= 0x40u << sh; }
+    if (8 + b < n) m1 |= 0x07u << sh;
+    if (12 + b < n) m1 |= 0x38u << sh;
+    if (28 + b < n) { m1 |= 0xC0u << sh; m2 |= 0x80u << sh; }
+    if (16 + b < n) m2 |= 0x07u << sh;
+    if (20 + b < n) m2 |= 0x38u << sh;
+  }
+}
+
+// One workgroup owns one 32-token tile of one (sequence, KV head).  Its 64
+// four-lane groups take the 32 key and 32 value vectors of the tile's slots; lane r
+// of a group holds elements EPL r .. EPL r + EPL - 1 of the vector.  New slots are
+// quantised; key rows are stored straight from the lanes; value codes go through LDS
+// to be regrouped per dimension (old codes of earlier tokens are kept, slots after
+// the new tokens stay zero).
+template <int D, int BLOCK, bool ASYM>
 __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
-  constexpr int LPV = D / 8;      // lanes per vector
-  constexpr int VPP = 256 / LPV;  // vectors per pass of the workgroup
-  __shared__ uint8_t vt[kTile][D];
+  constexpr int EPL = D / 4;                          // elements per lane
+  constexpr int GPL = EPL / 32;                       // 32-code groups per lane
+  constexpr int BPL = EPL >= BLOCK ? EPL / BLOCK : 1; // quantisation blocks per lane
+  constexpr int LPB = BLOCK > EPL ? BLOCK / EPL : 1;  // lanes per block
+  constexpr int NBLK = D / BLOCK;
+  constexpr int BE = BLOCK < EPL ? BLOCK : EPL;       // a block's elements in one lane
+  __shared__ __align__(16) uint8_t vt[kTile][D];      // value codes u of the tile, [slot][dim]
 
   const int tile = p.tile0 + static_cast<int>(blockIdx.x);
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int tile_base = tile * kTile;
   const int s_lo = max(p.len - tile_base, 0);
   const int s_hi = min(p.len + p.n_new - tile_base, kTile);
-  const int nnew = s_hi - s_lo;
   const size_t unit = static_cast<size_t>(b) * p.hkv + h;
-  uint8_t* vtile = p.v_codes + (unit * p.ntile_cap + tile) * static_cast<size_t>(D) * 12;
-  const int nblk = D / p.block;
 
-  for (int i = tid; i < kTile * D / 4; i += 256) reinterpret_cast<uint32_t*>(&vt[0][0])[i] = 0u;
-  __syncthreads();
-  if (s_lo > 0) {
-    // tile already holds tokens 0 .. s_lo-1: keep their value codes
-    for (int j = tid; j < D; j += 256) {
-      const uint32_t* g = reinterpret_cast<const uint32_t*>(vtile + 12 * j);
-      const uint32_t w0 = g[0], w1 = g[1], w2 = g[2];
-      for (int i = 0; i < s_lo; ++i) vt[i][j] = static_cast<uint8_t>(g32_code(w0, w1, w2, i));
-    }
-  }
+  const int vi = tid >> 2, r = tid & 3;
+  const int tensor = vi >> 5, slot = vi & 31;
+  const bool active = slot >= s_lo && slot < s_hi;    // uniform over the four lanes
+  uint32_t* vdst = reinterpret_cast<uint32_t*>(&vt[slot][EPL * r]);
 
-  const int r = tid % LPV;  // lane index inside the vector: elements 8r .. 8r+7
-  const float cnorm = (D == 128) ? __uint_as_float(0x3DB504F3u) : 0.0625f;  // RN32(1/sqrt(D))
-  const int nvec = 2 * nnew;
-  for (int base = 0; base < nvec; base += VPP) {
-    const int vi = base + tid / LPV;
-    if (vi >= nvec) continue;  // uniform over the LPV lanes of one vector
-    const int tensor = vi / nnew;
-    const int slot = s_lo + vi % nnew;
+  if (active) {
     const int pos = tile_base + slot;
-    const int t_in = pos - p.len;
-    const size_t src = ((static_cast<size_t>(b) * p.n_new + t_in) * p.hkv + h) * D + 8 * r;
-
-    float x[8];
-    load8(tensor ? p.v : p.k, src, p.in_bf16, x);
-
-    if (p.rotation == kRotSign) {
+    const size_t src = ((static_cast<size_t>(b) * p.n_new + (pos - p.len)) * p.hkv + h) * D + EPL * r;
+    float x[EPL];
+    if (p.in_bf16) {
+      const uint4* s4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(tensor ? p.v : p.k) + src);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * p.rot[8 * r + e];
+      for (int i = 0; i < EPL / 8; ++i) {
+        const uint4 w = s4[i];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[8 * i + 2 * k] = bf16_bits_to_f32(ws[k] & 0xFFFFu);
+          x[8 * i + 2 * k + 1] = bf16_bits_to_f32(ws[k] >> 16);
+        }
+      }
+    } else {
+      const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(tensor ? p.v : p.k) + src);
+#pragma unroll
+      for (int i = 0; i < EPL / 4; ++i) {
+        const float4 w = s4[i];
+        x[4 * i] = w.x; x[4 * i + 1] = w.y; x[4 * i + 2] = w.z; x[4 * i + 3] = w.w;
+      }
     }
-    // butterfly stages of stride 1, 2, 4 inside the lane
+    if (p.rotation == kRotSign) {
+      const float4* sg = reinterpret_cast<const float4*>(p.rot + EPL * r);
 #pragma unroll
-    for (int hs = 1; hs < 8; hs <<= 1) {
+      for (int i = 0; i < EPL / 4; ++i) {
+        const float4 g = sg[i];
+        x[4 * i] *= g.x; x[4 * i + 1] *= g.y; x[4 * i + 2] *= g.z; x[4 * i + 3] *= g.w;
+      }
+    }
+    // butterfly stages of stride 1 .. EPL/2 inside the lane
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+    for (int hs = 1; hs < EPL; hs <<= 1) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
         if (!(e & hs)) {
           const float a = x[e], c = x[e + hs];
           x[e] = a + c;
@@ -84,124 +137,214 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         }
       }
     }
-    // stages of stride 8, 16, ... across lanes (partner lane r ^ bit)
+    // strides EPL and 2 EPL: partner lane r ^ 1, then r ^ 2.  Each stage is one
+    // fma(sg, partner, own) = RN(own +- partner): the lower lane gets a + b, the upper
+    // one b - a = -(a - b).  After both stages lanes 1 and 2 hold their values negated
+    // (RN is odd, so the magnitudes are exactly the specified ones); sigma undoes it.
+    {
+      const float sg1 = (r & 1) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int bit = 1; bit < LPV; bit <<= 1) {
-      const bool upper = (r & bit) != 0;
+      for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg1, dpp<kXor1>(x[e]), x[e]);
+      const float sg2 = (r & 2) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float o = shfl_xor(x[e], bit);
-        x[e] = upper ? (o - x[e]) : (x[e] + o);
-      }
+      for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg2, dpp<kXor2>(x[e]), x[e]);
     }
+    const float cnorm = (D == 128) ? __uint_as_float(0x3DB504F3u) : 0.0625f;  // RN32(1/sqrt(D))
+    const float sc = ((r ^ (r >> 1)) & 1) ? -cnorm : cnorm;   // sigma * c
+    // Symmetric codes with the sign-flip rotation use the unnormalised values: the
+    // block maximum of |RN(x c)| is RN(max|x| c) (rounding is monotone), and the
+    // code quotient folds c in.  Otherwise y = RN(x c) is formed here.
+    const bool normalized = ASYM || p.rotation == kRotSo4;
+    if (normalized) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * cnorm;
-
+      for (int e = 0; e < EPL; ++e) x[e] = x[e] * sc;
+    }
     if (p.rotation == kRotSo4) {
       // y_row = ((R_row0 x0 + R_row1 x1) + R_row2 x2) + R_row3 x3 per 4-block
 #pragma unroll
-      for (int qd = 0; qd < 2; ++qd) {
-        const float* R = p.rot + 16 * (2 * r + qd);
-        const float x0 = x[4 * qd], x1 = x[4 * qd + 1], x2 = x[4 * qd + 2], x3 = x[4 * qd + 3];
+      for (int q4 = 0; q4 < EPL / 4; ++q4) {
+        const float4* R = reinterpret_cast<const float4*>(p.rot + 16 * (EPL / 4 * r + q4));
+        const float x0 = x[4 * q4], x1 = x[4 * q4 + 1], x2 = x[4 * q4 + 2], x3 = x[4 * q4 + 3];
 #pragma unroll
         for (int row = 0; row < 4; ++row) {
-          float acc = R[4 * row] * x0;
-          acc = acc + R[4 * row + 1] * x1;
-          acc = acc + R[4 * row + 2] * x2;
-          acc = acc + R[4 * row + 3] * x3;
-          x[4 * qd + row] = acc;
+          const float4 rr = R[row];
+          float acc = rr.x * x0;
+          acc = acc + rr.y * x1;
+          acc = acc + rr.z * x2;
+          acc = acc + rr.w * x3;
+          x[4 * q4 + row] = acc;
         }
       }
     }
+    const float xs = normalized ? 1.0f : sc;    // y = RN(x xs) for every element
 
-    // block statistics over the m/8 lanes of a block
-    const int lpb = p.block / 8;
-    uint32_t u[8];
+    // ---- block statistics, scales and metadata
     const size_t row = unit * p.tcap + pos;
     void* meta = tensor ? p.v_meta : p.k_meta;
-    const int blk = (8 * r) / p.block;
-    const bool meta_lane = ((8 * r) % p.block) == 0;
-    if (p.quant == kQuantSym) {
-      float amax = 0.0f;
+    const bool meta_lane = (r % LPB) == 0;
+    float sblk[BPL], rsblk[BPL], zblk[BPL], mblk[BPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-      for (int bit = 1; bit < lpb; bit <<= 1) amax = fmaxf(amax, shfl_xor(amax, bit));
-      const float s32 = (amax + p.eps) / 3.0f;
-      float s;
-      if (p.scale_dtype == kScaleF16) {
-        const _Float16 s16 = static_cast<_Float16>(s32);
-        s = static_cast<float>(s16);
-        if (meta_lane) reinterpret_cast<_Float16*>(meta)[row * nblk + blk] = s16;
+    for (int bb = 0; bb < BPL; ++bb) {
+      const int blk = (EPL * r) / BLOCK + bb;
+      if constexpr (!ASYM) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < BE; ++e) amax = fmaxf(amax, fabsf(x[bb * BE + e]));
+        if constexpr (LPB >= 2) amax = fmaxf(amax, dpp<kXor1>(amax));
+        if constexpr (LPB >= 4) amax = fmaxf(amax, dpp<kXor2>(amax));
+        if (!normalized) amax = amax * cnorm;
+        const float s32 = (amax + p.eps) / 3.0f;
+        float s;
+        if (p.scale_dtype == kScaleF16) {
+          const _Float16 s16 = static_cast<_Float16>(s32);
+          s = static_cast<float>(s16);
+          if (meta_lane) reinterpret_cast<_Float16*>(meta)[row * NBLK + blk] = s16;
+        } else {
+          s = s32;
+          if (meta_lane) reinterpret_cast<float*>(meta)[row * NBLK + blk] = s32;
+        }
+        sblk[bb] = s;
+        zblk[bb] = 0.0f;
       } else {
-        s = s32;
-        if (meta_lane) reinterpret_cast<float*>(meta)[row * nblk + blk] = s32;
+        float mn = x[bb * BE], mx = x[bb * BE];
+#pragma unroll
+        for (int e = 1; e < BE; ++e) {
+          mn = fminf(mn, x[bb * BE + e]);
+          mx = fmaxf(mx, x[bb * BE + e]);
+        }
+        if constexpr (LPB >= 2) {
+          mn = fminf(mn, dpp<kXor1>(mn));
+          mx = fmaxf(mx, dpp<kXor1>(mx));
+        }
+        if constexpr (LPB >= 4) {
+          mn = fminf(mn, dpp<kXor2>(mn));
+          mx = fmaxf(mx, dpp<kXor2>(mx));
+        }
+        const float s32 = (mx - mn) / 7.0f;
+        const uint32_t sb = e4m3_encode(s32), zb = e4m3_encode(mn);
+        if (meta_lane) reinterpret_cast<uint16_t*>(meta)[row * NBLK + blk] = static_cast<uint16_t>(sb | (zb << 8));
+        sblk[bb] = e4m3_decode(sb);
+        zblk[bb] = e4m3_decode(zb);
       }
-      const float rs = __builtin_amdgcn_rcpf(s);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = static_cast<uint32_t>(rne_code(x[e], s, rs, -3, 3) + 4);
-    } else {
-      float mn = x[0], mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) { mn = fminf(mn, x[e]); mx = fmaxf(mx, x[e]); }
-      for (int bit = 1; bit < lpb; bit <<= 1) {
-        mn = fminf(mn, shfl_xor(mn, bit));
-        mx = fmaxf(mx, shfl_xor(mx, bit));
-      }
-      const float s32 = (mx - mn) / 7.0f;
-      const uint32_t sb = e4m3_encode(s32), zb = e4m3_encode(mn);
-      const float s = e4m3_decode(sb), z = e4m3_decode(zb);
-      if (meta_lane) reinterpret_cast<uint16_t*>(meta)[row * nblk + blk] = static_cast<uint16_t>(sb | (zb << 8));
-      const float rs = __builtin_amdgcn_rcpf(s);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = static_cast<uint32_t>(rne_code(x[e] - z, s, rs, 0, 7));
+      rsblk[bb] = __builtin_amdgcn_rcpf(sblk[bb]);
+      mblk[bb] = xs * rsblk[bb];      // quotient multiplier: y / s ~ x mblk
     }
 
-    if (tensor == 0) {
-      // key row: lane gi (0..3) of a 32-code group holds codes 8gi .. 8gi+7
-      const int gi = r & 3;
-      uint32_t w = 0, l0 = 0, l1 = 0, l2 = 0;
+    // ---- codes u (0..7) as integer-valued floats, written over x.  Fast rounding:
+    // rint of the approximate quotient (within ~2e-6 of the exact one, |q| <= 8).
+    // If any value of the wave lies within kNear of a rounding boundary, the wave
+    // takes the exact rounding of the exact quotient instead.
+    constexpr bool KEEP = EPL <= 32;            // keep the rounded quotients in registers
+    float kq[KEEP ? EPL : 1];
+    auto quotient = [&](int e) {
+      const int bb = e / BE;
+      if constexpr (!ASYM) return __builtin_fmaf(x[e], mblk[bb], 4.0f);   // 4 + y / s
+      else return (x[e] - zblk[bb]) * rsblk[bb];                          // RN32(y - z) / s
+    };
+    float dist = 0.0f;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        w |= (u[bb] | (u[4 + bb] << 3)) << (8 * bb);
-        l0 |= (u[bb] & 3u) << (8 * bb + 6);
-        l1 |= (u[4 + bb] & 3u) << (8 * bb + 6);
-        l2 |= ((u[bb] >> 2) << (8 * bb + 6)) | ((u[4 + bb] >> 2) << (8 * bb + 7));
-      }
-      // codes 24..31 (lane gi == 3) fill bits 6-7 of every byte of the group
-      const int src_lane = lane | 3;
-      const uint32_t f0 = __shfl(l0, src_lane, 64);
-      const uint32_t f1 = __shfl(l1, src_lane, 64);
-      const uint32_t f2 = __shfl(l2, src_lane, 64);
-      if (gi < 3) {
-        const uint32_t word = w | (gi == 0 ? f0 : (gi == 1 ? f1 : f2));
-        uint8_t* dst = p.k_codes + row * (3 * D / 8) + 12 * (r >> 2) + 4 * gi;
-        *reinterpret_cast<uint32_t*>(dst) = word;
+    for (int e = 0; e < EPL; ++e) {
+      const float t = quotient(e);
+      const float k = __builtin_rintf(t);
+      if constexpr (KEEP) kq[e] = k;
+      dist = fmaxf(dist, fabsf(t - k));
+    }
+    if (__any(dist > kNear)) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int bb = e / BE;
+        const float y = x[e] * xs;
+        x[e] = ASYM ? static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, 7))
+                    : static_cast<float>(rne_code(y, sblk[bb], rsblk[bb], -3, 3) + 4);
       }
     } else {
-      uint2 packed;
-      packed.x = u[0] | (u[1] << 8) | (u[2] << 16) | (u[3] << 24);
-      packed.y = u[4] | (u[5] << 8) | (u[6] << 16) | (u[7] << 24);
-      *reinterpret_cast<uint2*>(&vt[slot][8 * r]) = packed;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float k;
+        if constexpr (KEEP) k = kq[e];
+        else k = __builtin_rintf(quotient(e));
+        x[e] = ASYM ? __builtin_amdgcn_fmed3f(k, 0.0f, 7.0f) : __builtin_amdgcn_fmed3f(k, 1.0f, 7.0f);
+      }
+#pragma unroll
+      for (int bb = 0; bb < BPL; ++bb) {
+        if (!(sblk[bb] > 0.0f)) {
+#pragma unroll
+          for (int e = 0; e < BE; ++e) x[bb * BE + e] = ASYM ? 0.0f : 4.0f;   // zero scale: code 0
+        }
+      }
     }
+    const float* u = x;
+
+    // ---- pack
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      uint32_t d[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) d[k] = bytes_of(&u[32 * g + 4 * k]);
+      if (tensor == 0) {
+        uint32_t w0, w1, w2;
+        pack_g32(d, w0, w1, w2);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + row * (3 * D / 8) + 12 * (GPL * r + g));
+        dst[0] = w0;
+        dst[1] = w1;
+        dst[2] = w2;
+      } else {
+        reinterpret_cast<uint4*>(vdst)[2 * g] = make_uint4(d[0], d[1], d[2], d[3]);
+        reinterpret_cast<uint4*>(vdst)[2 * g + 1] = make_uint4(d[4], d[5], d[6], d[7]);
+      }
+    }
+  } else if (tensor == 1) {
+    // value slot without a new token: code 0
+#pragma unroll
+    for (int i = 0; i < EPL / 16; ++i) reinterpret_cast<uint4*>(vdst)[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
 
-  // value tile: dim j is one group over the tile's 32 tokens; thread idx writes word
-  // k = idx % 3 of dim j = idx / 3 (contiguous 4-byte stores)
-  for (int idx = tid; idx < 3 * D; idx += 256) {
-    const int j = idx / 3;
-    const int k = idx - 3 * j;
-    uint32_t w = 0;
+  // ---- value tile: dim j is one group over the tile's 32 tokens
+  uint8_t* vtile = p.v_codes + (unit * p.ntile_cap + tile) * static_cast<size_t>(D) * 12;
+  for (int j = tid; j < D; j += 256) {
+    uint32_t d[8];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      w |= (static_cast<uint32_t>(vt[8 * k + bb][j]) | (static_cast<uint32_t>(vt[8 * k + 4 + bb][j]) << 3))
-           << (8 * bb);
-      const uint32_t a = vt[24 + bb][j], c = vt[28 + bb][j];
-      if (k == 0) w |= (a & 3u) << (8 * bb + 6);
-      else if (k == 1) w |= (c & 3u) << (8 * bb + 6);
-      else w |= ((a >> 2) << (8 * bb + 6)) | ((c >> 2) << (8 * bb + 7));
+    for (int k = 0; k < 8; ++k) {
+      d[k] = static_cast<uint32_t>(vt[4 * k][j]) | (static_cast<uint32_t>(vt[4 * k + 1][j]) << 8) |
+             (static_cast<uint32_t>(vt[4 * k + 2][j]) << 16) | (static_cast<uint32_t>(vt[4 * k + 3][j]) << 24);
     }
-    reinterpret_cast<uint32_t*>(vtile)[idx] = w;
+    uint32_t w0, w1, w2;
+    pack_g32(d, w0, w1, w2);
+    uint32_t* g = reinterpret_cast<uint32_t*>(vtile + 12 * j);
+    if (s_lo > 0) {
+      // keep the codes of the tile's earlier tokens
+      uint32_t m0, m1, m2;
+      keep_mask(s_lo, m0, m1, m2);
+      w0 |= g[0] & m0;
+      w1 |= g[1] & m1;
+      w2 |= g[2] & m2;
+    }
+    g[0] = w0;
+    g[1] = w1;
+    g[2] = w2;
+  }
+}
+
+template <int D, int BLOCK>
+void launch_q(const WriteParams& p, dim3 grid, hipStream_t s) {
+  if (p.quant == kQuantAsym) hipLaunchKernelGGL((write_kernel<D, BLOCK, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((write_kernel<D, BLOCK, false>), grid, dim3(256), 0, s, p);
+}
+
+template <int D>
+bool launch_d(const WriteParams& p, dim3 grid, hipStream_t s) {
+  switch (p.block) {
+    case 32: launch_q<D, 32>(p, grid, s); return true;
+    case 64: launch_q<D, 64>(p, grid, s); return true;
+    case 128: launch_q<D, 128>(p, grid, s); return true;
+    case 256:
+      if constexpr (D >= 256) {
+        launch_q<D, 256>(p, grid, s);
+        return true;
+      }
+      return false;
+    default: return false;
   }
 }
 
@@ -209,9 +352,10 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
 
 hipError_t launch_write(const WriteParams& p, int ntiles, int batch, int d, hipStream_t s) {
   const dim3 grid(ntiles, p.hkv, batch);
-  if (d == 128) hipLaunchKernelGGL(write_kernel<128>, grid, dim3(256), 0, s, p);
-  else if (d == 256) hipLaunchKernelGGL(write_kernel<256>, grid, dim3(256), 0, s, p);
-  else return hipErrorInvalidValue;
+  bool ok = false;
+  if (d == 128) ok = launch_d<128>(p, grid, s);
+  else if (d == 256) ok = launch_d<256>(p, grid, s);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
