@@ -39,6 +39,31 @@ def write_bytes_per_position(wl):
     return wl.batch * wl.hkv * 2 * (wl.d * in_b + wl.row_bytes())
 
 
+# source files of each decode kernel (the recorded HBM counters hold for these bytes)
+KERNEL_SOURCES = {
+    "per_head": ["okv_decode.hip", "okv_decode_common.hpp", "okv_device.hpp"],
+    "grouped": ["okv_decode_mfma.hip", "okv_decode_common.hpp", "okv_device.hpp"],
+}
+
+
+def recorded_traffic(wl, kernel):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3 counter
+    record (profiles/traffic_<workload>.txt: FETCH_SIZE and WRITE_SIZE scaled by a
+    calibration copy), or None when there is none or the kernel source has changed
+    since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = json.loads(open(path).read())
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "decode_attention_okv_amd", "csrc", f), "rb").read())
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return int(rec["read_bytes"]) + int(rec["write_bytes"])
+
+
 def cpu_baseline(wl, target_s=12.0):
     """Time the CPU oracle's decode on (sequence, KV head) units of the workload at
     its full context length (same distributions; values drawn on the host)."""
@@ -151,6 +176,7 @@ def main():
         cache.decode_attn(qs[i], out)
     torch.cuda.synchronize()
     splits = cache.splits()
+    kernel = cache.decode_kernel()
     ts, te = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ts.record()
     for i in range(W, steps):
@@ -200,13 +226,14 @@ def main():
         "write_tokens_per_s": round(write_tok_s, 1),
         "write_prefill_ms": round(prefill_ms, 3),
         "write_prefill_GBs": round(write_bytes_per_position(wl) * T0 / (prefill_ms * 1e-3) / 1e9, 2),
+        "decode_kernel": kernel,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(wl, kernel),
         },
     }
     if not args.no_cpu_baseline:
