@@ -41,7 +41,7 @@ def write_bytes_per_position(wl):
 
 # source files of each decode kernel (the recorded HBM counters hold for these bytes)
 KERNEL_SOURCES = {
-    "per_head": ["okv_decode.hip", "okv_decode_common.hpp", "okv_device.hpp"],
+    "per_head": ["okv_decode_head.hip", "okv_decode_common.hpp", "okv_device.hpp"],
     "grouped": ["okv_decode_mfma.hip", "okv_decode_common.hpp", "okv_device.hpp"],
 }
 

@@ -30,9 +30,10 @@ COMMON = [
 SOURCES = [
     # (source, extra flags)
     ("okv_write.hip", ["-ffp-contract=off"]),   # bit-exact float32 write path
-    ("okv_decode.hip", []),
-    # MFMA results in VGPRs: the kernel reads every accumulator with VALU right away
+    # MFMA results in VGPRs: the kernels read every accumulator with VALU right away
+    ("okv_decode_head.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("okv_decode_mfma.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("okv_reduce.hip", []),
     ("okv_host.cpp", ["-x", "hip"]),
 ]
 
@@ -68,7 +69,7 @@ def dump_isa(out_dir: str) -> None:
     """Write the gfx950 assembly of the kernels (for reading only)."""
     os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
-    for src, extra in SOURCES[:3]:
+    for src, extra in SOURCES[:4]:
         out = os.path.join(out_dir, os.path.splitext(src)[0] + ".s")
         subprocess.run([cc, *COMMON, *extra, "--cuda-device-only", "-S",
                         os.path.join(CSRC, src), "-o", out], check=True)

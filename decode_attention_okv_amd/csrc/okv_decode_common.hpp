@@ -1,5 +1,5 @@
-// Helpers shared by the decode kernels (included by okv_decode.hip and
-// okv_decode_mfma.hip only).
+// Helpers shared by the decode and reduce kernels (included by okv_decode_head.hip,
+// okv_decode_mfma.hip and okv_reduce.hip).
 #pragma once
 
 #include "okv_device.hpp"
@@ -40,8 +40,32 @@ __device__ __forceinline__ float swz_xor4(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
 }
 
+__device__ __forceinline__ float dpp_ror4(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float dpp_ror8(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+}
+
+// Maximum / sum over the 16 lanes of each row (all lanes active): quad xor 1 and 2,
+// then rotations by 4 and 8 inside the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_xor1(v));
+  v = fmaxf(v, dpp_xor2(v));
+  v = fmaxf(v, dpp_ror4(v));
+  return fmaxf(v, dpp_ror8(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_xor1(v);
+  v += dpp_xor2(v);
+  v += dpp_ror4(v);
+  return v + dpp_ror8(v);
+}
+__device__ __forceinline__ int row16_sum(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  v += __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true);
+  return v + __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
 }
 __device__ __forceinline__ float swz_xor16(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
@@ -80,6 +104,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
 }
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i mfma64(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// a * 2^sa + b * 2^sb + c in wrapping int32 arithmetic (the true value fits).  The
+// empty asm keeps the two shift-adds apart, so each maps to one v_lshl_add_u32
+// instead of two shifts and an add3.
+template <int SA, int SB>
+__device__ __forceinline__ int combine3(int a, int b, int c) {
+  uint32_t t = (static_cast<uint32_t>(b) << SB) + static_cast<uint32_t>(c);
+  asm("" : "+v"(t));
+  return static_cast<int>((static_cast<uint32_t>(a) << SA) + t);
+}
+
+// 16-byte slot of chunk c (16 tokens) in a 64-byte LDS row r: rotating the chunk
+// order by bits 2-3 of the row spreads 16 consecutive rows over all 64 banks.
+__device__ __forceinline__ int slot16(int c, int r) { return (c ^ (r >> 2)) & 3; }
 
 template <int FMT>
 __device__ __forceinline__ uint32_t buf_meta(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

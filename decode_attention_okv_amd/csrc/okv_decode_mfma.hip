@@ -33,28 +33,12 @@ namespace {
 
 using namespace dec;
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 constexpr int kStep = 64;                 // tokens per wave step (two value tiles)
 constexpr int kW7 = (1 << 21) - 1;        // P.V weights: 21-bit integers per step and row
 
 __device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
 __device__ __forceinline__ int xor16i(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
 __device__ __forceinline__ int xor32i(int v) { return __shfl_xor(v, 32, 64); }
-
-__device__ __forceinline__ v4i mfma64(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-// a * 2^sa + b * 2^sb + c in wrapping int32 arithmetic (the true value fits).  The
-// empty asm keeps the two shift-adds apart, so each maps to one v_lshl_add_u32
-// instead of two shifts and an add3.
-template <int SA, int SB>
-__device__ __forceinline__ int combine3(int a, int b, int c) {
-  uint32_t t = (static_cast<uint32_t>(b) << SB) + static_cast<uint32_t>(c);
-  asm("" : "+v"(t));
-  return static_cast<int>((static_cast<uint32_t>(a) << SA) + t);
-}
 
 // Balanced base-256 digits: q = 65536 hi + 256 mi + lo, each in [-128, 127].
 __device__ __forceinline__ void digits_q(int q, int& hi, int& mi, int& lo) {
@@ -68,10 +52,6 @@ __device__ __forceinline__ void digits_q(int q, int& hi, int& mi, int& lo) {
 __device__ __forceinline__ uint32_t bytes4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
   return (x3 << 24) | (x2 << 16) | (x1 << 8) | x0;   // v_lshl_or_b32 chain
 }
-
-// 16-byte slot of chunk c (16 tokens) in a 64-byte LDS row r: rotating the chunk
-// order by bits 2-3 of the row spreads 16 consecutive rows over all 64 banks.
-__device__ __forceinline__ int slot16(int c, int r) { return (c ^ (r >> 2)) & 3; }
 
 template <int MDW>
 __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
@@ -283,8 +263,6 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 
   const int T = p.T;
   const int ntiles = (T + kTile - 1) / kTile;
-  const int t_begin = split * p.tiles_per_split;   // even: splits hold whole steps
-  const int t_end = min(t_begin + p.tiles_per_split, ntiles);
   // buffer resources of this (sequence, KV head); offsets carry the step base in the
   // vector offset, so rows past T (and tiles past the last) read as zero
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_codes + unit * p.tcap * ROWB, static_cast<uint32_t>(T) * ROWB);
@@ -552,11 +530,13 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
     }
   };
 
-  // (past the split's end the prefetch reloads the wave's last step, from L2)
-  const int s_begin = t_begin / 2;
-  const int s_end = (t_end + 1) / 2;
+  // Steps are interleaved over the workgroups of a (sequence, KV head): wave w of
+  // split s takes steps 4 s + w, then every 4 nsplit-th, so the running workgroups
+  // sweep the cache together.  (After its last step the prefetch reloads it, from L2.)
+  const int s_end = (ntiles + 1) / 2;
+  const int sstr = 4 * p.nsplit;
   Raw r;
-  int st = s_begin + wave;
+  int st = split * 4 + wave;
   if (st < s_end) {
     load_m(r, st);
 #pragma unroll
@@ -564,7 +544,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 #pragma unroll
     for (int hf = 0; hf < 4; ++hf) load_k(r, st, hf);
   }
-  for (; st < s_end; st += 4) compute_step(r, st, min(st + 4, s_end - 1));
+  for (; st < s_end; st += sstr) compute_step(r, st, st + sstr < s_end ? st + sstr : st);
 
   // ---- combine the four waves; partials per query head
   l_run += swz_xor16(l_run);
@@ -650,7 +630,7 @@ bool grouped_decode_supported(int d, int block, int group) {
 hipError_t launch_decode_grouped(const DecodeParams& p, int batch, int d, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1) {
   if (p.nsplit < 1 || p.nsplit > kMaxSplitsDev) return hipErrorInvalidValue;
-  if (p.hkv < 1 || p.hq % p.hkv != 0 || p.tiles_per_split % 2 != 0) return hipErrorInvalidValue;
+  if (p.hkv < 1 || p.hq % p.hkv != 0) return hipErrorInvalidValue;
   const int group = p.hq / p.hkv;
   if (!grouped_decode_supported(d, p.block, group)) return hipErrorInvalidValue;
   const dim3 grid(p.nsplit, p.hkv, batch);

@@ -17,7 +17,7 @@ namespace {
 
 constexpr int kMaxSplits = 256;      // split-K workspace capacity per (sequence, query head)
 constexpr int kTargetGroups = 2048;  // workgroups the automatic split count aims for
-constexpr int kMinSplitTiles = 32;   // automatic splits keep >= 4 two-tile steps per wave
+constexpr int kMinSplitSteps = 16;   // automatic splits keep >= 4 64-token steps per wave
 constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -112,26 +112,23 @@ int decode_kernel_of(const okv_handle* h) {
   return grouped_built(h->cfg) ? OKV_DECODE_GROUPED : OKV_DECODE_PER_HEAD;
 }
 
-// Split count and tiles per split for a cache of T tokens: every split holds a
-// whole number of decode steps (kStepTiles tiles) and none is empty.
-int choose_splits(const okv_handle* h, int32_t T, int* tiles_per_split) {
-  const int ntiles = (T + okv::kTile - 1) / okv::kTile;
+// Split count for a cache of T tokens.  The decode kernels interleave their
+// 64-token steps over the splits of a (sequence, head); none is empty.
+int choose_splits(const okv_handle* h, int32_t T) {
+  const int nsteps = (T + 63) / 64;
   int s = h->splits;
   if (s <= 0) {
     // workgroups per split: one per query head, or one per KV head when grouped
     const int heads = decode_kernel_of(h) == OKV_DECODE_GROUPED ? h->cfg.num_kv_heads : h->cfg.num_q_heads;
     const int units = h->cfg.batch * heads;
     s = (kTargetGroups + units - 1) / units;
-    const int cap = ntiles / kMinSplitTiles;   // short caches: fewer, longer splits
+    const int cap = nsteps / kMinSplitSteps;   // short caches: fewer, longer splits
     if (s > cap) s = cap;
   }
   if (s > kMaxSplits) s = kMaxSplits;
-  if (s > ntiles) s = ntiles;
+  if (s > nsteps) s = nsteps;
   if (s < 1) s = 1;
-  int tps = (ntiles + s - 1) / s;
-  tps = (tps + okv::kStepTiles - 1) / okv::kStepTiles * okv::kStepTiles;
-  if (tiles_per_split) *tiles_per_split = tps;
-  return (ntiles + tps - 1) / tps;
+  return s;
 }
 
 void free_timing(okv_handle* h) {
@@ -277,8 +274,7 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   if (h->len < 1) return OKV_E_INVALID;
   const okv_config& c = h->cfg;
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  int tps = 0;
-  const int nsplit = choose_splits(h, h->len, &tps);
+  const int nsplit = choose_splits(h, h->len);
   okv::DecodeParams p{};
   p.k_codes = static_cast<const uint8_t*>(c.k_codes);
   p.v_codes = static_cast<const uint8_t*>(c.v_codes);
@@ -292,7 +288,6 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   p.tcap = c.max_tokens;
   p.ntile_cap = c.max_tokens / okv::kTile;
   p.T = h->len;
-  p.tiles_per_split = tps;
   p.nsplit = nsplit;
   p.block = c.block;
   p.quant = c.quant;
@@ -312,8 +307,8 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   const hipError_t le = decode_kernel_of(h) == OKV_DECODE_GROUPED
                            ? okv::launch_decode_grouped(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
                                                         ts ? ts->e1 : nullptr)
-                           : okv::launch_decode(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
-                                                ts ? ts->e1 : nullptr);
+                       : okv::launch_decode_head(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
+                                                 ts ? ts->e1 : nullptr);
   if (!hip_ok(le)) return OKV_E_HIP;
   if (!hip_ok(okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr))) {
     return OKV_E_HIP;
@@ -347,7 +342,7 @@ int okv_max_splits(const okv_handle* h, int32_t* n) {
 
 int okv_get_splits(const okv_handle* h, int32_t* n) {
   if (h == nullptr || n == nullptr) return OKV_E_INVALID;
-  *n = h->len > 0 ? choose_splits(h, h->len, nullptr) : 0;
+  *n = h->len > 0 ? choose_splits(h, h->len) : 0;
   return OKV_OK;
 }
 

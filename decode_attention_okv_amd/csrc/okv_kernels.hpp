@@ -9,7 +9,6 @@ namespace okv {
 
 constexpr int kTile = 32;   // tokens per value tile
 constexpr int kGroup = 32;  // codes per 12-byte packed group
-constexpr int kStepTiles = 2;  // tiles per decode compute step: splits hold whole steps
 
 enum : int { kQuantSym = 0, kQuantAsym = 1 };
 enum : int { kScaleF32 = 0, kScaleF16 = 1, kScaleE4M3 = 3 };
@@ -36,7 +35,7 @@ struct DecodeParams {
   const void* q;         // [B][Hq][D] input type
   const float* rot;
   float* ws;             // [B][Hq][nsplit][D + 2]: acc[D], m (log2 units), l
-  int hq, hkv, tcap, ntile_cap, T, tiles_per_split, nsplit;
+  int hq, hkv, tcap, ntile_cap, T, nsplit;   // steps interleave over the nsplit splits
   int block, quant, scale_dtype, rotation, in_bf16;
 };
 
@@ -50,14 +49,18 @@ struct ReduceParams {
 hipError_t launch_write(const WriteParams& p, int ntiles, int batch, int d, hipStream_t s);
 // ev0/ev1 (may be null): events recorded at the start and the end of the kernel's
 // own dispatch (hipExtLaunchKernelGGL), so their elapsed time is the kernel time.
-hipError_t launch_decode(const DecodeParams& p, int batch, int d, hipStream_t s,
-                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s,
                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
+// Per-head decode on MFMA (one workgroup per query head): head_dim 128/256, blocks
+// of 32 .. head_dim.  Grid (nsplit, hq, batch); writes the split-K workspace.
+bool head_decode_supported(int d, int block);
+hipError_t launch_decode_head(const DecodeParams& p, int batch, int d, hipStream_t s,
+                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
 // Grouped decode (one workgroup per KV head serves its whole query group on MFMA):
 // built for head_dim 128/256 with (group 4, block 32) or (group 8, block 64).  Grid
-// (nsplit, hkv, batch); writes the same workspace as launch_decode.
+// (nsplit, hkv, batch); writes the same workspace as launch_decode_head.
 bool grouped_decode_supported(int d, int block, int group);
 hipError_t launch_decode_grouped(const DecodeParams& p, int batch, int d, hipStream_t s,
                                  hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);

@@ -114,6 +114,21 @@ def test_split_count_invariance(splits):
     run_case(wl, 1111, [1111], splits=splits, kernel="grouped")
 
 
+@pytest.mark.parametrize("d,block,quant", [
+    (128, 64, "sym"), (128, 128, "sym"), (128, 32, "asym"), (128, 128, "asym"),
+    (256, 64, "sym"), (256, 128, "asym"), (256, 256, "sym"), (256, 256, "asym"),
+])
+def test_block_sizes(d, block, quant):
+    # every quantisation block the library builds, per-head kernel (G = 1) and
+    # query groups of 2 (per-head kernel, each KV head read twice)
+    meta = "e4m3" if quant == "asym" else "f16"
+    rot = "so4" if d == 256 else "sign"
+    for hq in (2, 4):
+        wl = okv_synth.workload("so4_d256_b32_t8k").with_(
+            batch=1, hq=hq, hkv=2, d=d, block=block, quant=quant, scale_dtype=meta, rotation=rot)
+        run_case(wl, 300, [200, 100], kernel="per_head")
+
+
 @pytest.mark.parametrize("t,chunks", [(1, [1]), (32, [32]), (33, [1, 31, 1]), (64, [20, 20, 24]),
                                       (97, [97])])
 def test_small_lengths(t, chunks):
