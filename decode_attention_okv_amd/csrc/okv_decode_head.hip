@@ -398,7 +398,8 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
 
   // Steps are interleaved over the workgroups of a (sequence, head): wave w of split s
   // takes steps 4 s + w, then every 4 nsplit-th, so the running workgroups sweep the
-  // cache together.  (After its last step the prefetch reloads it, from L2.)
+  // cache together.  After a wave's last step its prefetch names step s_end, wholly
+  // past the buffer ranges: those loads return zeros without touching memory.
   const int s_end = (ntiles + 1) / 2;
   const int sstr = 4 * p.nsplit;
   Raw r;
@@ -412,10 +413,10 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
     for (int hf = 0; hf < 4; ++hf) load_k(r, st, hf);
   }
   while (st < s_end) {
-    compute_step(r, ma, mb, st, st + sstr < s_end ? st + sstr : st);
+    compute_step(r, ma, mb, st, st + sstr < s_end ? st + sstr : s_end);
     st += sstr;
     if (st >= s_end) break;
-    compute_step(r, mb, ma, st, st + sstr < s_end ? st + sstr : st);
+    compute_step(r, mb, ma, st, st + sstr < s_end ? st + sstr : s_end);
     st += sstr;
   }
 

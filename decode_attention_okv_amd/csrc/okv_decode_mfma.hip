@@ -532,7 +532,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 
   // Steps are interleaved over the workgroups of a (sequence, KV head): wave w of
   // split s takes steps 4 s + w, then every 4 nsplit-th, so the running workgroups
-  // sweep the cache together.  (After its last step the prefetch reloads it, from L2.)
+  // sweep the cache together.  After a wave's last step its prefetch names step
+  // s_end, wholly past the buffer ranges: those loads return zeros without touching
+  // memory.
   const int s_end = (ntiles + 1) / 2;
   const int sstr = 4 * p.nsplit;
   Raw r;
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 #pragma unroll
     for (int hf = 0; hf < 4; ++hf) load_k(r, st, hf);
   }
-  for (; st < s_end; st += sstr) compute_step(r, st, st + sstr < s_end ? st + sstr : st);
+  for (; st < s_end; st += sstr) compute_step(r, st, st + sstr < s_end ? st + sstr : s_end);
 
   // ---- combine the four waves; partials per query head
   l_run += swz_xor16(l_run);

@@ -65,8 +65,9 @@ int validate_shape(const okv_config* c) {
   if (c->head_dim != 128 && c->head_dim != 256) return OKV_E_UNSUPPORTED;
   if (c->block % 32 != 0) return OKV_E_UNSUPPORTED;
   // the kernels address one (sequence, KV head) slice of a cache buffer with 32-bit
-  // byte offsets (buffer resources): the packed codes of a slice stay below 4 GiB
-  if (static_cast<int64_t>(c->max_tokens) * (3 * c->head_dim / 8) >= (int64_t{1} << 32)) {
+  // byte offsets (buffer resources), up to 128 tokens past its end: the packed codes
+  // of a slice plus that margin stay below 4 GiB
+  if ((static_cast<int64_t>(c->max_tokens) + 128) * (3 * c->head_dim / 8) >= (int64_t{1} << 32)) {
     return OKV_E_UNSUPPORTED;
   }
   return OKV_OK;

@@ -104,7 +104,7 @@ typedef struct okv_config {
   int32_t num_kv_heads;  /* >= 1 */
   int32_t head_dim;      /* d: power of two, 4 | d; this build: 128 or 256 */
   int32_t max_tokens;    /* cache capacity per sequence, multiple of 32; this build:
-                          * max_tokens * 3 * head_dim / 8 < 2^32 */
+                          * (max_tokens + 128) * 3 * head_dim / 8 < 2^32 */
   int32_t block;         /* quantisation block m: m | d, 8 | m; this build: 32 or 64 */
   int32_t quant;         /* okv_quant */
   int32_t scale_dtype;   /* OKV_DT_F32 or OKV_DT_F16 (SYM3); OKV_DT_E4M3 (ASYM3) */

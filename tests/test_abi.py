@@ -33,8 +33,8 @@ def base(**kw):
 
 
 def test_largest_slice_is_accepted():
-    st, lay = okv.okv_layout(base(max_tokens=89478464))               # 2^32 - 1024 bytes
-    assert st == okv.OKV_OK and lay.k_codes_bytes == 2 * 2 * 89478464 * 48   # batch 2 x 2 KV heads
+    st, lay = okv.okv_layout(base(max_tokens=89478336))   # (89478336 + 128) x 48 < 2^32
+    assert st == okv.OKV_OK and lay.k_codes_bytes == 2 * 2 * 89478336 * 48   # batch 2 x 2 KV heads
 
 
 def test_layout_sizes():
@@ -68,7 +68,7 @@ def test_layout_sizes():
     (dict(head_dim=64, rot_params=[1.0] * 64), okv.OKV_E_UNSUPPORTED),
     (dict(block=16), okv.OKV_E_UNSUPPORTED),
     # one (sequence, KV head) slice of packed codes must stay below 4 GiB
-    (dict(max_tokens=89478496), okv.OKV_E_UNSUPPORTED),              # 48 B rows: 2^32 + 512
+    (dict(max_tokens=89478368), okv.OKV_E_UNSUPPORTED),   # 48 B rows: (89478368 + 128) x 48 > 2^32
     (dict(max_tokens=44739264, head_dim=256, rot_params=[1.0] * 256), okv.OKV_E_UNSUPPORTED),
 ])
 def test_rejections(kw, status):
