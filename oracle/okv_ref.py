@@ -20,7 +20,7 @@ __all__ = [
     "rne_codes", "quantize_f32", "dequantize",
     "G32_BIT_POSITIONS", "pack_g32", "unpack_g32", "pack_rows", "unpack_rows",
     "pack_vtiles", "unpack_vtiles",
-    "write_unit", "meta_values", "attend_unit", "attend_exact",
+    "write_unit", "meta_values", "attend_unit", "attend_exact", "attend_prefill_unit",
 ]
 
 F32 = np.float32
@@ -451,3 +451,27 @@ def attend_unit(q, k_codes, k_meta, v_codes, v_meta, t: int, spec, u_mat) -> np.
     q1 = np.asarray(q, dtype=np.float64) @ u_mat.T          # rows of U q
     y1 = attend_exact(q1, k_hat, v_hat)
     return y1 @ u_mat                                       # rows of U^T y1
+
+
+def attend_prefill_unit(q, positions, k_codes, k_meta, v_codes, v_meta, spec, u_mat) -> np.ndarray:
+    """Causal attention of new query rows over the packed cache of one KV head (the
+    prefill half of serving, over the same stored codes and metadata).
+
+    q: (n, G, d) query heads of n new positions; query row i sits at cache position
+    positions[i] (its own key and value are already stored) and attends to the
+    cached tokens 0 .. positions[i].  Each row is the read path of the idea card's
+    Implementation notes over that prefix: rotate q by U, softmax of the logits with
+    the decoded rotated keys, weights on the decoded rotated values, U^T back.
+    Returns (n, G, d) float64.
+    """
+    positions = [int(x) for x in positions]
+    t = max(positions) + 1
+    d = spec.d
+    k_hat = dequantize(unpack_rows(np.asarray(k_codes)[:t], d), np.asarray(k_meta)[:t], spec)
+    v_hat = dequantize(unpack_vtiles(v_codes, t), np.asarray(v_meta)[:t], spec)
+    q = np.asarray(q, dtype=np.float64)
+    out = np.empty(q.shape, dtype=np.float64)
+    for i, pos in enumerate(positions):
+        q1 = q[i] @ u_mat.T
+        out[i] = attend_exact(q1, k_hat[:pos + 1], v_hat[:pos + 1]) @ u_mat
+    return out

@@ -93,3 +93,36 @@ def test_quantised_attention_close_to_exact_and_rotation_helps():
     e_norot = np.sqrt(np.mean((y_norot - y_ref) ** 2)) / np.sqrt(np.mean(y_ref ** 2))
     assert e_rot < e_norot
     assert e_rot < 0.5
+
+
+@pytest.mark.parametrize("name,t,n", [("tiny_d128_t256", 100, 100), ("tiny_d128_t256", 100, 37),
+                                      ("so4_d256_b32_t8k", 70, 70), ("gqa_b16h64kv8_t128k_asym", 90, 21)])
+def test_attend_prefill_equals_causal_sdpa_on_unrotated_dequantised_cache(name, t, n):
+    # independent route for the prefill rows: torch's float64 scaled-dot-product
+    # attention with a causal mask (query at position p sees tokens 0..p) on the
+    # dequantised cache rotated back with U^T and the original queries
+    wl, k, v, _, p32, u = make_unit(name, t)
+    rng = np.random.default_rng(5)
+    g = wl.group
+    q = rng.standard_normal((n, g, wl.d))
+    pos = np.arange(t - n, t)
+    c = oracle.write_unit(k, v, wl, p32)
+    y = oracle.attend_prefill_unit(q, pos, c["k_codes"], c["k_meta"], c["v_codes"], c["v_meta"], wl, u)
+    k_hat = torch.from_numpy(oracle.dequantize(c["k_u"], c["k_meta"], wl) @ u)
+    v_hat = torch.from_numpy(oracle.dequantize(c["v_u"], c["v_meta"], wl) @ u)
+    mask = torch.from_numpy(np.arange(t)[None, :] <= pos[:, None])          # (n, t)
+    for h in range(g):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h])[None], k_hat[None], v_hat[None], attn_mask=mask[None])[0].numpy()
+        assert np.abs(y[:, h] - ref).max() < 1e-11 * np.abs(ref).max()
+
+
+def test_attend_prefill_first_position_is_its_own_value():
+    # closed form: the query at position 0 sees one token, so its output is that
+    # token's dequantised value rotated back (softmax of a single logit is 1)
+    wl, k, v, _, p32, u = make_unit("tiny_d128_t256", 8)
+    c = oracle.write_unit(k, v, wl, p32)
+    q = np.random.default_rng(1).standard_normal((3, 1, wl.d)) * 7.0
+    y = oracle.attend_prefill_unit(q, [0, 0, 0], c["k_codes"], c["k_meta"], c["v_codes"], c["v_meta"], wl, u)
+    v0 = oracle.dequantize(c["v_u"][:1], c["v_meta"][:1], wl)[0] @ u
+    assert np.abs(y[:, 0] - v0).max() <= 1e-13 * np.abs(v0).max()
