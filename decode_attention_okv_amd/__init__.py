@@ -21,6 +21,7 @@ __all__ = [
     "okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror", "okv_layout",
     "okv_get_len", "okv_set_len", "okv_set_splits", "okv_get_splits", "okv_max_splits",
     "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel", "okv_get_decode_kernel",
+    "okv_prefill_attn",
     "DECODE_KERNEL", "make_config", "OkvCache",
 ]
 
@@ -36,7 +37,7 @@ DECODE_KERNEL = {"auto": 0, "per_head": 1, "grouped": 2}
 EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror",
            "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
            "okv_get_splits", "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel",
-           "okv_get_decode_kernel", "okv_last_hip_error")
+           "okv_get_decode_kernel", "okv_last_hip_error", "okv_prefill_attn")
 
 
 class OkvConfig(ctypes.Structure):
@@ -85,6 +86,7 @@ def _load():
         "okv_create": (i32, [P(OkvConfig), P(vp)]),
         "okv_write": (i32, [vp, vp, vp, i32, vp]),
         "okv_decode_attn": (i32, [vp, vp, vp, vp]),
+        "okv_prefill_attn": (i32, [vp, vp, i32, vp, vp]),
         "okv_destroy": (i32, [vp]),
         "okv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "okv_last_hip_error": (ctypes.c_char_p, []),
@@ -154,6 +156,10 @@ def okv_write(h, k_ptr: int, v_ptr: int, n_new: int, stream=None) -> int:
 
 def okv_decode_attn(h, q_ptr: int, out_ptr: int, stream=None) -> int:
     return lib.okv_decode_attn(h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(out_ptr), _stream_ptr(stream))
+
+
+def okv_prefill_attn(h, q_ptr: int, n_q: int, out_ptr: int, stream=None) -> int:
+    return lib.okv_prefill_attn(h, ctypes.c_void_p(q_ptr), n_q, ctypes.c_void_p(out_ptr), _stream_ptr(stream))
 
 
 def okv_destroy(h) -> int:
@@ -291,6 +297,16 @@ class OkvCache:
         if out is None:
             out = torch.empty((self.batch, self.hq, self.d), dtype=torch.float32, device=self.device)
         _check(okv_decode_attn(self.handle, q.data_ptr(), out.data_ptr(), stream), "okv_decode_attn")
+        return out
+
+    def prefill_attn(self, q, out=None, stream=None):
+        """Causal attention of the last q.shape[1] cached positions (q: [batch, n, hq, d])."""
+        import torch
+        n = q.shape[1]
+        self._in_check(q, (self.batch, n, self.hq, self.d))
+        if out is None:
+            out = torch.empty((self.batch, n, self.hq, self.d), dtype=torch.float32, device=self.device)
+        _check(okv_prefill_attn(self.handle, q.data_ptr(), n, out.data_ptr(), stream), "okv_prefill_attn")
         return out
 
     @property

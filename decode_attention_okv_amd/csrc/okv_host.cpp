@@ -317,6 +317,38 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   return OKV_OK;
 }
 
+int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void* hip_stream) {
+  if (h == nullptr || q == nullptr || out == nullptr) return OKV_E_INVALID;
+  if (!aligned16(q) || !aligned16(out)) return OKV_E_ALIGN;
+  if (n_q < 1 || n_q > h->len) return OKV_E_INVALID;
+  const okv_config& c = h->cfg;
+  okv::PrefillParams p{};
+  p.k_codes = static_cast<const uint8_t*>(c.k_codes);
+  p.v_codes = static_cast<const uint8_t*>(c.v_codes);
+  p.k_meta = c.k_meta;
+  p.v_meta = c.v_meta;
+  p.q = q;
+  p.rot = h->d_rot;
+  p.out = out;
+  p.hq = c.num_q_heads;
+  p.hkv = c.num_kv_heads;
+  p.tcap = c.max_tokens;
+  p.ntile_cap = c.max_tokens / okv::kTile;
+  p.len = h->len;
+  p.n_q = n_q;
+  p.pos0 = h->len - n_q;
+  p.block = c.block;
+  p.quant = c.quant;
+  p.scale_dtype = c.scale_dtype;
+  p.rotation = c.rotation;
+  p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
+  if (!hip_ok(okv::launch_prefill(p, c.batch, c.head_dim, static_cast<hipStream_t>(hip_stream)))) {
+    return OKV_E_HIP;
+  }
+  return OKV_OK;
+}
+
 int okv_get_len(const okv_handle* h, int32_t* len) {
   if (h == nullptr || len == nullptr) return OKV_E_INVALID;
   *len = h->len;

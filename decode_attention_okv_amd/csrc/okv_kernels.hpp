@@ -46,7 +46,21 @@ struct ReduceParams {
   int hq, nsplit, rotation;
 };
 
+struct PrefillParams {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const void* k_meta;
+  const void* v_meta;
+  const void* q;         // [B][n_q][Hq][D] input type: the rows of positions pos0 .. len-1
+  const float* rot;
+  float* out;            // [B][n_q][Hq][D] float32
+  int hq, hkv, tcap, ntile_cap, len, n_q, pos0;
+  int block, quant, scale_dtype, rotation, in_bf16;
+};
+
 hipError_t launch_write(const WriteParams& p, int ntiles, int batch, int d, hipStream_t s);
+// Causal attention of the last n_q cached positions over the cache (prefill).
+hipError_t launch_prefill(const PrefillParams& p, int batch, int d, hipStream_t s);
 // ev0/ev1 (may be null): events recorded at the start and the end of the kernel's
 // own dispatch (hipExtLaunchKernelGGL), so their elapsed time is the kernel time.
 hipError_t launch_reduce(const ReduceParams& p, int batch, int d, hipStream_t s,

@@ -154,6 +154,18 @@ int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* 
  * cache is empty.  Asynchronous on hip_stream. */
 int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream);
 
+/* Prefill attention: the last n_q cached positions of every sequence (len - n_q ..
+ * len - 1, already appended by okv_write) attend causally over the cache: the row at
+ * position p sees tokens 0 .. p, its own included.  Each row is the read path of
+ * okv_decode_attn over that prefix (the idea card, Implementation notes: read path,
+ * and Key formulas, with a causal mask; the OIQ report, Section 2.3).  Keys and
+ * values are unpacked from the cache inside the kernel (codes as exact float16
+ * integers in LDS, block scales applied in float32; nothing dequantised is written
+ * to memory).  q: device [batch][n_q][num_q_heads][d] in the input type; out:
+ * device float32 [batch][n_q][num_q_heads][d]; both 16-byte aligned.  1 <= n_q <=
+ * len, else OKV_E_INVALID.  Asynchronous on hip_stream. */
+int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void* hip_stream);
+
 /* Free the handle's device memory (not the caller's buffers).  NULL is OK. */
 int okv_destroy(okv_handle* h);
 

@@ -41,7 +41,7 @@ __all__ = ["Workload", "WORKLOADS", "workload", "channel_model", "rotation_param
            "kv_tokens", "queries"]
 
 # stream ids of the SeedSequence
-_S_ROT, _S_KCH, _S_VCH, _S_K, _S_V, _S_Q, _S_STEP = range(7)
+_S_ROT, _S_KCH, _S_VCH, _S_K, _S_V, _S_Q, _S_STEP, _S_QROWS = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -192,6 +192,14 @@ def queries(wl: Workload, step: int = 0, device="cpu"):
     """One query token per (sequence, query head): [B][Hq][d] in the input dtype."""
     g = _gen(device, wl.wid, _S_Q, step)
     q = torch.randn((wl.batch, wl.hq, wl.d), generator=g, device=device, dtype=torch.float32)
+    return q.to(wl.torch_dtype)
+
+
+def query_rows(wl: Workload, pos0: int, n: int, device="cpu"):
+    """Query rows of the new positions [pos0, pos0 + n) of every sequence (prefill):
+    [B][n][Hq][d] in the input dtype, N(0,1)."""
+    g = _gen(device, wl.wid, _S_QROWS, pos0, n)
+    q = torch.randn((wl.batch, n, wl.hq, wl.d), generator=g, device=device, dtype=torch.float32)
     return q.to(wl.torch_dtype)
 
 

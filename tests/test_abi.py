@@ -106,4 +106,5 @@ def test_null_handle_calls():
     assert okv.okv_timing_read(null)[0] == okv.OKV_E_INVALID
     assert okv.okv_set_decode_kernel(null, 0) == okv.OKV_E_INVALID
     assert okv.okv_get_decode_kernel(null)[0] == okv.OKV_E_INVALID
+    assert okv.okv_prefill_attn(null, 16, 1, 16, 0) == okv.OKV_E_INVALID
     assert okv.okv_strerror(okv.OKV_E_CAPACITY) == "cache capacity exceeded"
