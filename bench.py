@@ -9,7 +9,9 @@ Default workload: 7B MHA shape at 128K context (batch 4, 32 heads, d 128,
 131,072 cached tokens per sequence, 8.3 % outlier channels, block 32, fp16 scales).
 Prints one JSON line.  `value` is decode-attention GB/s over the algorithmic bytes
 of the packed cache (codes + scales read, q read, output written), timed over
-whole steps.
+whole steps.  A second leg times chunked-prefill attention over the packed cache
+(okv_prefill_attn: the last 2,048 positions of a 32,768-token GQA context attend
+causally) and reports it under "prefill_attn".
 """
 from __future__ import annotations
 
@@ -23,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+F16_PEAK_TFLOPS = 2500.0   # dense f16 MFMA
 METRIC = "decode attn GB/s over packed 3-bit KV (% HBM peak); okv_write tokens/s"
 
 
@@ -62,6 +65,49 @@ def recorded_traffic(wl, kernel):
     if h.hexdigest()[:16] != rec.get("source_sha256_16"):
         return None
     return int(rec["read_bytes"]) + int(rec["write_bytes"])
+
+
+def prefill_attn_leg(name, rows, reps=5):
+    """Chunked-prefill attention over the packed cache: the last `rows` positions of a
+    full context attend causally (okv_prefill_attn).  Algorithmic work: 4 d flops per
+    (query head, causal query-key pair), QK^T and P.V; the kernel issues each product
+    twice (float16 hi + lo), which the f16 MFMA peak fraction does not count."""
+    import numpy as np
+    import torch
+
+    import decode_attention_okv_amd as okv
+    import okv_synth
+    wl = okv_synth.workload(name)
+    t = wl.tokens
+    p32 = okv_synth.rotation_params(wl, dtype=np.float32)
+    cache = okv.OkvCache(batch=wl.batch, num_q_heads=wl.hq, num_kv_heads=wl.hkv, head_dim=wl.d,
+                         max_tokens=t, block=wl.block, quant=wl.quant, scale_dtype=wl.scale_dtype,
+                         in_dtype=wl.in_dtype, rotation=wl.rotation, eps=wl.eps, rot_params=p32,
+                         device="cuda")
+    step = 4096
+    for pos in range(0, t, step):
+        k, v = okv_synth.kv_tokens(wl, pos, min(step, t - pos), device="cuda")
+        cache.write(k, v)
+    q = okv_synth.query_rows(wl, t - rows, rows, device="cuda")
+    out = torch.empty((wl.batch, rows, wl.hq, wl.d), dtype=torch.float32, device="cuda")
+    cache.prefill_attn(q, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        cache.prefill_attn(q, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = rows * (t - rows) + rows * (rows + 1) // 2
+    flops = 4.0 * wl.d * wl.hq * wl.batch * pairs
+    cache.close()
+    return {
+        "workload": wl.name, "context": t, "rows": rows, "calls": reps, "ms": round(ms, 3),
+        "tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 1),
+        "frac_f16_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS, 4),
+    }
 
 
 def cpu_baseline(wl, target_s=12.0):
@@ -110,6 +156,9 @@ def main():
     ap.add_argument("--workload", default="mha_b4h32_t128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--prefill-workload", default="gqa_h32kv8_t32k",
+                    help="workload of the chunked-prefill attention leg ('' to skip)")
+    ap.add_argument("--prefill-rows", type=int, default=2048)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -236,9 +285,13 @@ def main():
             "traffic": recorded_traffic(wl, kernel),
         },
     }
+    cache.close()
+    del cache, news, qs, out
+    torch.cuda.empty_cache()
+    if args.prefill_workload:
+        res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
-    cache.close()
     print(json.dumps(res), flush=True)
 
 
