@@ -35,7 +35,7 @@ SOURCES = [
     ("okv_decode_mfma.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("okv_reduce.hip", []),
     # products are fused only where the source writes fmaf (hi + lo splits stay exact)
-    ("okv_prefill.hip", ["-ffp-contract=off"]),
+    ("okv_prefill.hip", ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("okv_host.cpp", ["-x", "hip"]),
 ]
 

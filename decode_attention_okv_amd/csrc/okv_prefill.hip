@@ -66,8 +66,8 @@ __device__ __forceinline__ void meta_pair(uint32_t raw, float& s, float& z) {
 }
 
 // The 32 codes of a 12-byte group as exact float16 integers: u - 4 for symmetric codes,
-// u for asymmetric ones.  Half 0x6400 | u is 1024 + u, so one packed subtraction of
-// 1024 + bias gives the integer.
+// u for asymmetric ones.  Half 0x64uu is 1024 + u: one v_perm_b32 places two code bytes
+// under 0x64 bytes, then one packed subtraction of 1024 + bias gives the integers.
 template <bool ASYM>
 __device__ __forceinline__ void codes_h16(const uint32_t w0, const uint32_t w1, const uint32_t w2, h8 out[4]) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -77,8 +77,9 @@ __device__ __forceinline__ void codes_h16(const uint32_t w0, const uint32_t w1, 
   uint32_t hw[16];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const uint32_t lo = (d[k] & 0xFFu) | ((d[k] & 0xFF00u) << 8) | 0x64006400u;
-    const uint32_t hi = ((d[k] >> 16) & 0xFFu) | ((d[k] >> 8) & 0xFF0000u) | 0x64006400u;
+    // selector bytes 0..3 pick bytes of d[k], 4 picks a byte of 0x64646464
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, d[k], 0x04010400u);   // u0, u1
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, d[k], 0x04030402u);   // u2, u3
     hw[2 * k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lo) - bias);
     hw[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, hi) - bias);
   }
@@ -118,18 +119,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   constexpr int VROW = kKT + 4;            // halves per LDS value row (8 bytes of padding; rows 8-byte aligned)
   constexpr int NT = D / 16;               // 16-dim output tiles
   constexpr int KTB = kKT * KROW * 2;      // bytes of the key tile
-  constexpr int VTB = D * VROW * 2;        // bytes of the value tile
+  constexpr int VTB = D * VROW * 2;        // bytes of one value plane
   constexpr int QB = kQT * D * 4;          // bytes of the float32 query / output rows
-  constexpr int UB = (KTB + VTB > QB) ? KTB + VTB : QB;
+  constexpr int UB = (KTB + 2 * VTB > QB) ? KTB + 2 * VTB : QB;
   constexpr int NZ = ASYM ? NBLK : 1;
+  // value unpacking: wave w owns dims [w D / 4, (w + 1) D / 4) and the blocks they lie in
+  constexpr int WD = D / 4;                // dims per wave
+  constexpr int NBW = WD >= BLOCK ? WD / BLOCK : 1;   // value blocks per wave
+  constexpr int VGW = WD * 2 / 64;         // (dim, 32-token half) groups per lane
+  constexpr int NTW = NT / 4;              // output tiles per wave's dims
 
-  // u_s: float32 query rows (prologue), then the key and value code tiles, then
-  // float32 output rows (end)
+  // u_s: float32 query rows (prologue), then the key codes and the two value planes,
+  // then float32 output rows (end)
   __shared__ __align__(16) uint8_t u_s[UB];
-  __shared__ __align__(16) float kms_s[NBLK][kKT];   // key scales of the tile, [block][token]
+  __shared__ __align__(16) float kms_s[NBLK][kKT];      // key scales of the tile, [block][token]
   __shared__ __align__(16) float kmz_s[NZ][kKT];
-  __shared__ __align__(16) float vms_s[NBLK][kKT];   // value scales
-  __shared__ __align__(16) float vmz_s[NZ][kKT];
+  __shared__ __align__(16) float vmz_s[NZ][kKT];        // value zero-points (asymmetric)
+  __shared__ __align__(16) _Float16 sfh_s[NBLK][kKT];   // normalised value scales, hi part
+  __shared__ __align__(16) _Float16 sfl_s[NBLK][kKT];   // and lo part
+  __shared__ float g_s[4];                              // per wave: 1 / normaliser
 
   const int qt = blockIdx.x;
   const int hq = blockIdx.y;
@@ -238,53 +246,124 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12,
                                               static_cast<uint32_t>(ntiles) * D * 12);
-  _Float16* kt = reinterpret_cast<_Float16*>(u_s);              // [kKT][KROW] key codes
-  _Float16* vt = reinterpret_cast<_Float16*>(u_s + KTB);        // [D][VROW] value codes
+  _Float16* kt = reinterpret_cast<_Float16*>(u_s);                   // [kKT][KROW] key codes
+  _Float16* vh = reinterpret_cast<_Float16*>(u_s + KTB);             // [D][VROW] u sf_hi
+  _Float16* vl = reinterpret_cast<_Float16*>(u_s + KTB + VTB);       // [D][VROW] u sf_lo
+  const int blk0 = (wave * WD) / BLOCK;                              // first value block of the wave
 
   const int n_kt = pos_last / kKT + 1;                // key tiles any row of the group sees
+  // ---- raw tile data in registers, loaded one tile ahead: key code groups, the wave's
+  // value code groups, and the metadata of the wave's blocks (token = lane)
+  constexpr int KGT = (kKT * NG + 255) / 256;         // key groups per thread
+  uint32_t kw[KGT][3], vw[VGW][3], kmr[NBW], vmr[NBW];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < KGT; ++i) {
+      const int e = tid + 256 * i;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b96(
+          rk, static_cast<uint32_t>((t0 + e / NG) * ROWB + 12 * (e % NG)), 0, 0);
+      kw[i][0] = w[0];
+      kw[i][1] = w[1];
+      kw[i][2] = w[2];
+    }
+#pragma unroll
+    for (int i = 0; i < VGW; ++i) {
+      const int grp = lane + 64 * i, dim = wave * WD + grp % WD, half = grp / WD;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b96(
+          rv, static_cast<uint32_t>((t0 / kTile + half) * D * 12 + 12 * dim), 0, 0);
+      vw[i][0] = w[0];
+      vw[i][1] = w[1];
+      vw[i][2] = w[2];
+    }
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const uint32_t off = static_cast<uint32_t>(((t0 + lane) * NBLK + blk0 + i) * MB);
+      kmr[i] = buf_meta<FMT>(rkm, off, 0);
+      vmr[i] = buf_meta<FMT>(rvm, off, 0);
+    }
+  };
+  load_tile(0);
   for (int it = 0; it < n_kt; ++it) {
     const int t0 = it * kKT;
     __syncthreads();   // the previous tile (or the query rows) is no longer read
-    // ---- scales of the tile (zero past T); codes of the tile as float16 integers
-    for (int e = tid; e < kKT * NBLK; e += 256) {
-      const int tok = e / NBLK, blk = e % NBLK;
-      const uint32_t off = static_cast<uint32_t>(((t0 + tok) * NBLK + blk) * MB);
+    // ---- scales of the wave's blocks, token = lane.  Value scales are normalised by a
+    // power of two f (largest scale of the wave's blocks in [1/2, 1)) and split into
+    // an 8-bit hi part and a float16 lo part, so that code x hi is exact in float16.
+    float vsr[NBW];
+    float vmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const int blk = blk0 + i;
       float s, z;
-      meta_pair<FMT>(buf_meta<FMT>(rkm, off, 0), s, z);
-      kms_s[blk][tok] = s;
-      if constexpr (ASYM) kmz_s[blk][tok] = z;
-      meta_pair<FMT>(buf_meta<FMT>(rvm, off, 0), s, z);
-      vms_s[blk][tok] = s;
-      if constexpr (ASYM) vmz_s[blk][tok] = z;
+      meta_pair<FMT>(kmr[i], s, z);
+      kms_s[blk][lane] = s;
+      if constexpr (ASYM) kmz_s[blk][lane] = z;
+      meta_pair<FMT>(vmr[i], s, z);
+      vsr[i] = s;
+      vmax = fmaxf(vmax, s);
+      if constexpr (ASYM) vmz_s[blk][lane] = z;
     }
-    for (int e = tid; e < kKT * NG; e += 256) {
-      const int tok = e / NG, g = e % NG;
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, static_cast<uint32_t>((t0 + tok) * ROWB + 12 * g), 0, 0);
+    vmax = wave_max_fast(vmax);
+    const int ex = vmax > 0.0f ? static_cast<int>((__float_as_uint(vmax) >> 23) & 0xFFu) - 126 : 0;
+    const float fnorm = __builtin_amdgcn_ldexpf(1.0f, -ex);
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const float sf = vsr[i] * fnorm;                              // exact (power of two)
+      const float hi = __uint_as_float(__float_as_uint(sf) & 0xFFFF0000u);
+      sfh_s[blk0 + i][lane] = static_cast<_Float16>(hi);
+      sfl_s[blk0 + i][lane] = static_cast<_Float16>(sf - hi);
+    }
+    if (lane == 0) g_s[wave] = __builtin_amdgcn_ldexpf(1.0f, ex);
+    // ---- key codes as float16 integers
+#pragma unroll
+    for (int i = 0; i < KGT; ++i) {
+      const int e = tid + 256 * i;
       h8 hv[4];
-      codes_h16<ASYM>(w[0], w[1], w[2], hv);
-      h8* dst = reinterpret_cast<h8*>(kt + tok * KROW + 32 * g);
+      codes_h16<ASYM>(kw[i][0], kw[i][1], kw[i][2], hv);
+      h8* dst = reinterpret_cast<h8*>(kt + (e / NG) * KROW + 32 * (e % NG));
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = hv[k];
     }
-    for (int e = tid; e < 2 * D; e += 256) {          // (dim, 32-token half) groups
-      const int dim = e % D, half = e / D;
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(
-          rv, static_cast<uint32_t>((t0 / kTile + half) * D * 12 + 12 * dim), 0, 0);
+    // the wave reads back only the scales it wrote itself
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- value planes: u sf_hi (exact) and u sf_lo, [dim][token]
+#pragma unroll
+    for (int i = 0; i < VGW; ++i) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const int grp = lane + 64 * i, dim = wave * WD + grp % WD, half = grp / WD;
+      const int blk = dim / BLOCK;
       h8 hv[4];
-      codes_h16<ASYM>(w[0], w[1], w[2], hv);
-      // value rows are 8-byte aligned only (VROW * 2 = 136 bytes): 8-byte stores
-      uint2* dst = reinterpret_cast<uint2*>(vt + dim * VROW + 32 * half);
+      codes_h16<ASYM>(vw[i][0], vw[i][1], vw[i][2], hv);
+      const uint4* sh = reinterpret_cast<const uint4*>(&sfh_s[blk][32 * half]);
+      const uint4* sl = reinterpret_cast<const uint4*>(&sfl_s[blk][32 * half]);
+      uint2* dh = reinterpret_cast<uint2*>(vh + dim * VROW + 32 * half);   // 8-byte aligned rows
+      uint2* dl = reinterpret_cast<uint2*>(vl + dim * VROW + 32 * half);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint4 x = __builtin_bit_cast(uint4, hv[k]);
-        dst[2 * k] = make_uint2(x.x, x.y);
-        dst[2 * k + 1] = make_uint2(x.z, x.w);
+        const uint4 c = __builtin_bit_cast(uint4, hv[k]);
+        const uint4 a = sh[k], b = sl[k];
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w}, aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+        uint32_t oh[4], ol[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const h2 cc = __builtin_bit_cast(h2, cw[m]);
+          oh[m] = __builtin_bit_cast(uint32_t, cc * __builtin_bit_cast(h2, aw[m]));
+          ol[m] = __builtin_bit_cast(uint32_t, cc * __builtin_bit_cast(h2, bw[m]));
+        }
+        dh[2 * k] = make_uint2(oh[0], oh[1]);
+        dh[2 * k + 1] = make_uint2(oh[2], oh[3]);
+        dl[2 * k] = make_uint2(ol[0], ol[1]);
+        dl[2 * k + 1] = make_uint2(ol[2], ol[3]);
       }
     }
+    if (it + 1 < n_kt) load_tile(t0 + kKT);
     __syncthreads();
 
     // ---- S^T for the wave's 16 queries: 4 token tiles of 16; per key block the exact
     // code products are scaled by the tokens' block scales
+    const bool masked = t0 + kKT - 1 > pos_first + 16 * wave;   // some token after a query
     float sv[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -313,11 +392,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = t0 + 16 * tt + 4 * lq + r;
-        const float lg = __builtin_fmaf(s4[r], qmax, z4[r]);
-        sv[tt][r] = tok <= my_pos ? lg : -INFINITY;    // causal mask (and tokens past T)
-      }
+      for (int r = 0; r < 4; ++r) sv[tt][r] = __builtin_fmaf(s4[r], qmax, z4[r]);
+    }
+    if (masked) {   // causal mask (and tokens past T)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t0 + 16 * tt + 4 * lq + r > my_pos) sv[tt][r] = -INFINITY;
     }
     float tmax = -INFINITY;
 #pragma unroll
@@ -342,72 +424,53 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[nt][r] *= al[r];
     }
-    // ---- probabilities of query j; tokens 16 tt + 4 lq + r
-    float pr[4][4];
+    // ---- probabilities of query j (tokens 16 tt + 4 lq + r) as float16 hi + lo, packed
+    // as the A operand of P.V: K chunk cc covers tokens 32 cc + 4 lq + r and
+    // 32 cc + 16 + 4 lq + r.  p <= 2^8 (lazy maximum), so float16 holds it.
+    h8 ph[2], pl[2];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[tt][r] = __builtin_amdgcn_exp2f(sv[tt][r] - m_run);
-        l_run += pr[tt][r];
-      }
-    // ---- P.V per value block: weights w = p s_v relative to their maximum over the
-    // tile, as float16 hi + lo packed as the A operand (K chunk cc covers tokens
-    // 32 cc + 4 lq + r and 32 cc + 16 + 4 lq + r of this lane's query j)
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-      float w[4][4];
-      float wm = 0.0f;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float4 vs = *reinterpret_cast<const float4*>(&vms_s[blk][16 * tt + 4 * lq]);
-        const float vsr[4] = {vs.x, vs.y, vs.z, vs.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          w[tt][r] = pr[tt][r] * vsr[r];
-          wm = fmaxf(wm, w[tt][r]);
-        }
+        const float pr = __builtin_amdgcn_exp2f(sv[tt][r] - m_run);
+        l_run += pr;
+        const H2 xs = split_h16(pr);
+        ph[tt >> 1][4 * (tt & 1) + r] = xs.hi;
+        pl[tt >> 1][4 * (tt & 1) + r] = xs.lo;
         if constexpr (ASYM) {
-          const float4 vz = *reinterpret_cast<const float4*>(&vmz_s[blk][16 * tt + 4 * lq]);
-          zacc[blk] = __builtin_fmaf(pr[tt][0], vz.x, zacc[blk]);
-          zacc[blk] = __builtin_fmaf(pr[tt][1], vz.y, zacc[blk]);
-          zacc[blk] = __builtin_fmaf(pr[tt][2], vz.z, zacc[blk]);
-          zacc[blk] = __builtin_fmaf(pr[tt][3], vz.w, zacc[blk]);
+          // zero-points: sum of p z_v per block, in float32
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk)
+            zacc[blk] = __builtin_fmaf(pr, vmz_s[blk][16 * tt + 4 * lq + r], zacc[blk]);
         }
       }
-      wm = fmaxf(wm, swz_xor16(wm));
-      wm = fmaxf(wm, __shfl_xor(wm, 32, 64));
-      // weights below 1e-30 of a whole tile and block are dropped (no reciprocal overflow)
-      const float winv = wm > 1.0e-30f ? 1.0f / wm : 0.0f;
-      h8 ph[2], pl[2];
+    // ---- P.V: ph vh + ph vl + pl vh per 32-token chunk, scaled back by the normaliser
+    // of the wave that unpacked the dims
+    float gw[4];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+    for (int w = 0; w < 4; ++w) gw[w] = g_s[w];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const H2 xs = split_h16(w[tt][r] * winv);
-          ph[tt >> 1][4 * (tt & 1) + r] = xs.hi;
-          pl[tt >> 1][4 * (tt & 1) + r] = xs.lo;
-        }
-      float wq[4];
+    for (int nt = 0; nt < NT; ++nt) {
+      const _Float16* rh = vh + (16 * nt + j) * VROW + 4 * lq;
+      const _Float16* rl = vl + (16 * nt + j) * VROW + 4 * lq;
+      f4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wq[r] = __shfl(wm > 1.0e-30f ? wm : 0.0f, 4 * lq + r, 64);
-#pragma unroll
-      for (int t = 0; t < TPB; ++t) {
-        const int nt = blk * TPB + t;
-        const _Float16* vr = vt + (16 * nt + j) * VROW + 4 * lq;
-        f4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr + 32 * cc);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 32 * cc + 16);
-          const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
-          const h8 bv = __builtin_bit_cast(h8, w4);
-          c = mfma_f16(ph[cc], bv, c);
-          c = mfma_f16(pl[cc], bv, c);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(c[r], wq[r], acc[nt][r]);
+      for (int cc = 0; cc < 2; ++cc) {
+        const uint2 h0 = *reinterpret_cast<const uint2*>(rh + 32 * cc);
+        const uint2 h1 = *reinterpret_cast<const uint2*>(rh + 32 * cc + 16);
+        const uint2 l0 = *reinterpret_cast<const uint2*>(rl + 32 * cc);
+        const uint2 l1 = *reinterpret_cast<const uint2*>(rl + 32 * cc + 16);
+        const uint32_t wh[4] = {h0.x, h0.y, h1.x, h1.y};
+        const uint32_t wl[4] = {l0.x, l0.y, l1.x, l1.y};
+        const h8 bh = __builtin_bit_cast(h8, wh);
+        const h8 bl = __builtin_bit_cast(h8, wl);
+        c = mfma_f16(ph[cc], bh, c);
+        c = mfma_f16(ph[cc], bl, c);
+        c = mfma_f16(pl[cc], bh, c);
       }
+      const float g = gw[nt / NTW];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(c[r], g, acc[nt][r]);
     }
   }
 
