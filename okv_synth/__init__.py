@@ -62,6 +62,7 @@ class Workload:
     key_decay: bool
     decode_steps: int     # append-one-then-decode steps after the prefill
     eps: float = 1e-6
+    bits: int = 3         # code width b (2, 3 or 4)
 
     @property
     def group(self) -> int:
@@ -77,7 +78,7 @@ class Workload:
 
     def row_bytes(self) -> int:
         """Bytes one (token, KV head, tensor) record occupies: codes + metadata."""
-        return 3 * self.d // 8 + self.meta_bytes_per_row()
+        return self.bits * self.d // 8 + self.meta_bytes_per_row()
 
     def cache_bytes(self, tokens: int | None = None) -> int:
         t = self.tokens if tokens is None else tokens

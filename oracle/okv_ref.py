@@ -5,7 +5,8 @@ HIP library.
 
 A "spec" argument is any object with the attributes ``d``, ``block``, ``quant``
 ('sym' | 'asym'), ``scale_dtype`` ('f32' | 'f16' | 'e4m3'), ``eps`` and
-``rotation`` ('sign' | 'so4').
+``rotation`` ('sign' | 'so4'), and optionally ``bits`` (the code width b: 2, 3 or
+4; 3 when absent).
 
 Readings of points the pages leave open are marked READING; the list of all of
 them, with reasons, is kept with the design notes of the repository.
@@ -17,15 +18,29 @@ import numpy as np
 __all__ = [
     "hadamard", "rotation_matrix", "fwht_f32", "rotate_f32", "c_norm_f32",
     "f16_store", "e4m3_encode", "e4m3_decode",
-    "rne_codes", "quantize_f32", "dequantize",
-    "G32_BIT_POSITIONS", "pack_g32", "unpack_g32", "pack_rows", "unpack_rows",
+    "rne_codes", "quantize_f32", "dequantize", "bits_of", "group_bytes",
+    "G32_BIT_POSITIONS", "group_bit_positions", "pack_g32", "unpack_g32", "pack_rows", "unpack_rows",
     "pack_vtiles", "unpack_vtiles",
     "write_unit", "meta_values", "attend_unit", "attend_exact", "attend_prefill_unit",
 ]
 
 F32 = np.float32
 TILE = 32          # tokens per V tile
-GROUP = 32         # codes per packed group (12 bytes)
+GROUP = 32         # codes per packed group (4 b bytes: 12 for b = 3)
+BITS = (2, 3, 4)   # code widths
+
+
+def bits_of(spec) -> int:
+    """Code width b of a spec (3 unless the spec says otherwise)."""
+    b = int(getattr(spec, "bits", 3))
+    if b not in BITS:
+        raise ValueError(f"code width {b} not in {BITS}")
+    return b
+
+
+def group_bytes(bits: int) -> int:
+    """Bytes of one packed group of 32 b-bit codes."""
+    return 4 * bits
 
 
 # ---------------------------------------------------------------------------
@@ -226,45 +241,52 @@ def rne_codes(y, s, lo: int, hi: int) -> np.ndarray:
 
 
 def quantize_f32(y, spec):
-    """Blockwise 3-bit quantisation of rotated vectors (last axis d).
+    """Blockwise b-bit quantisation of rotated vectors (last axis d).
 
-    Symmetric ('sym'; the idea card, Mathematical statement / Key formulas, b = 3):
-      s   = RN32(RN32(max_j |y_j| + eps) / 3), stored as scale_dtype (RNE);
-      c_j = clip(round(y_j / s_st), -3, 3), stored as u_j = c_j + 4 in 0..7.
+    Symmetric ('sym'; the idea card, Mathematical statement / Key formulas, with
+    L = 2^(b-1) - 1 levels on each side; the card fixes b = 3, L = 3):
+      s   = RN32(RN32(max_j |y_j| + eps) / L), stored as scale_dtype (RNE);
+      c_j = clip(round(y_j / s_st), -L, L), stored as u_j = c_j + 2^(b-1).
     Asymmetric ('asym'; the news item, third paragraph: unsigned 3-bit codes with
-    an FP8 scale and zero-point per 64-element sub-block):
-      s   = RN32(RN32(max - min) / 7), z = min, both stored as E4M3 (RNE, sat);
-      u_j = clip(round(RN32(y_j - z_st) / s_st), 0, 7).
+    an FP8 scale and zero-point per 64-element sub-block; for b bits the 2^b codes
+    0 .. 2^b - 1 span max - min):
+      s   = RN32(RN32(max - min) / (2^b - 1)), z = min, both stored as E4M3 (RNE, sat);
+      u_j = clip(round(RN32(y_j - z_st) / s_st), 0, 2^b - 1).
     READING: the codes are taken against the *stored* scale (and zero-point), so
     the reconstruction x_hat = s_st * c (or s_st * u + z_st) uses exactly what is
     kept; eps is added for 'sym' only.
+    READING: widths other than 3 keep every other choice of the 3-bit path (the
+    same excess code u = c + 2^(b-1), the same rounding and scale storage).
     Returns (u uint8 (..., d), meta): meta is the stored scale array (..., d/m)
     for 'sym' and a uint8 (..., d/m, 2) array of (scale, zero-point) E4M3 bits
     for 'asym'.
     """
+    b = bits_of(spec)
     y = np.asarray(y, dtype=F32)
     d = y.shape[-1]
     m = spec.block
     yb = y.reshape(y.shape[:-1] + (d // m, m))
     if spec.quant == "sym":
+        lev = 2 ** (b - 1) - 1
         mx = np.max(np.abs(yb), axis=-1)
-        s32 = (mx + F32(spec.eps)) / F32(3.0)
+        s32 = (mx + F32(spec.eps)) / F32(lev)
         stored, s_val = _store_scale(s32, spec.scale_dtype)
-        c = rne_codes(yb, s_val, -3, 3)
-        u = (c + 4).astype(np.uint8)
+        c = rne_codes(yb, s_val, -lev, lev)
+        u = (c + 2 ** (b - 1)).astype(np.uint8)
         return u.reshape(y.shape), stored
     if spec.quant == "asym":
         if spec.scale_dtype != "e4m3":
             raise ValueError("asymmetric quantiser stores E4M3 meta")
+        top = 2 ** b - 1
         mn = np.min(yb, axis=-1)
         mx = np.max(yb, axis=-1)
-        s32 = (mx - mn) / F32(7.0)
+        s32 = (mx - mn) / F32(top)
         s_bits = e4m3_encode(s32)
         z_bits = e4m3_encode(mn)
         s_val = e4m3_decode(s_bits)
         z_val = e4m3_decode(z_bits)
         t = yb - z_val[..., None]                       # float32, one rounding
-        u = rne_codes(t, s_val, 0, 7).astype(np.uint8)
+        u = rne_codes(t, s_val, 0, top).astype(np.uint8)
         return u.reshape(y.shape), np.stack([s_bits, z_bits], axis=-1)
     raise ValueError(spec.quant)
 
@@ -272,12 +294,12 @@ def quantize_f32(y, spec):
 def meta_values(meta, spec):
     """(scale, offset) float64 arrays (..., d/m) such that x_hat = scale * u + offset.
 
-    'sym':  x_hat = s (u - 4)       -> (s, -4 s)
-    'asym': x_hat = s u + z         -> (s, z)
+    'sym':  x_hat = s (u - 2^(b-1))     -> (s, -2^(b-1) s)
+    'asym': x_hat = s u + z             -> (s, z)
     """
     if spec.quant == "sym":
         s = np.asarray(meta).astype(np.float64)
-        return s, -4.0 * s
+        return s, -float(2 ** (bits_of(spec) - 1)) * s
     s = e4m3_decode(meta[..., 0]).astype(np.float64)
     z = e4m3_decode(meta[..., 1]).astype(np.float64)
     return s, z
@@ -296,79 +318,93 @@ def dequantize(u, meta, spec) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Packing ("pack3": 32 three-bit codes -> 12 bytes)
+# Packing: 32 b-bit codes -> 4 b bytes
 # ---------------------------------------------------------------------------
 
-def _g32_positions() -> np.ndarray:
-    """Bit index (0..95, little-endian over the 12 bytes) of bit q of code i.
+def group_bit_positions(bits: int = 3) -> np.ndarray:
+    """Bit index (little-endian over the 4 b bytes) of bit q of code i: (32, b).
 
     READING: the idea card (Implementation notes) only says that the codes are
-    packed into bytes; the layout chosen here keeps 8 codes per 32-bit word in
-    byte lanes:
-      codes 0..23: word k = i // 8, r = i % 8, byte b = r % 4, field f = r // 4,
-                   bits 8b + 3f .. 8b + 3f + 2 of word k;
-      codes 24..27 (b = i - 24): bits 0-1 -> bits 8b+6, 8b+7 of word 0,
-                   bit 2 -> bit 8b+6 of word 2;
-      codes 28..31 (b = i - 28): bits 0-1 -> bits 8b+6, 8b+7 of word 1,
-                   bit 2 -> bit 8b+7 of word 2.
+    packed into bytes; the layouts chosen here keep the codes in byte lanes of
+    32-bit words, so that byte j of unpacked word k holds code 4 k + j:
+      b = 4: word k = i // 8, r = i % 8, byte r % 4, field f = r // 4:
+             bits 8 (r % 4) + 4 f .. + 3 of word k (two codes per byte);
+      b = 2: word k = i // 16, r = i % 16, byte r % 4, field f = r // 4:
+             bits 8 (r % 4) + 2 f .. + 1 of word k (four codes per byte);
+      b = 3: codes 0..23: word k = i // 8, r = i % 8, byte r % 4, field f = r // 4,
+             bits 8 (r % 4) + 3 f .. + 2 of word k;
+             codes 24..27 (j = i - 24): bits 0-1 -> bits 8j+6, 8j+7 of word 0,
+             bit 2 -> bit 8j+6 of word 2;
+             codes 28..31 (j = i - 28): bits 0-1 -> bits 8j+6, 8j+7 of word 1,
+             bit 2 -> bit 8j+7 of word 2.
     """
-    pos = np.zeros((GROUP, 3), dtype=np.int64)
+    pos = np.zeros((GROUP, bits), dtype=np.int64)
     for i in range(GROUP):
-        if i < 24:
+        if bits in (2, 4):
+            per_word = 32 // bits
+            k, r = divmod(i, per_word)
+            byte, f = r % 4, r // 4
+            for q in range(bits):
+                pos[i, q] = 32 * k + 8 * byte + bits * f + q
+        elif i < 24:
             k, r = divmod(i, 8)
-            b, f = r % 4, r // 4
+            byte, f = r % 4, r // 4
             for q in range(3):
-                pos[i, q] = 32 * k + 8 * b + 3 * f + q
+                pos[i, q] = 32 * k + 8 * byte + 3 * f + q
         elif i < 28:
-            b = i - 24
-            pos[i] = [8 * b + 6, 8 * b + 7, 64 + 8 * b + 6]
+            j = i - 24
+            pos[i] = [8 * j + 6, 8 * j + 7, 64 + 8 * j + 6]
         else:
-            b = i - 28
-            pos[i] = [32 + 8 * b + 6, 32 + 8 * b + 7, 64 + 8 * b + 7]
+            j = i - 28
+            pos[i] = [32 + 8 * j + 6, 32 + 8 * j + 7, 64 + 8 * j + 7]
     return pos
 
 
-G32_BIT_POSITIONS = _g32_positions()
+G32_BIT_POSITIONS = group_bit_positions(3)
+_POSITIONS = {b: group_bit_positions(b) for b in BITS}
 
 
-def pack_g32(e) -> np.ndarray:
-    """(..., 32) codes in 0..7 -> (..., 12) bytes (layout of _g32_positions)."""
+def pack_g32(e, bits: int = 3) -> np.ndarray:
+    """(..., 32) codes in 0 .. 2^b - 1 -> (..., 4 b) bytes (layout of
+    group_bit_positions)."""
     e = np.asarray(e).astype(np.int64)
-    if e.shape[-1] != GROUP or np.any((e < 0) | (e > 7)):
-        raise ValueError("need (..., 32) codes in 0..7")
-    bits = np.zeros(e.shape[:-1] + (96,), dtype=np.uint8)
-    for q in range(3):
-        bits[..., G32_BIT_POSITIONS[:, q]] = ((e >> q) & 1).astype(np.uint8)
-    return np.packbits(bits, axis=-1, bitorder="little")
+    if e.shape[-1] != GROUP or np.any((e < 0) | (e >= 2 ** bits)):
+        raise ValueError(f"need (..., 32) codes in 0..{2 ** bits - 1}")
+    pos = _POSITIONS[bits]
+    out = np.zeros(e.shape[:-1] + (32 * bits,), dtype=np.uint8)
+    for q in range(bits):
+        out[..., pos[:, q]] = ((e >> q) & 1).astype(np.uint8)
+    return np.packbits(out, axis=-1, bitorder="little")
 
 
-def unpack_g32(g) -> np.ndarray:
-    """(..., 12) bytes -> (..., 32) codes (uint8)."""
+def unpack_g32(g, bits: int = 3) -> np.ndarray:
+    """(..., 4 b) bytes -> (..., 32) codes (uint8)."""
     g = np.asarray(g, dtype=np.uint8)
-    bits = np.unpackbits(g, axis=-1, bitorder="little").astype(np.int64)
+    raw = np.unpackbits(g, axis=-1, bitorder="little").astype(np.int64)
+    pos = _POSITIONS[bits]
     e = np.zeros(g.shape[:-1] + (GROUP,), dtype=np.int64)
-    for q in range(3):
-        e |= bits[..., G32_BIT_POSITIONS[:, q]] << q
+    for q in range(bits):
+        e |= raw[..., pos[:, q]] << q
     return e.astype(np.uint8)
 
 
-def pack_rows(u) -> np.ndarray:
-    """Key cache rows: (..., d) codes -> (..., 3d/8) bytes; dims 32g..32g+31 form
-    group g at bytes 12g..12g+11."""
+def pack_rows(u, bits: int = 3) -> np.ndarray:
+    """Key cache rows: (..., d) codes -> (..., b d/8) bytes; dims 32g..32g+31 form
+    group g at bytes 4 b g .. 4 b g + 4 b - 1."""
     u = np.asarray(u)
     d = u.shape[-1]
-    g = pack_g32(u.reshape(u.shape[:-1] + (d // GROUP, GROUP)))
-    return g.reshape(u.shape[:-1] + (3 * d // 8,))
+    g = pack_g32(u.reshape(u.shape[:-1] + (d // GROUP, GROUP)), bits)
+    return g.reshape(u.shape[:-1] + (bits * d // 8,))
 
 
-def unpack_rows(r, d: int) -> np.ndarray:
+def unpack_rows(r, d: int, bits: int = 3) -> np.ndarray:
     r = np.asarray(r, dtype=np.uint8)
-    e = unpack_g32(r.reshape(r.shape[:-1] + (d // GROUP, 12)))
+    e = unpack_g32(r.reshape(r.shape[:-1] + (d // GROUP, group_bytes(bits))), bits)
     return e.reshape(r.shape[:-1] + (d,))
 
 
-def pack_vtiles(u) -> np.ndarray:
-    """Value cache tiles: (T, d) codes of one (sequence, head) -> (ceil(T/32), d, 12).
+def pack_vtiles(u, bits: int = 3) -> np.ndarray:
+    """Value cache tiles: (T, d) codes of one (sequence, head) -> (ceil(T/32), d, 4 b).
 
     READING (layout): tokens are grouped 32 to a tile; inside a tile, dim j holds
     the codes of the tile's 32 tokens as one group (token 32 tau + i is code i).
@@ -380,12 +416,12 @@ def pack_vtiles(u) -> np.ndarray:
     full = np.zeros((nt * TILE, d), dtype=np.uint8)
     full[:t] = u
     tiles = full.reshape(nt, TILE, d).transpose(0, 2, 1)      # (tile, dim, token-in-tile)
-    return pack_g32(tiles)
+    return pack_g32(tiles, bits)
 
 
-def unpack_vtiles(v, t: int) -> np.ndarray:
-    """(ntiles, d, 12) -> (t, d) codes."""
-    e = unpack_g32(np.asarray(v, dtype=np.uint8))            # (tile, dim, 32)
+def unpack_vtiles(v, t: int, bits: int = 3) -> np.ndarray:
+    """(ntiles, d, 4 b) -> (t, d) codes."""
+    e = unpack_g32(np.asarray(v, dtype=np.uint8), bits)      # (tile, dim, 32)
     nt, d, _ = e.shape
     return e.transpose(0, 2, 1).reshape(nt * TILE, d)[:t]
 
@@ -398,9 +434,10 @@ def write_unit(k, v, spec, params32):
     """Rotate, quantise and pack the keys and values of one (sequence, KV head).
 
     The idea card, Implementation notes (write path): each new key and value
-    vector is rotated by U, given one scale per block, rounded to signed 3-bit
-    codes and packed; only codes and scales are kept.  k, v: (T, d) float32 (exact widening of the inputs).
-    Returns a dict: k_codes (T, 3d/8) uint8, v_codes (ceil(T/32), d, 12) uint8,
+    vector is rotated by U, given one scale per block, rounded to signed b-bit
+    codes (b = 3 on the card) and packed; only codes and scales are kept.  k, v:
+    (T, d) float32 (exact widening of the inputs).
+    Returns a dict: k_codes (T, b d/8) uint8, v_codes (ceil(T/32), d, 4 b) uint8,
     k_meta / v_meta (T, d/m) scales or (T, d/m, 2) E4M3 bytes, plus the code
     arrays k_u / v_u (T, d) and the rotated float32 vectors k_rot / v_rot.
     """
@@ -408,8 +445,9 @@ def write_unit(k, v, spec, params32):
     v_rot = rotate_f32(v, spec.rotation, params32)
     k_u, k_meta = quantize_f32(k_rot, spec)
     v_u, v_meta = quantize_f32(v_rot, spec)
+    b = bits_of(spec)
     return {
-        "k_codes": pack_rows(k_u), "v_codes": pack_vtiles(v_u),
+        "k_codes": pack_rows(k_u, b), "v_codes": pack_vtiles(v_u, b),
         "k_meta": k_meta, "v_meta": v_meta,
         "k_u": k_u, "v_u": v_u, "k_rot": k_rot, "v_rot": v_rot,
     }
@@ -445,9 +483,9 @@ def attend_unit(q, k_codes, k_meta, v_codes, v_meta, t: int, spec, u_mat) -> np.
     vectors.
     Returns (G, d) float64.
     """
-    d = spec.d
-    k_hat = dequantize(unpack_rows(np.asarray(k_codes)[:t], d), np.asarray(k_meta)[:t], spec)
-    v_hat = dequantize(unpack_vtiles(v_codes, t), np.asarray(v_meta)[:t], spec)
+    d, b = spec.d, bits_of(spec)
+    k_hat = dequantize(unpack_rows(np.asarray(k_codes)[:t], d, b), np.asarray(k_meta)[:t], spec)
+    v_hat = dequantize(unpack_vtiles(v_codes, t, b), np.asarray(v_meta)[:t], spec)
     q1 = np.asarray(q, dtype=np.float64) @ u_mat.T          # rows of U q
     y1 = attend_exact(q1, k_hat, v_hat)
     return y1 @ u_mat                                       # rows of U^T y1
@@ -466,9 +504,9 @@ def attend_prefill_unit(q, positions, k_codes, k_meta, v_codes, v_meta, spec, u_
     """
     positions = [int(x) for x in positions]
     t = max(positions) + 1
-    d = spec.d
-    k_hat = dequantize(unpack_rows(np.asarray(k_codes)[:t], d), np.asarray(k_meta)[:t], spec)
-    v_hat = dequantize(unpack_vtiles(v_codes, t), np.asarray(v_meta)[:t], spec)
+    d, b = spec.d, bits_of(spec)
+    k_hat = dequantize(unpack_rows(np.asarray(k_codes)[:t], d, b), np.asarray(k_meta)[:t], spec)
+    v_hat = dequantize(unpack_vtiles(v_codes, t, b), np.asarray(v_meta)[:t], spec)
     q = np.asarray(q, dtype=np.float64)
     out = np.empty(q.shape, dtype=np.float64)
     for i, pos in enumerate(positions):

@@ -214,3 +214,104 @@ def test_asym_codes_range_and_reconstruction():
     # z is the block minimum to E4M3 precision
     mn = y.reshape(300, 2, 64).min(-1)
     assert np.all(np.abs(z - mn) <= np.abs(mn) * 2.0 ** -4 + 2.0 ** -10)
+
+
+# ---- code widths b = 2 and 4 (the idea card's quantiser with b symbolic:
+# s = (max |x| + eps) / (2^(b-1) - 1), codes clipped to +-(2^(b-1) - 1))
+
+@pytest.mark.parametrize("lo,hi", [(-1, 1), (0, 3), (-7, 7), (0, 15)])
+def test_rne_codes_brute_force_other_widths(lo, hi):
+    s = np.float32(0.3125)
+    ys = []
+    for k in range(lo - 2, hi + 2):
+        t = np.float32((k + 0.5) * np.float64(s))
+        ys.append(t)
+        for n in (1, 2, 7):
+            up, dn = t, t
+            for _ in range(n):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+            ys += [up, dn]
+    ys = np.array(ys, dtype=np.float32)
+    got = oracle.rne_codes(ys[None, :], np.array([s], np.float32), lo, hi)[0]
+    assert list(got) == [rne_fraction(y, s, lo, hi) for y in ys]
+
+
+@pytest.mark.parametrize("bits,lev", [(2, 1), (4, 7)])
+def test_sym_unit_vector_codes_b(bits, lev):
+    d = 128
+    sp = spec(bits=bits)
+    h = scipy.linalg.hadamard(d)
+    for j in (0, 33, 127):
+        x = np.zeros(d, np.float32)
+        x[j] = 1.0
+        y = oracle.rotate_f32(x, "sign", np.ones(d, np.float32))
+        u, meta = oracle.quantize_f32(y, sp)
+        assert np.array_equal(u.astype(int) - 2 ** (bits - 1), lev * h[:, j])
+        # s = RN32(RN32(1/sqrt(d) + eps) / lev)
+        want = (np.float32(oracle.c_norm_f32(d)) + np.float32(1e-6)) / np.float32(lev)
+        assert np.all(meta == want)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_sym_block_max_and_error_bound_b(bits):
+    lev = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(20 + bits)
+    sp = spec(bits=bits, scale_dtype="f16")
+    y = (rng.standard_normal((400, 128)) * rng.lognormal(0, 1, (400, 1))).astype(np.float32)
+    u, meta = oracle.quantize_f32(y, sp)
+    assert u.min() >= 1 and u.max() <= 2 ** bits - 1
+    c = (u.astype(int) - 2 ** (bits - 1)).reshape(400, 4, 32)
+    yb = y.reshape(400, 4, 32)
+    s = np.asarray(meta).astype(np.float64)
+    arg = np.abs(yb).argmax(-1)
+    cm = np.take_along_axis(c, arg[..., None], -1)[..., 0]
+    ym = np.take_along_axis(yb, arg[..., None], -1)[..., 0]
+    assert np.all(cm == lev * np.sign(ym))
+    assert np.all(np.abs(yb - s[..., None] * c) <= s[..., None] / 2)
+    s32 = (np.abs(yb).max(-1) + np.float32(1e-6)) / np.float32(lev)
+    assert np.array_equal(meta, s32.astype(np.float16))
+    # meta_values: x_hat = s (u - 2^(b-1))
+    xh = oracle.dequantize(u, meta, sp).reshape(400, 4, 32)
+    assert np.array_equal(xh, s[..., None] * c)
+
+
+def test_asym_small_example_by_hand_b4():
+    # block of 64 values 0..63: s = RN32(63 / 15) = 4.2 -> E4M3 4.0 (the neighbours
+    # are 4.0 and 4.5); z = 0; u_j = rne(j / 4) clipped to 15: 2/4 -> 0 (tie, even),
+    # 6/4 -> 2, 10/4 -> 2, 59/4 -> 15 (14.75), 63/4 -> 16 -> clip 15
+    sp = spec(quant="asym", block=64, scale_dtype="e4m3", eps=0.0, bits=4)
+    y = np.tile(np.arange(64, dtype=np.float32), 2)[None]
+    u, meta = oracle.quantize_f32(y, sp)
+    assert oracle.e4m3_decode(meta[0, 0, 0]) == 4.0 and oracle.e4m3_decode(meta[0, 0, 1]) == 0.0
+    assert list(u[0, :64]) == [rne_fraction(j, 4.0, 0, 15) for j in range(64)]
+    assert (u[0, 2], u[0, 6], u[0, 10], u[0, 59], u[0, 63]) == (0, 2, 2, 15, 15)
+
+
+def test_asym_small_example_by_hand_b2():
+    # s = RN32(63 / 3) = 21 -> E4M3: 21 lies halfway between 20 (mantissa 010) and
+    # 22 (mantissa 011), ties to even -> 20; u_j = rne(j / 20) clipped to 3:
+    # 10 -> 0 (tie), 29 -> 1, 30 -> 2 (tie), 31 -> 2, 50 -> 2 (tie), 63 -> 3
+    sp = spec(quant="asym", block=64, scale_dtype="e4m3", eps=0.0, bits=2)
+    y = np.tile(np.arange(64, dtype=np.float32), 2)[None]
+    u, meta = oracle.quantize_f32(y, sp)
+    assert oracle.e4m3_decode(meta[0, 0, 0]) == 20.0
+    assert list(u[0, :64]) == [rne_fraction(j, 20.0, 0, 3) for j in range(64)]
+    assert (u[0, 10], u[0, 29], u[0, 30], u[0, 31], u[0, 50], u[0, 63]) == (0, 1, 2, 2, 2, 3)
+
+
+def test_more_bits_less_error():
+    # same rotated data: reconstruction error falls with b (one code step is 2 s / ...)
+    rng = np.random.default_rng(31)
+    y = (rng.standard_normal((300, 128)) * 0.5).astype(np.float32)
+    errs = []
+    for bits in (2, 3, 4):
+        sp = spec(bits=bits)
+        u, meta = oracle.quantize_f32(y, sp)
+        errs.append(np.mean((oracle.dequantize(u, meta, sp) - y) ** 2))
+    assert errs[0] > 2 * errs[1] > 4 * errs[2]
+
+
+def test_bits_validation():
+    with pytest.raises(ValueError):
+        oracle.quantize_f32(np.zeros((1, 128), np.float32), spec(bits=5))
