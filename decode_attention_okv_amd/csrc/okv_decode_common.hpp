@@ -10,6 +10,20 @@ namespace dec {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kWMax = 4194303.0f;   // value weights: 22-bit fixed point per step (2^22 - 1)
 constexpr int kQMax = 8000000;        // |q| fixed-point limit: three balanced int8 digits
+
+// Fixed-point limit of q for sums of q times a code term over `span` dims: the int32
+// accumulators wrap, so only the final sum must fit, and |sum| <= span * limit * cmax
+// where cmax bounds |code term| (|u - 4| <= 3 for symmetric 3-bit codes, u <= 7 for
+// asymmetric ones).  Capped at kQMax.
+constexpr int q_limit(int span, int cmax) {
+  return 2147483647LL / (static_cast<long long>(span) * cmax) < kQMax
+             ? static_cast<int>(2147483647LL / (static_cast<long long>(span) * cmax))
+             : kQMax;
+}
+// Same for the value weights (64 tokens per product), capped at `cap`.
+constexpr int w_limit(int cmax, int cap) {
+  return 2147483647LL / (64LL * cmax) < cap ? static_cast<int>(2147483647LL / (64LL * cmax)) : cap;
+}
 constexpr int kMaxSplitsDev = 256;    // must match the host's split-K capacity
 
 enum : int { kFmtSymF32 = 0, kFmtSymF16 = 1, kFmtAsym = 2 };

@@ -78,6 +78,8 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
   constexpr int NBQ = 8;               // 16-dim output blocks per quad
   constexpr int DPL = D / 64;          // value groups per lane and tile
   constexpr int WPLANE = 16 * kWRow;   // bytes of one quad's 16 weight rows
+  // fixed-point limits that keep every int32 sum exact (see q_limit)
+  constexpr int QMAX = q_limit(SEG, ASYM ? 7 : 3);
   using Raw = HeadRaw<NQ, DPL>;
   using Meta = HeadMeta<NQ>;
   static_assert(D * 7 + 64 <= 4 * 128 * 64, "prologue fits the value-row region");
@@ -133,9 +135,9 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
   __syncthreads();
   amax_q = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
   if (tid < D) {
-    const float inv = amax_q > 0.0f ? static_cast<float>(kQMax) / amax_q : 0.0f;
+    const float inv = amax_q > 0.0f ? static_cast<float>(QMAX) / amax_q : 0.0f;
     int qi = static_cast<int>(__builtin_rintf(yq * inv));
-    qi = qi > kQMax ? kQMax : (qi < -kQMax ? -kQMax : qi);
+    qi = qi > QMAX ? QMAX : (qi < -QMAX ? -QMAX : qi);
     const int lo = ((qi + 128) & 255) - 128;
     const int q2 = (qi - lo) >> 8;
     const int mi = ((q2 + 128) & 255) - 128;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
   const int j = lane & 15;             // token (Q.K) / dim in the 16-dim block (P.V); A row
   const int lq = lane >> 4;            // k-chunk of the operands; block of the result rows
   const bool bvalid = lq < BPQ;        // lane's result rows belong to segment lq of the quad
-  const float c_logit = fmaxf((amax_q / static_cast<float>(kQMax)) * kLog2e * cn, 1.0e-30f);
+  const float c_logit = fmaxf((amax_q / static_cast<float>(QMAX)) * kLog2e * cn, 1.0e-30f);
   // A operands of Q.K: row j = 4 bA + d, dims 32 (4 qd + lq) + 16 c + e (e < 16)
   v4i qa[NQ][2];
   int cinit[NQ][4];

@@ -111,6 +111,8 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   constexpr int DPL = D / 64;          // value groups per lane and tile
   constexpr int UPB = 4 / BPQ;         // useful P.V rows per lane and 16-dim block
   constexpr int NU = G * D / 256;      // query elements per thread in the prologue
+  // fixed-point limit that keeps every int32 block sum exact (see q_limit)
+  constexpr int QMAX = q_limit(BLOCK, FMT == kFmtAsym ? 7 : 3);
   constexpr int UB0 = 4 * 128 * 64;    // per-wave value rows of one quad
   constexpr int UB1 = 4 * G * D * 4;   // wave partials in the final combine
   constexpr int UB = UB0 > UB1 ? UB0 : UB1;
@@ -188,9 +190,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   for (int u = 0; u < NU; ++u) {
     const int e = tid + 256 * u, h = e / D, jd = e % D;
     const float am = __uint_as_float(qam_s[h]);
-    const float inv = am > 0.0f ? static_cast<float>(kQMax) / am : 0.0f;
+    const float inv = am > 0.0f ? static_cast<float>(QMAX) / am : 0.0f;
     int qi = static_cast<int>(__builtin_rintf(yq[u] * inv));
-    qi = qi > kQMax ? kQMax : (qi < -kQMax ? -kQMax : qi);
+    qi = qi > QMAX ? QMAX : (qi < -QMAX ? -QMAX : qi);
     int hi, mi, lo;
     digits_q(qi, hi, mi, lo);
     qd_s[0][h][jd] = static_cast<uint8_t>(hi);
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   const int bq = j % BPQ;              // block (within a quad) of this lane's QK column
   const float am_h = __uint_as_float(qam_s[h]);
   // base-2 logit per integer unit (kept positive: a zero query has all-zero logits)
-  const float c_logit = fmaxf((am_h / static_cast<float>(kQMax)) * kLog2e * cn, 1.0e-30f);
+  const float c_logit = fmaxf((am_h / static_cast<float>(QMAX)) * kLog2e * cn, 1.0e-30f);
   // QK B operands: digit d of q_h at dims 32 (4 qd + lq) + 16 c + e (e < 16), zero
   // outside the column's block
   v4i qb[NQ][2][3];

@@ -168,6 +168,50 @@ def test_degenerate_inputs(kernel):
     cache.close()
 
 
+@pytest.mark.parametrize("d,block,quant,hq,kernel", [
+    (128, 128, "sym", 1, "per_head"), (256, 256, "sym", 2, "per_head"),
+    (128, 64, "asym", 8, "grouped"), (128, 64, "asym", 1, "per_head"),
+])
+def test_fixed_point_headroom_aligned(d, block, quant, hq, kernel):
+    # worst case of the int32 sums of q times codes: the rotated query is constant
+    # (every fixed-point element at its limit) and each rotated key block sits at its
+    # top code (symmetric: all +-a; asymmetric: 63 of 64 at +a, one at -a), half of
+    # the tokens flipped so that the two halves have very different logits
+    _need_gpu()
+    import oracle
+    meta = "e4m3" if quant == "asym" else "f16"
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(
+        batch=1, hq=hq, hkv=1, d=d, block=block, quant=quant, scale_dtype=meta, rotation="sign",
+        in_dtype="f32")
+    p32, u = params_of(wl)
+    t = 96
+    yk = np.ones((t, d))
+    if quant == "asym":
+        yk[:, block - 1::block] = -1.0
+    yk[1::2] *= -1.0
+    yk *= (0.5 + np.arange(t) / t)[:, None]
+    rng = np.random.default_rng(5)
+    kx = (yk @ u).astype(np.float32)                       # x = U^T y, as rows
+    vx = rng.standard_normal((t, d)).astype(np.float32)
+    qx = (np.full((hq, d), 0.05) @ u).astype(np.float32)
+    cache = make_cache(wl, 128, p32)
+    cache.set_decode_kernel(kernel)
+    assert cache.decode_kernel() == kernel
+    k = torch.from_numpy(kx).reshape(1, t, 1, d).cuda()
+    v = torch.from_numpy(vx).reshape(1, t, 1, d).cuda()
+    q = torch.from_numpy(qx).reshape(1, hq, d).cuda()
+    say("headroom okv_write/okv_decode_attn", d, block, quant, kernel)
+    cache.write(k, v)
+    out = cache.decode_attn(q).cpu().numpy()
+    ref = oracle.write_unit(kx, vx, wl, p32)
+    assert all(x == 0 for x in compare_unit(cache, wl, 0, 0, t, ref).values())
+    y_ref = decode_ref_unit(wl, qx[None], 0, 0, ref, t, u)
+    err, _ = out_error(out[0], y_ref)
+    say(f"headroom max_err/rms={err:.3e}")
+    assert err <= TOL
+    cache.close()
+
+
 def test_error_paths():
     _need_gpu()
     import decode_attention_okv_amd as okv
