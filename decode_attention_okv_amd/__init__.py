@@ -27,7 +27,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libokv.so")
 
-OKV_ABI_VERSION = 1
+OKV_ABI_VERSION = 2
 OKV_OK, OKV_E_INVALID, OKV_E_ALIGN, OKV_E_CAPACITY, OKV_E_UNSUPPORTED, OKV_E_HIP = range(6)
 QUANT = {"sym": 0, "asym": 1}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
@@ -53,6 +53,7 @@ class OkvConfig(ctypes.Structure):
         ("scale_dtype", ctypes.c_int32),
         ("in_dtype", ctypes.c_int32),
         ("rotation", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
         ("eps", ctypes.c_float),
         ("rot_params", ctypes.POINTER(ctypes.c_float)),
         ("k_codes", ctypes.c_void_p),
@@ -210,7 +211,7 @@ def okv_get_decode_kernel(h):
 
 def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block=32,
                 quant="sym", scale_dtype="f16", in_dtype="bf16", rotation="sign", eps=1e-6,
-                rot_params=None, k_codes=0, v_codes=0, k_meta=0, v_meta=0):
+                rot_params=None, k_codes=0, v_codes=0, k_meta=0, v_meta=0, bits=3):
     """Fill an OkvConfig; ``rot_params`` is a float32 sequence (kept alive on the
     returned object until okv_create copies it)."""
     import array
@@ -223,6 +224,7 @@ def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block
     cfg.in_dtype = DTYPE[in_dtype] if isinstance(in_dtype, str) else in_dtype
     cfg.rotation = ROTATION[rotation] if isinstance(rotation, str) else rotation
     cfg.eps = eps
+    cfg.bits = bits
     if rot_params is not None:
         buf = array.array("f", [float(x) for x in rot_params])
         cfg._rot_buf = buf  # keep alive
@@ -233,7 +235,8 @@ def make_config(*, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block
 
 
 class OkvCache:
-    """A rotated 3-bit KV cache on one GPU: four caller-side tensors plus a handle.
+    """A rotated b-bit KV cache (b = 2, 3 or 4; 3 by default) on one GPU: four
+    caller-side tensors plus a handle.
 
     Shapes follow include/okv.h.  ``rot_params`` is the float32 sign vector (d) or
     the (d/4, 4, 4) SO(4) matrices.
@@ -241,12 +244,13 @@ class OkvCache:
 
     def __init__(self, *, batch, num_q_heads, num_kv_heads, head_dim, max_tokens, block=32,
                  quant="sym", scale_dtype="f16", in_dtype="bf16", rotation="sign", eps=1e-6,
-                 rot_params=None, device="cuda"):
+                 rot_params=None, device="cuda", bits=3):
         import numpy as np
         import torch
         self.batch, self.hq, self.hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
         self.max_tokens, self.block, self.quant, self.scale_dtype = max_tokens, block, quant, scale_dtype
         self.in_dtype = in_dtype
+        self.bits = bits
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -254,13 +258,13 @@ class OkvCache:
         cfg = make_config(batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                           head_dim=head_dim, max_tokens=max_tokens, block=block, quant=quant,
                           scale_dtype=scale_dtype, in_dtype=in_dtype, rotation=rotation, eps=eps,
-                          rot_params=rp)
+                          rot_params=rp, bits=bits)
         st, lay = okv_layout(cfg)
         _check(st, "okv_layout")
         nb = head_dim // block
         shp = (batch, num_kv_heads, max_tokens)
-        self.k_codes = torch.empty(shp + (3 * head_dim // 8,), dtype=torch.uint8, device=self.device)
-        self.v_codes = torch.empty((batch, num_kv_heads, max_tokens // 32, head_dim, 12),
+        self.k_codes = torch.empty(shp + (bits * head_dim // 8,), dtype=torch.uint8, device=self.device)
+        self.v_codes = torch.empty((batch, num_kv_heads, max_tokens // 32, head_dim, 4 * bits),
                                    dtype=torch.uint8, device=self.device)
         if quant == "asym":
             meta_shape, meta_dtype = shp + (nb, 2), torch.uint8

@@ -48,16 +48,25 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link libokv.so."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = []
+    cmds, objs = [], []
     for src, extra in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmds.append([cc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+
+    def run(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+
+    workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "6"))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(run, c) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

@@ -12,9 +12,8 @@ constexpr float kWMax = 4194303.0f;   // value weights: 22-bit fixed point per s
 constexpr int kQMax = 8000000;        // |q| fixed-point limit: three balanced int8 digits
 
 // Fixed-point limit of q for sums of q times a code term over `span` dims: the int32
-// accumulators wrap, so only the final sum must fit, and |sum| <= span * limit * cmax
-// where cmax bounds |code term| (|u - 4| <= 3 for symmetric 3-bit codes, u <= 7 for
-// asymmetric ones).  Capped at kQMax.
+// digit combinations wrap, so only the final sum must fit, and |sum| <= span * limit *
+// cmax where cmax bounds |code term| (code_max).  Capped at kQMax.
 constexpr int q_limit(int span, int cmax) {
   return 2147483647LL / (static_cast<long long>(span) * cmax) < kQMax
              ? static_cast<int>(2147483647LL / (static_cast<long long>(span) * cmax))
@@ -138,6 +137,32 @@ __device__ __forceinline__ int combine3(int a, int b, int c) {
 // 16-byte slot of chunk c (16 tokens) in a 64-byte LDS row r: rotating the chunk
 // order by bits 2-3 of the row spreads 16 consecutive rows over all 64 banks.
 __device__ __forceinline__ int slot16(int c, int r) { return (c ^ (r >> 2)) & 3; }
+
+// One b-bit code group (4 b bytes) at byte offset voff of a buffer resource; zero past
+// the resource's range.
+template <int BITS>
+__device__ __forceinline__ void buf_group(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* w) {
+  if constexpr (BITS == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    w[0] = x[0];
+    w[1] = x[1];
+  } else if constexpr (BITS == 3) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0);
+    w[0] = x[0];
+    w[1] = x[1];
+    w[2] = x[2];
+  } else {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    w[0] = x[0];
+    w[1] = x[1];
+    w[2] = x[2];
+    w[3] = x[3];
+  }
+}
+
+// Largest |code term| of b-bit codes: |u - 2^(b-1)| <= 2^(b-1) - 1 (symmetric, centred)
+// or u <= 2^b - 1 (asymmetric).
+constexpr int code_max(bool asym, int bits) { return asym ? (1 << bits) - 1 : (1 << (bits - 1)) - 1; }
 
 template <int FMT>
 __device__ __forceinline__ uint32_t buf_meta(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

@@ -35,10 +35,10 @@ using namespace dec;
 constexpr int kStep = 64;           // tokens per wave step (two value tiles)
 constexpr int kWRow = 80;           // bytes per LDS weight row (64 tokens + padding)
 
-template <int NQ, int DPL>
+template <int NQ, int DPL, int BITS>
 struct HeadRaw {
-  uint32_t kw[4][NQ][3];  // token 16 hf + (lane % 16), key group 4 qd + lane / 16
-  uint32_t vw[2][DPL][3]; // value tile tt of the step, dims lane + 64 k
+  uint32_t kw[4][NQ][BITS];  // token 16 hf + (lane % 16), key group 4 qd + lane / 16
+  uint32_t vw[2][DPL][BITS]; // value tile tt of the step, dims lane + 64 k
 };
 
 template <int NQ>
@@ -65,22 +65,25 @@ __device__ __forceinline__ void meta_sz(uint32_t raw, float& s, float& z) {
 
 // One workgroup = one (split, query head, sequence); its four waves take the split's
 // 64-token steps in turn.
-template <int D, int FMT, int BLOCK>
+template <int D, int FMT, int BLOCK, int BITS>
 __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) {
   constexpr int NQ = D / 128;          // 128-dim quads
   constexpr int SEG = BLOCK < 128 ? BLOCK : 128;   // block part inside one quad
   constexpr int BPQ = 128 / SEG;       // segments per quad (1, 2 or 4)
   constexpr int NSEG = D / SEG;
   constexpr int NBLK = D / BLOCK;
-  constexpr int ROWB = 3 * D / 8;
+  constexpr int ROWB = BITS * D / 8;    // bytes per key row
+  constexpr int GB = 4 * BITS;         // bytes per 32-code group
+  constexpr int EXC = 1 << (BITS - 1); // excess of symmetric codes
   constexpr int MB = FMT == kFmtSymF32 ? 4 : 2;
   constexpr bool ASYM = FMT == kFmtAsym;
   constexpr int NBQ = 8;               // 16-dim output blocks per quad
   constexpr int DPL = D / 64;          // value groups per lane and tile
   constexpr int WPLANE = 16 * kWRow;   // bytes of one quad's 16 weight rows
   // fixed-point limits that keep every int32 sum exact (see q_limit)
-  constexpr int QMAX = q_limit(SEG, ASYM ? 7 : 3);
-  using Raw = HeadRaw<NQ, DPL>;
+  constexpr int QMAX = q_limit(SEG, code_max(ASYM, BITS));
+  constexpr int WMAX = w_limit(code_max(ASYM, BITS), static_cast<int>(kWMax));
+  using Raw = HeadRaw<NQ, DPL, BITS>;
   using Meta = HeadMeta<NQ>;
   static_assert(D * 7 + 64 <= 4 * 128 * 64, "prologue fits the value-row region");
 
@@ -188,10 +191,10 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
                         : v4i{0, 0, 0, 0};
       }
       // result rows 4 lq + r = (segment lq, digit r); symmetric codes centred by
-      // -4 sum(digits) over the segment
+      // -2^(b-1) sum(digits) over the segment
       const int sg = qd * BPQ + (bvalid ? lq : 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cinit[qd][r] = (!ASYM && bvalid && r < 3) ? -4 * qds_s[sg][1 + r] : 0;
+      for (int r = 0; r < 4; ++r) cinit[qd][r] = (!ASYM && bvalid && r < 3) ? -EXC * qds_s[sg][1 + r] : 0;
       qsum_f[qd] = bvalid ? static_cast<float>(qds_s[sg][0]) : 0.0f;
     }
   }
@@ -216,9 +219,9 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
       reinterpret_cast<const uint8_t*>(p.k_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
   const __amdgpu_buffer_rsrc_t rvm = make_rsrc(
       reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12,
-                                              static_cast<uint32_t>(ntiles) * D * 12);
-  const uint32_t koff = static_cast<uint32_t>(j * ROWB + 12 * lq);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * GB,
+                                              static_cast<uint32_t>(ntiles) * D * GB);
+  const uint32_t koff = static_cast<uint32_t>(j * ROWB + GB * lq);
   const uint32_t moff = static_cast<uint32_t>(j * NBLK * MB);
   uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
 
@@ -226,19 +229,15 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
     const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 48 * qd), 0, 0);
-      r.kw[hf][qd][0] = w[0]; r.kw[hf][qd][1] = w[1]; r.kw[hf][qd][2] = w[2];
+      buf_group<BITS>(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
     }
   };
   auto load_v = [&](Raw& r, int st, int qd) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * 12;
+      const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * GB;
 #pragma unroll
-      for (int k = 2 * qd; k < 2 * qd + 2; ++k) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, tv + 12 * lane + 768 * k, 0, 0);
-        r.vw[tt][k][0] = w[0]; r.vw[tt][k][1] = w[1]; r.vw[tt][k][2] = w[2];
-      }
+      for (int k = 2 * qd; k < 2 * qd + 2; ++k) buf_group<BITS>(rv, tv + GB * lane + 64 * GB * k, r.vw[tt][k]);
     }
   };
   auto load_m = [&](Meta& m, int st) {
@@ -262,8 +261,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         uint32_t dv[8];
-        const uint32_t* g = r.vw[tt][2 * qd + kk];
-        g32_to_bytes(g[0], g[1], g[2], dv);
+        group_to_bytes<BITS>(r.vw[tt][2 * qd + kk], dv);
         *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt, rrow)) =
             make_uint4(dv[0], dv[1], dv[2], dv[3]);
         *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt + 1, rrow)) =
@@ -290,7 +288,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
         uint32_t dk[8];
-        g32_to_bytes(r.kw[hf][qd][0], r.kw[hf][qd][1], r.kw[hf][qd][2], dk);
+        group_to_bytes<BITS>(r.kw[hf][qd], dk);
         if (qd == NQ - 1) load_k(r, nx, hf);
         const v4i b0 = {static_cast<int>(dk[0]), static_cast<int>(dk[1]), static_cast<int>(dk[2]),
                         static_cast<int>(dk[3])};
@@ -299,7 +297,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
         v4i c = {cinit[qd][0], cinit[qd][1], cinit[qd][2], cinit[qd][3]};
         c = mfma64(qa[qd][0], b0, c);
         c = mfma64(qa[qd][1], b1, c);
-        // sum over block lq of q (u - 4) (symmetric) or q u (asymmetric), exact
+        // sum over block lq of q (u - 2^(b-1)) (symmetric) or q u (asymmetric), exact
         const int comb = combine3<16, 8>(c[0], c[1], c[2]);
         float s, z;
         meta_sz<FMT>(mc.k[hf][qd], s, z);
@@ -359,8 +357,8 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
         wm = fmaxf(wm, w[hf]);
       }
       wm = row16_max(wm);
-      // w winv + 1/2 stays below kWMax + 1 (rcp is within an ulp), so truncation rounds
-      const float winv = wm > 1.0e-30f ? (kWMax - 1.0f) * __builtin_amdgcn_rcpf(wm) : 0.0f;
+      // w winv + 1/2 stays below WMAX + 1 (rcp is within an ulp), so truncation rounds
+      const float winv = wm > 1.0e-30f ? (WMAX - 1.0f) * __builtin_amdgcn_rcpf(wm) : 0.0f;
       int ws = 0;
       uint8_t* wrow = &wq_s[wave][qd][0];
 #pragma unroll
@@ -374,8 +372,9 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
         wrow[(4 * lq + 2) * kWRow + tok] = static_cast<uint8_t>(wi);
       }
       int wcen = 0;
-      if constexpr (!ASYM) wcen = 4 * row16_sum(ws);      // centring of (u - 4)
-      const float wsig = wm * (1.0f / (kWMax - 1.0f));
+      // centring of (u - 2^(b-1)); unsigned: only the centred sum below must fit in int32
+      if constexpr (!ASYM) wcen = static_cast<int>(static_cast<uint32_t>(EXC) * static_cast<uint32_t>(row16_sum(ws)));
+      const float wsig = wm * (1.0f / (WMAX - 1.0f));
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_wave_barrier();
       // ---- P.V: A = weight rows 4 b + d (lane row j), K = the step's 64 tokens
@@ -390,7 +389,8 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
                         static_cast<int>(xb.w)};
         const v4i e = mfma64(a, bv, v4i{0, 0, 0, 0});
         // valid in the lanes whose segment lq holds dims 16 nb .. 16 nb + 15
-        const int ai = combine3<16, 8>(e[0], e[1], e[2]) - wcen;
+        const int ai = static_cast<int>(static_cast<uint32_t>(combine3<16, 8>(e[0], e[1], e[2])) -
+                                        static_cast<uint32_t>(wcen));
         acc[qd][nb] = __builtin_fmaf(wsig, static_cast<float>(ai), acc[qd][nb]);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -465,7 +465,9 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
 
 template <int D, int FMT, int BLOCK>
 void launch_t(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  if (p.bits == 2) hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 2>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  else if (p.bits == 4) hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 4>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  else hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 3>), grid, dim3(256), 0, s, e0, e1, 0, p);
 }
 
 template <int D, int BLOCK>

@@ -16,7 +16,7 @@
 //
 // Block metadata is decoded once per (token, block) into LDS as floats.  With the
 // asymmetric quantiser the zero-point enters directly (s u + z); with the symmetric
-// one the codes are centred (s (u - 4)) through the integer accumulators.
+// one the codes are centred (s (u - 2^(b-1))) through the integer accumulators.
 //
 // Method: "Orthogonally mixed 3-bit KV cache" (idea card), Implementation notes,
 // read path, and Key formulas; "Orthogonal Invariance in Activation Space",
@@ -88,23 +88,25 @@ __device__ __forceinline__ void meta_entry(const uint32_t* w, int bb, float& s, 
   }
 }
 
-template <int NQ, int DPL, int MDW>
+template <int NQ, int DPL, int MDW, int BITS>
 struct StepRaw {
-  uint32_t kw[4][NQ][3];  // token 16 hf + (lane % 16) of the step, key group 4 qd + lane / 16
-  uint32_t vw[2][DPL][3]; // value tile tt of the step, dims lane + 64 k
+  uint32_t kw[4][NQ][BITS];  // token 16 hf + (lane % 16) of the step, key group 4 qd + lane / 16
+  uint32_t vw[2][DPL][BITS]; // value tile tt of the step, dims lane + 64 k
   uint32_t km[MDW];       // key metadata row of token `lane` of the step
   uint32_t vm[MDW];       // value metadata row of token `lane`
 };
 
 // One workgroup = one (split, KV head, sequence) and all G query heads of that KV
 // head; its four waves take the split's 64-token steps in turn.
-template <int D, int FMT, int BLOCK, int G>
+template <int D, int FMT, int BLOCK, int G, int BITS>
 __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams p) {
   constexpr int NQ = D / 128;          // quads of four 32-dim groups (128 dims each)
   constexpr int BPQ = 128 / BLOCK;     // quantisation blocks per quad
   constexpr int NBLK = D / BLOCK;
   static_assert(G * BPQ == 16, "one 16-column (head, block) set per quad");
-  constexpr int ROWB = 3 * D / 8;
+  constexpr int ROWB = BITS * D / 8;    // bytes per key row
+  constexpr int GB = 4 * BITS;         // bytes per 32-code group
+  constexpr int EXC = 1 << (BITS - 1); // excess of symmetric codes
   constexpr int MB = FMT == kFmtSymF32 ? 4 : 2;      // bytes per metadata entry
   constexpr int MDW = NBLK * MB / 4;                 // metadata dwords per token
   constexpr int NBQ = 8;               // 16-dim output blocks per quad
@@ -112,7 +114,8 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   constexpr int UPB = 4 / BPQ;         // useful P.V rows per lane and 16-dim block
   constexpr int NU = G * D / 256;      // query elements per thread in the prologue
   // fixed-point limit that keeps every int32 block sum exact (see q_limit)
-  constexpr int QMAX = q_limit(BLOCK, FMT == kFmtAsym ? 7 : 3);
+  constexpr int QMAX = q_limit(BLOCK, code_max(FMT == kFmtAsym, BITS));
+  constexpr int WMAX = w_limit(code_max(FMT == kFmtAsym, BITS), kW7);
   constexpr int UB0 = 4 * 128 * 64;    // per-wave value rows of one quad
   constexpr int UB1 = 4 * G * D * 4;   // wave partials in the final combine
   constexpr int UB = UB0 > UB1 ? UB0 : UB1;
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   // padded LDS row of one block's metadata floats: consecutive blocks start 16 banks
   // apart, so the four-token reads of a quad's blocks never share a bank
   constexpr int MST = ASYM ? 72 : 80;
-  using Raw = StepRaw<NQ, DPL, MDW>;
+  using Raw = StepRaw<NQ, DPL, MDW, BITS>;
 
   // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
   __shared__ __align__(16) uint8_t u_s[UB];
@@ -244,9 +247,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
                               : v4i{0, 0, 0, 0};
       }
     }
-    // symmetric codes are centred (u - 4) by the accumulator's initial value
+    // symmetric codes are centred (u - 2^(b-1)) by the accumulator's initial value
 #pragma unroll
-    for (int d = 0; d < 3; ++d) cinit[qd][d] = ASYM ? 0 : -4 * qds_s[h][blk][1 + d];
+    for (int d = 0; d < 3; ++d) cinit[qd][d] = ASYM ? 0 : -EXC * qds_s[h][blk][1 + d];
     qsum_f[qd] = static_cast<float>(qds_s[h][blk][0]);
   }
   __syncthreads();   // u_s is reused for value rows below
@@ -272,9 +275,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       reinterpret_cast<const uint8_t*>(p.k_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
   const __amdgpu_buffer_rsrc_t rvm = make_rsrc(
       reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12,
-                                              static_cast<uint32_t>(ntiles) * D * 12);
-  const uint32_t koff = static_cast<uint32_t>(j * ROWB + 12 * lq);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * GB,
+                                              static_cast<uint32_t>(ntiles) * D * GB);
+  const uint32_t koff = static_cast<uint32_t>(j * ROWB + GB * lq);
   uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
   float(*mf)[NBLK][NS][MST] = mf_s[wave];
 
@@ -283,19 +286,17 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
     const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 48 * qd), 0, 0);
-      r.kw[hf][qd][0] = w[0]; r.kw[hf][qd][1] = w[1]; r.kw[hf][qd][2] = w[2];
+      buf_group<BITS>(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
     }
   };
   // value groups of quad qd (dims 128 qd + lane + 64 kk) of both tiles
   auto load_v = [&](Raw& r, int st, int qd) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * 12;
+      const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * GB;
 #pragma unroll
       for (int k = 2 * qd; k < 2 * qd + 2; ++k) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b96(rv, tv + 12 * lane + 768 * k, 0, 0);
-        r.vw[tt][k][0] = w[0]; r.vw[tt][k][1] = w[1]; r.vw[tt][k][2] = w[2];
+        buf_group<BITS>(rv, tv + GB * lane + 64 * GB * k, r.vw[tt][k]);
       }
     }
   };
@@ -307,8 +308,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         uint32_t dv[8];
-        const uint32_t* g = r.vw[tt][2 * qd + kk];
-        g32_to_bytes(g[0], g[1], g[2], dv);
+        group_to_bytes<BITS>(r.vw[tt][2 * qd + kk], dv);
         *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt, rrow)) =
             make_uint4(dv[0], dv[1], dv[2], dv[3]);
         *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt + 1, rrow)) =
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
         uint32_t dk[8];
-        g32_to_bytes(r.kw[hf][qd][0], r.kw[hf][qd][1], r.kw[hf][qd][2], dk);
+        group_to_bytes<BITS>(r.kw[hf][qd], dk);
         if (qd == NQ - 1) load_k(r, nx, hf);
         const v4i a0 = {static_cast<int>(dk[0]), static_cast<int>(dk[1]), static_cast<int>(dk[2]),
                         static_cast<int>(dk[3])};
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
         const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          // sum over the block of q (u - 4) (symmetric) or q u (asymmetric), exact
+          // sum over the block of q (u - 2^(b-1)) (symmetric) or q u (asymmetric), exact
           const int comb = combine3<16, 8>(c[0][rr], c[1][rr], c[2][rr]);
           float v = __builtin_fmaf(sv[rr], static_cast<float>(comb), val[rr]);
           if constexpr (ASYM) v = __builtin_fmaf(zv[rr], qsum_f[qd], v);
@@ -456,8 +456,8 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       }
       wm = fmaxf(wm, swz_xor16(wm));
       wm = fmaxf(wm, xor32f(wm));
-      // w winv + 1/2 stays below kW7 (rcp is within an ulp), so truncation rounds
-      const float winv = wm > 1.0e-30f ? static_cast<float>(kW7 - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
+      // w winv + 1/2 stays below WMAX (rcp is within an ulp), so truncation rounds
+      const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
       int ws = 0;
 #pragma unroll
       for (int hf = 0; hf < 4; ++hf) {
@@ -482,8 +482,10 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
         ws += xor32i(ws);
       }
       if (lq == 0) {
-        wsum_s[wave][qd][j] = 4 * ws;             // centring of (u - 4); zero when asymmetric
-        wsig_s[wave][qd][j] = wm * (1.0f / static_cast<float>(kW7 - 1));
+        // centring of (u - 2^(b-1)) (unused when asymmetric); unsigned: only the centred
+        // sum must fit in int32
+        wsum_s[wave][qd][j] = static_cast<int>(static_cast<uint32_t>(EXC) * static_cast<uint32_t>(ws));
+        wsig_s[wave][qd][j] = wm * (1.0f / static_cast<float>(WMAX - 1));
       }
       if (qd > 0) {
         // the previous quad's P.V is done with the value rows
@@ -522,7 +524,8 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 #pragma unroll
         for (int u = 0; u < UPB; ++u) {
           const int rr = u * BPQ + bqn;             // C row 4 lq + rr = (head, block bqn)
-          const int ai = combine3<14, 7>(e0[rr], e1[rr], e2[rr]) - wcen[bqn][u];
+          const int ai = static_cast<int>(static_cast<uint32_t>(combine3<14, 7>(e0[rr], e1[rr], e2[rr])) -
+                                          static_cast<uint32_t>(wcen[bqn][u]));
           acc[qd][nb][u] = __builtin_fmaf(wsg[bqn][u], static_cast<float>(ai), acc[qd][nb][u]);
         }
       }
@@ -602,7 +605,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 
 template <int D, int FMT, int BLOCK, int G>
 void launch_t(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  hipExtLaunchKernelGGL((decode_grouped_kernel<D, FMT, BLOCK, G>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  if (p.bits == 2) hipExtLaunchKernelGGL((decode_grouped_kernel<D, FMT, BLOCK, G, 2>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  else if (p.bits == 4) hipExtLaunchKernelGGL((decode_grouped_kernel<D, FMT, BLOCK, G, 4>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  else hipExtLaunchKernelGGL((decode_grouped_kernel<D, FMT, BLOCK, G, 3>), grid, dim3(256), 0, s, e0, e1, 0, p);
 }
 
 template <int D, int BLOCK, int G>

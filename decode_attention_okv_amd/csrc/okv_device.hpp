@@ -88,6 +88,29 @@ __device__ __forceinline__ void g32_to_bytes(uint32_t w0, uint32_t w1, uint32_t 
   d[7] = ((w1 >> 6) & 0x03030303u) | ((w2 >> 5) & 0x04040404u);
 }
 
+// b-bit groups (b = 2, 3, 4): 32 codes in 4 b bytes.  Byte j of unpacked word k is
+// code 4k + j in every width.  b = 4: byte j of word k holds code 8k + j in bits 0-3
+// and code 8k + 4 + j in bits 4-7; b = 2: byte j of word k holds codes 16k + 4f + j
+// in bits 2f, 2f + 1 (f = 0..3); b = 3: the 12-byte layout above.
+template <int BITS>
+__device__ __forceinline__ void group_to_bytes(const uint32_t* w, uint32_t d[8]) {
+  static_assert(BITS >= 2 && BITS <= 4, "code width");
+  if constexpr (BITS == 3) {
+    g32_to_bytes(w[0], w[1], w[2], d);
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      d[2 * k] = w[k] & 0x0F0F0F0Fu;
+      d[2 * k + 1] = (w[k] >> 4) & 0x0F0F0F0Fu;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) d[4 * k + f] = (w[k] >> (2 * f)) & 0x03030303u;
+  }
+}
+
 // Same, but the byte-lane words are made opaque to the optimiser so that byte
 // extraction stays a single v_cvt_f32_ubyteN instead of a 3-bit field extract.
 __device__ __forceinline__ void g32_to_bytes_opaque(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t d[8]) {

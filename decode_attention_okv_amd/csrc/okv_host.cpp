@@ -34,7 +34,7 @@ bool hip_ok(hipError_t e) {
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 int meta_entry_bytes(const okv_config& c) {
-  if (c.quant == OKV_QUANT_ASYM3) return 2;           // E4M3 scale + zero-point
+  if (c.quant == OKV_QUANT_ASYM) return 2;           // E4M3 scale + zero-point
   return c.scale_dtype == OKV_DT_F32 ? 4 : 2;
 }
 
@@ -47,10 +47,11 @@ int validate_shape(const okv_config* c) {
   if (!is_pow2(c->head_dim) || c->head_dim % 4 != 0) return OKV_E_INVALID;
   if (c->block < 8 || c->block % 8 != 0 || c->head_dim % c->block != 0) return OKV_E_INVALID;
   if (c->max_tokens < 1 || c->max_tokens % 32 != 0) return OKV_E_INVALID;
-  if (c->quant != OKV_QUANT_SYM3 && c->quant != OKV_QUANT_ASYM3) return OKV_E_INVALID;
+  if (c->quant != OKV_QUANT_SYM && c->quant != OKV_QUANT_ASYM) return OKV_E_INVALID;
   if (c->in_dtype != OKV_DT_F32 && c->in_dtype != OKV_DT_BF16) return OKV_E_INVALID;
   if (c->rotation != OKV_ROT_SIGN && c->rotation != OKV_ROT_SO4) return OKV_E_INVALID;
-  if (c->quant == OKV_QUANT_SYM3) {
+  if (c->bits < 2 || c->bits > 4) return OKV_E_INVALID;
+  if (c->quant == OKV_QUANT_SYM) {
     if (c->scale_dtype != OKV_DT_F32 && c->scale_dtype != OKV_DT_F16) {
       return c->scale_dtype == OKV_DT_E4M3 ? OKV_E_UNSUPPORTED : OKV_E_INVALID;
     }
@@ -67,7 +68,7 @@ int validate_shape(const okv_config* c) {
   // the kernels address one (sequence, KV head) slice of a cache buffer with 32-bit
   // byte offsets (buffer resources), up to 128 tokens past its end: the packed codes
   // of a slice plus that margin stay below 4 GiB
-  if ((static_cast<int64_t>(c->max_tokens) + 128) * (3 * c->head_dim / 8) >= (int64_t{1} << 32)) {
+  if ((static_cast<int64_t>(c->max_tokens) + 128) * (c->bits * c->head_dim / 8) >= (int64_t{1} << 32)) {
     return OKV_E_UNSUPPORTED;
   }
   return OKV_OK;
@@ -76,8 +77,8 @@ int validate_shape(const okv_config* c) {
 void layout_of(const okv_config& c, okv_layout_info* li) {
   const uint64_t units = static_cast<uint64_t>(c.batch) * c.num_kv_heads;
   const uint64_t rows = units * static_cast<uint64_t>(c.max_tokens);
-  li->k_codes_bytes = rows * (3u * c.head_dim / 8);
-  li->v_codes_bytes = rows * (3u * c.head_dim / 8);
+  li->k_codes_bytes = rows * (static_cast<uint64_t>(c.bits) * c.head_dim / 8);
+  li->v_codes_bytes = rows * (static_cast<uint64_t>(c.bits) * c.head_dim / 8);
   li->k_meta_bytes = rows * static_cast<uint64_t>(c.head_dim / c.block) * meta_entry_bytes(c);
   li->v_meta_bytes = li->k_meta_bytes;
 }
@@ -258,6 +259,7 @@ int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* 
   p.scale_dtype = c.scale_dtype;
   p.rotation = c.rotation;
   p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  p.bits = c.bits;
   p.eps = c.eps;
   const int tile1 = (h->len + n_new - 1) / okv::kTile;
   const int ntiles = tile1 - p.tile0 + 1;
@@ -295,6 +297,7 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   p.scale_dtype = c.scale_dtype;
   p.rotation = c.rotation;
   p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  p.bits = c.bits;
   okv::ReduceParams r{};
   r.ws = h->d_ws;
   r.rot = h->d_rot;
@@ -342,6 +345,7 @@ int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void
   p.scale_dtype = c.scale_dtype;
   p.rotation = c.rotation;
   p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  p.bits = c.bits;
   if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
   if (!hip_ok(okv::launch_prefill(p, c.batch, c.head_dim, static_cast<hipStream_t>(hip_stream)))) {
     return OKV_E_HIP;

@@ -17,13 +17,13 @@ enum : int { kRotSign = 0, kRotSo4 = 1 };
 struct WriteParams {
   const void* k;         // [B][n_new][Hkv][D] input type
   const void* v;
-  uint8_t* k_codes;      // [B][Hkv][tcap][3D/8]
-  uint8_t* v_codes;      // [B][Hkv][tcap/32][D][12]
+  uint8_t* k_codes;      // [B][Hkv][tcap][b D/8]
+  uint8_t* v_codes;      // [B][Hkv][tcap/32][D][4 b]
   void* k_meta;          // [B][Hkv][tcap][D/m] (x2 bytes for E4M3 pairs)
   void* v_meta;
   const float* rot;      // device: D signs or (D/4) 4x4 matrices
   int n_new, len, hkv, tcap, ntile_cap, tile0;
-  int block, quant, scale_dtype, rotation, in_bf16;
+  int block, quant, scale_dtype, rotation, in_bf16, bits;
   float eps;
 };
 
@@ -36,7 +36,7 @@ struct DecodeParams {
   const float* rot;
   float* ws;             // [B][Hq][nsplit][D + 2]: acc[D], m (log2 units), l
   int hq, hkv, tcap, ntile_cap, T, nsplit;   // steps interleave over the nsplit splits
-  int block, quant, scale_dtype, rotation, in_bf16;
+  int block, quant, scale_dtype, rotation, in_bf16, bits;
 };
 
 struct ReduceParams {
@@ -55,7 +55,7 @@ struct PrefillParams {
   const float* rot;
   float* out;            // [B][n_q][Hq][D] float32
   int hq, hkv, tcap, ntile_cap, len, n_q, pos0;
-  int block, quant, scale_dtype, rotation, in_bf16;
+  int block, quant, scale_dtype, rotation, in_bf16, bits;
 };
 
 hipError_t launch_write(const WriteParams& p, int ntiles, int batch, int d, hipStream_t s);

@@ -65,15 +65,16 @@ __device__ __forceinline__ void meta_pair(uint32_t raw, float& s, float& z) {
   }
 }
 
-// The 32 codes of a 12-byte group as exact float16 integers: u - 4 for symmetric codes,
+// The 32 codes of a group as exact float16 integers: u - 2^(b-1) for symmetric codes,
 // u for asymmetric ones.  Half 0x64uu is 1024 + u: one v_perm_b32 places two code bytes
 // under 0x64 bytes, then one packed subtraction of 1024 + bias gives the integers.
-template <bool ASYM>
-__device__ __forceinline__ void codes_h16(const uint32_t w0, const uint32_t w1, const uint32_t w2, h8 out[4]) {
+template <bool ASYM, int BITS>
+__device__ __forceinline__ void codes_h16(const uint32_t* w, h8 out[4]) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   uint32_t d[8];
-  g32_to_bytes(w0, w1, w2, d);
-  const h2 bias = {static_cast<_Float16>(ASYM ? 1024.0f : 1028.0f), static_cast<_Float16>(ASYM ? 1024.0f : 1028.0f)};
+  group_to_bytes<BITS>(w, d);
+  constexpr float kBias = ASYM ? 1024.0f : 1024.0f + (1 << (BITS - 1));
+  const h2 bias = {static_cast<_Float16>(kBias), static_cast<_Float16>(kBias)};
   uint32_t hw[16];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -106,13 +107,14 @@ __device__ __forceinline__ H2 split_h16(float x) {
 }
 
 // One workgroup = 64 consecutive query rows of one (sequence, query head).
-template <int D, int FMT, int BLOCK>
+template <int D, int FMT, int BLOCK, int BITS>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   constexpr int NG = D / 32;               // 32-dim groups per key row
   constexpr int NBLK = D / BLOCK;
   constexpr int CPB = BLOCK / 32;          // 32-dim chunks per block
   constexpr int TPB = BLOCK / 16;          // 16-dim output tiles per block
-  constexpr int ROWB = 3 * D / 8;
+  constexpr int ROWB = BITS * D / 8;       // bytes per key row
+  constexpr int GB = 4 * BITS;             // bytes per 32-code group
   constexpr int MB = FMT == kFmtSymF32 ? 4 : 2;
   constexpr bool ASYM = FMT == kFmtAsym;
   constexpr int KROW = D + 8;              // halves per LDS key row (16 bytes of padding; rows 16-byte aligned)
@@ -128,6 +130,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   constexpr int NBW = WD >= BLOCK ? WD / BLOCK : 1;   // value blocks per wave
   constexpr int VGW = WD * 2 / 64;         // (dim, 32-token half) groups per lane
   constexpr int NTW = NT / 4;              // output tiles per wave's dims
+  // significant bits of the scale's hi part: code x hi must be exact in float16 (11 bits)
+  constexpr int CMAX = ASYM ? (1 << BITS) - 1 : (1 << (BITS - 1)) - 1;
+  constexpr int HIB = 11 - (CMAX >= 8 ? 4 : CMAX >= 4 ? 3 : CMAX >= 2 ? 2 : 1);
+  constexpr uint32_t HIMASK = 0xFFFFFFFFu << (24 - HIB);
 
   // u_s: float32 query rows (prologue), then the key codes and the two value planes,
   // then float32 output rows (end)
@@ -244,8 +250,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       reinterpret_cast<const uint8_t*>(p.k_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
   const __amdgpu_buffer_rsrc_t rvm = make_rsrc(
       reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * 12,
-                                              static_cast<uint32_t>(ntiles) * D * 12);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * GB,
+                                              static_cast<uint32_t>(ntiles) * D * GB);
   _Float16* kt = reinterpret_cast<_Float16*>(u_s);                   // [kKT][KROW] key codes
   _Float16* vh = reinterpret_cast<_Float16*>(u_s + KTB);             // [D][VROW] u sf_hi
   _Float16* vl = reinterpret_cast<_Float16*>(u_s + KTB + VTB);       // [D][VROW] u sf_lo
@@ -255,25 +261,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   // ---- raw tile data in registers, loaded one tile ahead: key code groups, the wave's
   // value code groups, and the metadata of the wave's blocks (token = lane)
   constexpr int KGT = (kKT * NG + 255) / 256;         // key groups per thread
-  uint32_t kw[KGT][3], vw[VGW][3], kmr[NBW], vmr[NBW];
+  uint32_t kw[KGT][BITS], vw[VGW][BITS], kmr[NBW], vmr[NBW];
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < KGT; ++i) {
       const int e = tid + 256 * i;
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(
-          rk, static_cast<uint32_t>((t0 + e / NG) * ROWB + 12 * (e % NG)), 0, 0);
-      kw[i][0] = w[0];
-      kw[i][1] = w[1];
-      kw[i][2] = w[2];
+      buf_group<BITS>(rk, static_cast<uint32_t>((t0 + e / NG) * ROWB + GB * (e % NG)), kw[i]);
     }
 #pragma unroll
     for (int i = 0; i < VGW; ++i) {
       const int grp = lane + 64 * i, dim = wave * WD + grp % WD, half = grp / WD;
-      const auto w = __builtin_amdgcn_raw_buffer_load_b96(
-          rv, static_cast<uint32_t>((t0 / kTile + half) * D * 12 + 12 * dim), 0, 0);
-      vw[i][0] = w[0];
-      vw[i][1] = w[1];
-      vw[i][2] = w[2];
+      buf_group<BITS>(rv, static_cast<uint32_t>((t0 / kTile + half) * D * GB + GB * dim), vw[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
@@ -288,7 +286,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     __syncthreads();   // the previous tile (or the query rows) is no longer read
     // ---- scales of the wave's blocks, token = lane.  Value scales are normalised by a
     // power of two f (largest scale of the wave's blocks in [1/2, 1)) and split into
-    // an 8-bit hi part and a float16 lo part, so that code x hi is exact in float16.
+    // a hi part of HIB significant bits and a float16 lo part, so that code x hi is
+    // exact in float16.
     float vsr[NBW];
     float vmax = 0.0f;
 #pragma unroll
@@ -309,7 +308,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
       const float sf = vsr[i] * fnorm;                              // exact (power of two)
-      const float hi = __uint_as_float(__float_as_uint(sf) & 0xFFFF0000u);
+      const float hi = __uint_as_float(__float_as_uint(sf) & HIMASK);
       sfh_s[blk0 + i][lane] = static_cast<_Float16>(hi);
       sfl_s[blk0 + i][lane] = static_cast<_Float16>(sf - hi);
     }
@@ -319,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     for (int i = 0; i < KGT; ++i) {
       const int e = tid + 256 * i;
       h8 hv[4];
-      codes_h16<ASYM>(kw[i][0], kw[i][1], kw[i][2], hv);
+      codes_h16<ASYM, BITS>(kw[i], hv);
       h8* dst = reinterpret_cast<h8*>(kt + (e / NG) * KROW + 32 * (e % NG));
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = hv[k];
@@ -335,7 +334,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       const int grp = lane + 64 * i, dim = wave * WD + grp % WD, half = grp / WD;
       const int blk = dim / BLOCK;
       h8 hv[4];
-      codes_h16<ASYM>(vw[i][0], vw[i][1], vw[i][2], hv);
+      codes_h16<ASYM, BITS>(vw[i], hv);
       const uint4* sh = reinterpret_cast<const uint4*>(&sfh_s[blk][32 * half]);
       const uint4* sl = reinterpret_cast<const uint4*>(&sfl_s[blk][32 * half]);
       uint2* dh = reinterpret_cast<uint2*>(vh + dim * VROW + 32 * half);   // 8-byte aligned rows
@@ -541,7 +540,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 
 template <int D, int FMT, int BLOCK>
 void launch_t(const PrefillParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, FMT, BLOCK>), grid, dim3(256), 0, s, p);
+  if (p.bits == 2) hipLaunchKernelGGL((prefill_kernel<D, FMT, BLOCK, 2>), grid, dim3(256), 0, s, p);
+  else if (p.bits == 4) hipLaunchKernelGGL((prefill_kernel<D, FMT, BLOCK, 4>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((prefill_kernel<D, FMT, BLOCK, 3>), grid, dim3(256), 0, s, p);
 }
 
 template <int D, int BLOCK>

@@ -1,5 +1,5 @@
 // Write path: rotate each new key and value head vector with U, quantise it
-// blockwise to 3-bit codes and pack the codes.
+// blockwise to b-bit codes (b = 2, 3, 4; the pages' method uses 3) and pack the codes.
 //
 // Pages: "Orthogonally mixed 3-bit KV cache", Implementation notes (k1 = U(k),
 // v1 = U(v), one scale per block, signed 3-bit codes, pack, store codes and scales)
@@ -31,7 +31,7 @@ constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
 // one: the approximate quotient is within ~2e-6 of the exact one for |q| <= 8.
 constexpr float kNear = 0.5f - 0x1.0p-17f;
 
-// Four codes (integer-valued floats 0..7) as the bytes of one word.
+// Four codes (integer-valued floats 0..15) as the bytes of one word.
 __device__ __forceinline__ uint32_t bytes_of(const float* u) {
   uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(u[0], 0, 0u);
   w = __builtin_amdgcn_cvt_pk_u8_f32(u[1], 1, w);
@@ -39,27 +39,47 @@ __device__ __forceinline__ uint32_t bytes_of(const float* u) {
   return __builtin_amdgcn_cvt_pk_u8_f32(u[3], 3, w);
 }
 
-// 32 codes as byte lanes (byte b of d[k] = code 4k+b) -> the 12-byte group.
-__device__ __forceinline__ void pack_g32(const uint32_t d[8], uint32_t& w0, uint32_t& w1, uint32_t& w2) {
-  w0 = d[0] | (d[1] << 3) | ((d[6] & 0x03030303u) << 6);
-  w1 = d[2] | (d[3] << 3) | ((d[7] & 0x03030303u) << 6);
-  w2 = d[4] | (d[5] << 3) | ((d[6] & 0x04040404u) << 4) | ((d[7] & 0x04040404u) << 5);
+// 32 codes as byte lanes (byte j of d[k] = code 4k+j) -> the 4b-byte group (the
+// layouts of group_to_bytes).
+template <int BITS>
+__device__ __forceinline__ void pack_group(const uint32_t d[8], uint32_t* w) {
+  if constexpr (BITS == 3) {
+    w[0] = d[0] | (d[1] << 3) | ((d[6] & 0x03030303u) << 6);
+    w[1] = d[2] | (d[3] << 3) | ((d[7] & 0x03030303u) << 6);
+    w[2] = d[4] | (d[5] << 3) | ((d[6] & 0x04040404u) << 4) | ((d[7] & 0x04040404u) << 5);
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = d[2 * k] | (d[2 * k + 1] << 4);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) w[k] = d[4 * k] | (d[4 * k + 1] << 2) | (d[4 * k + 2] << 4) | (d[4 * k + 3] << 6);
+  }
 }
 
-// Bits of a 12-byte group that hold the codes of tokens 0 .. n-1.
-__device__ __forceinline__ void keep_mask(int n, uint32_t& m0, uint32_t& m1, uint32_t& m2) {
-  m0 = m1 = m2 = 0u;
+// Bits of a group that hold the codes of tokens 0 .. n-1.
+template <int BITS>
+__device__ __forceinline__ void keep_mask(int n, uint32_t* m) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int sh = 8 * b;
-    if (b < n) m0 |= 0x07u << sh;
-    if (4 + b < n) m0 |= 0x38u << sh;
-    if (24 + b < n) { m0 |= 0xC0u << sh; m2 |= 0x40u << sh; }
-    if (8 + b < n) m1 |= 0x07u << sh;
-    if (12 + b < n) m1 |= 0x38u << sh;
-    if (28 + b < n) { m1 |= 0xC0u << sh; m2 |= 0x80u << sh; }
-    if (16 + b < n) m2 |= 0x07u << sh;
-    if (20 + b < n) m2 |= 0x38u << sh;
+  for (int k = 0; k < BITS; ++k) m[k] = 0u;
+  if constexpr (BITS == 3) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int sh = 8 * b;
+      if (b < n) m[0] |= 0x07u << sh;
+      if (4 + b < n) m[0] |= 0x38u << sh;
+      if (24 + b < n) { m[0] |= 0xC0u << sh; m[2] |= 0x40u << sh; }
+      if (8 + b < n) m[1] |= 0x07u << sh;
+      if (12 + b < n) m[1] |= 0x38u << sh;
+      if (28 + b < n) { m[1] |= 0xC0u << sh; m[2] |= 0x80u << sh; }
+      if (16 + b < n) m[2] |= 0x07u << sh;
+      if (20 + b < n) m[2] |= 0x38u << sh;
+    }
+  } else {
+    // code i: word i / (32 / b), byte i % 4, field (i % (32 / b)) / 4
+    constexpr int PW = 32 / BITS;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (i < n) m[i / PW] |= ((1u << BITS) - 1u) << (8 * (i % 4) + BITS * ((i % PW) / 4));
   }
 }
 
@@ -69,7 +89,7 @@ __device__ __forceinline__ void keep_mask(int n, uint32_t& m0, uint32_t& m1, uin
 // quantised; key rows are stored straight from the lanes; value codes go through LDS
 // to be regrouped per dimension (old codes of earlier tokens are kept, slots after
 // the new tokens stay zero).
-template <int D, int BLOCK, bool ASYM>
+template <int D, int BLOCK, bool ASYM, int BITS>
 __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   constexpr int EPL = D / 4;                          // elements per lane
   constexpr int GPL = EPL / 32;                       // 32-code groups per lane
@@ -77,6 +97,10 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   constexpr int LPB = BLOCK > EPL ? BLOCK / EPL : 1;  // lanes per block
   constexpr int NBLK = D / BLOCK;
   constexpr int BE = BLOCK < EPL ? BLOCK : EPL;       // a block's elements in one lane
+  constexpr int GB = 4 * BITS;                        // bytes per 32-code group
+  constexpr int EXC = 1 << (BITS - 1);                // excess of symmetric codes
+  constexpr int LEV = EXC - 1;                        // symmetric levels: codes -LEV .. LEV
+  constexpr int TOP = (1 << BITS) - 1;                // largest code
   __shared__ __align__(16) uint8_t vt[kTile][D];      // value codes u of the tile, [slot][dim]
 
   const int tile = p.tile0 + static_cast<int>(blockIdx.x);
@@ -193,7 +217,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         if constexpr (LPB >= 2) amax = fmaxf(amax, dpp<kXor1>(amax));
         if constexpr (LPB >= 4) amax = fmaxf(amax, dpp<kXor2>(amax));
         if (!normalized) amax = amax * cnorm;
-        const float s32 = (amax + p.eps) / 3.0f;
+        const float s32 = (amax + p.eps) / static_cast<float>(LEV);
         float s;
         if (p.scale_dtype == kScaleF16) {
           const _Float16 s16 = static_cast<_Float16>(s32);
@@ -220,7 +244,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
           mn = fminf(mn, dpp<kXor2>(mn));
           mx = fmaxf(mx, dpp<kXor2>(mx));
         }
-        const float s32 = (mx - mn) / 7.0f;
+        const float s32 = (mx - mn) / static_cast<float>(TOP);
         const uint32_t sb = e4m3_encode(s32), zb = e4m3_encode(mn);
         if (meta_lane) reinterpret_cast<uint16_t*>(meta)[row * NBLK + blk] = static_cast<uint16_t>(sb | (zb << 8));
         sblk[bb] = e4m3_decode(sb);
@@ -230,15 +254,17 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
       mblk[bb] = xs * rsblk[bb];      // quotient multiplier: y / s ~ x mblk
     }
 
-    // ---- codes u (0..7) as integer-valued floats, written over x.  Fast rounding:
-    // rint of the approximate quotient (within ~2e-6 of the exact one, |q| <= 8).
+    // ---- codes u (0 .. 2^b - 1) as integer-valued floats, written over x.  Fast
+    // rounding: rint of the approximate quotient (within ~3e-6 of the exact one,
+    // |q| <= 16); the excess 2^(b-1) added before rint is even, so ties keep their
+    // parity.
     // If any value of the wave lies within kNear of a rounding boundary, the wave
     // takes the exact rounding of the exact quotient instead.
     constexpr bool KEEP = EPL <= 32;            // keep the rounded quotients in registers
     float kq[KEEP ? EPL : 1];
     auto quotient = [&](int e) {
       const int bb = e / BE;
-      if constexpr (!ASYM) return __builtin_fmaf(x[e], mblk[bb], 4.0f);   // 4 + y / s
+      if constexpr (!ASYM) return __builtin_fmaf(x[e], mblk[bb], static_cast<float>(EXC));   // 2^(b-1) + y / s
       else return (x[e] - zblk[bb]) * rsblk[bb];                          // RN32(y - z) / s
     };
     float dist = 0.0f;
@@ -254,8 +280,8 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
       for (int e = 0; e < EPL; ++e) {
         const int bb = e / BE;
         const float y = x[e] * xs;
-        x[e] = ASYM ? static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, 7))
-                    : static_cast<float>(rne_code(y, sblk[bb], rsblk[bb], -3, 3) + 4);
+        x[e] = ASYM ? static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, TOP))
+                    : static_cast<float>(rne_code(y, sblk[bb], rsblk[bb], -LEV, LEV) + EXC);
       }
     } else {
 #pragma unroll
@@ -263,13 +289,14 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         float k;
         if constexpr (KEEP) k = kq[e];
         else k = __builtin_rintf(quotient(e));
-        x[e] = ASYM ? __builtin_amdgcn_fmed3f(k, 0.0f, 7.0f) : __builtin_amdgcn_fmed3f(k, 1.0f, 7.0f);
+        x[e] = ASYM ? __builtin_amdgcn_fmed3f(k, 0.0f, static_cast<float>(TOP))
+                    : __builtin_amdgcn_fmed3f(k, 1.0f, static_cast<float>(TOP));
       }
 #pragma unroll
       for (int bb = 0; bb < BPL; ++bb) {
         if (!(sblk[bb] > 0.0f)) {
 #pragma unroll
-          for (int e = 0; e < BE; ++e) x[bb * BE + e] = ASYM ? 0.0f : 4.0f;   // zero scale: code 0
+          for (int e = 0; e < BE; ++e) x[bb * BE + e] = ASYM ? 0.0f : static_cast<float>(EXC);   // zero scale: code 0
         }
       }
     }
@@ -282,12 +309,11 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) d[k] = bytes_of(&u[32 * g + 4 * k]);
       if (tensor == 0) {
-        uint32_t w0, w1, w2;
-        pack_g32(d, w0, w1, w2);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + row * (3 * D / 8) + 12 * (GPL * r + g));
-        dst[0] = w0;
-        dst[1] = w1;
-        dst[2] = w2;
+        uint32_t w[BITS];
+        pack_group<BITS>(d, w);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + row * (BITS * D / 8) + GB * (GPL * r + g));
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) dst[k] = w[k];
       } else {
         reinterpret_cast<uint4*>(vdst)[2 * g] = make_uint4(d[0], d[1], d[2], d[3]);
         reinterpret_cast<uint4*>(vdst)[2 * g + 1] = make_uint4(d[4], d[5], d[6], d[7]);
@@ -301,7 +327,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   __syncthreads();
 
   // ---- value tile: dim j is one group over the tile's 32 tokens
-  uint8_t* vtile = p.v_codes + (unit * p.ntile_cap + tile) * static_cast<size_t>(D) * 12;
+  uint8_t* vtile = p.v_codes + (unit * p.ntile_cap + tile) * static_cast<size_t>(D) * GB;
   for (int j = tid; j < D; j += 256) {
     uint32_t d[8];
 #pragma unroll
@@ -309,27 +335,32 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
       d[k] = static_cast<uint32_t>(vt[4 * k][j]) | (static_cast<uint32_t>(vt[4 * k + 1][j]) << 8) |
              (static_cast<uint32_t>(vt[4 * k + 2][j]) << 16) | (static_cast<uint32_t>(vt[4 * k + 3][j]) << 24);
     }
-    uint32_t w0, w1, w2;
-    pack_g32(d, w0, w1, w2);
-    uint32_t* g = reinterpret_cast<uint32_t*>(vtile + 12 * j);
+    uint32_t w[BITS];
+    pack_group<BITS>(d, w);
+    uint32_t* g = reinterpret_cast<uint32_t*>(vtile + GB * j);
     if (s_lo > 0) {
       // keep the codes of the tile's earlier tokens
-      uint32_t m0, m1, m2;
-      keep_mask(s_lo, m0, m1, m2);
-      w0 |= g[0] & m0;
-      w1 |= g[1] & m1;
-      w2 |= g[2] & m2;
+      uint32_t m[BITS];
+      keep_mask<BITS>(s_lo, m);
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) w[k] |= g[k] & m[k];
     }
-    g[0] = w0;
-    g[1] = w1;
-    g[2] = w2;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) g[k] = w[k];
   }
+}
+
+template <int D, int BLOCK, int BITS>
+void launch_b(const WriteParams& p, dim3 grid, hipStream_t s) {
+  if (p.quant == kQuantAsym) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS>), grid, dim3(256), 0, s, p);
 }
 
 template <int D, int BLOCK>
 void launch_q(const WriteParams& p, dim3 grid, hipStream_t s) {
-  if (p.quant == kQuantAsym) hipLaunchKernelGGL((write_kernel<D, BLOCK, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((write_kernel<D, BLOCK, false>), grid, dim3(256), 0, s, p);
+  if (p.bits == 2) launch_b<D, BLOCK, 2>(p, grid, s);
+  else if (p.bits == 4) launch_b<D, BLOCK, 4>(p, grid, s);
+  else launch_b<D, BLOCK, 3>(p, grid, s);
 }
 
 template <int D>

@@ -10,8 +10,9 @@
  * and 4.3; "Hardware-Fused Fast Hadamard Transforms Enable Lossless 3-Bit KV-Cache
  * Compression at 128K Context Without Perplexity Drift", third paragraph):
  *
- *   write:  k1 = U k, v1 = U v; one scale per block of m values; 3-bit codes;
- *           8 codes in 3 bytes; only codes and scales are stored.
+ *   write:  k1 = U k, v1 = U v; one scale per block of m values; b-bit codes
+ *           (b = 3 in the pages' method; 2 and 4 are built too); 32 codes in 4 b
+ *           bytes; only codes and scales are stored.
  *   decode: q1 = U q; logits from q1 and the dequantised rotated keys, unpacked
  *           and scaled inside the dot product; softmax; weighted sum of the
  *           dequantised rotated values; y = U^T y1.
@@ -20,35 +21,39 @@
  *               transform H_d)  or  U = B H_d  (OKV_ROT_SO4: H_d, then the
  *               block-diagonal SO(4) matrix B = diag(R_1 .. R_{d/4})).
  *
- * Quantisers (per block of m rotated values y):
- *   OKV_QUANT_SYM3:  s = (max|y| + eps) / 3 rounded to float32 then to the scale
- *                    type; c = clip(round_half_even(y / s), -3, 3); stored code
- *                    u = c + 4 (0..7); y_hat = s (u - 4).
- *   OKV_QUANT_ASYM3: s = (max - min) / 7, z = min, both stored as OCP FP8 E4M3
- *                    (round-half-even, saturating at 448); u = clip(round_half_even(
- *                    (y - z) / s), 0, 7); y_hat = s u + z.
+ * Quantisers (per block of m rotated values y; code width b, L = 2^(b-1) - 1):
+ *   OKV_QUANT_SYM:   s = (max|y| + eps) / L rounded to float32 then to the scale
+ *                    type; c = clip(round_half_even(y / s), -L, L); stored code
+ *                    u = c + 2^(b-1) (1 .. 2^b - 1); y_hat = s (u - 2^(b-1)).
+ *                    For b = 3: s = (max|y| + eps) / 3, u = c + 4.
+ *   OKV_QUANT_ASYM:  s = (max - min) / (2^b - 1), z = min, both stored as OCP FP8
+ *                    E4M3 (round-half-even, saturating at 448); u = clip(
+ *                    round_half_even((y - z) / s), 0, 2^b - 1); y_hat = s u + z.
  * Every float32 step of the write path is rounded to nearest-even in a fixed order
  * (butterfly stages of stride 1, 2, 4, ..., d/2, then one multiply by
  * RN32(1/sqrt d); SO(4) rows as ((R0 x0 + R1 x1) + R2 x2) + R3 x3 without fused
  * multiply-adds), so codes and scales are reproducible bit for bit.
  *
- * Packing: 32 codes e[0..31] form a 12-byte group of three little-endian 32-bit
- * words W0 W1 W2.  For k = 0,1,2 and byte b = 0..3: bits 0-2 of byte b of W_k hold
- * e[8k+b] and bits 3-5 hold e[8k+4+b].  Bits 6-7 of byte b of W0 hold the low two
- * bits of e[24+b], bits 6-7 of byte b of W1 the low two bits of e[28+b]; bit 6 of
- * byte b of W2 holds bit 2 of e[24+b] and bit 7 holds bit 2 of e[28+b].
+ * Packing: 32 codes e[0..31] form a group of 4 b bytes, b little-endian 32-bit
+ * words W0 .. W(b-1).
+ *   b = 3: for k = 0,1,2 and byte j = 0..3: bits 0-2 of byte j of W_k hold e[8k+j]
+ *          and bits 3-5 hold e[8k+4+j].  Bits 6-7 of byte j of W0 hold the low two
+ *          bits of e[24+j], bits 6-7 of byte j of W1 the low two bits of e[28+j];
+ *          bit 6 of byte j of W2 holds bit 2 of e[24+j] and bit 7 bit 2 of e[28+j].
+ *   b = 4: byte j of W_k holds e[8k+j] in bits 0-3 and e[8k+4+j] in bits 4-7.
+ *   b = 2: byte j of W_k holds e[16k+4f+j] in bits 2f, 2f+1 (f = 0..3).
  *
  * Cache layouts (caller-owned device buffers, row-major, contiguous):
- *   k_codes  uint8 [batch][num_kv_heads][max_tokens][3*head_dim/8]
- *            token-major rows; dims 32g..32g+31 are group g (bytes 12g..12g+11).
- *   v_codes  uint8 [batch][num_kv_heads][max_tokens/32][head_dim][12]
+ *   k_codes  uint8 [batch][num_kv_heads][max_tokens][b*head_dim/8]
+ *            token-major rows; dims 32g..32g+31 are group g (bytes 4bg .. 4bg+4b-1).
+ *   v_codes  uint8 [batch][num_kv_heads][max_tokens/32][head_dim][4b]
  *            32-token tiles; in tile t, dim j is one group holding the codes of
  *            tokens 32t .. 32t+31 (token 32t+i is code i).  Token slots of a
  *            tile that are not yet written hold code 0.
  *   k_meta, v_meta  [batch][num_kv_heads][max_tokens][head_dim/block] of the
- *            scale type (float32 or IEEE half) for OKV_QUANT_SYM3, and
+ *            scale type (float32 or IEEE half) for OKV_QUANT_SYM, and
  *            uint8 [batch][num_kv_heads][max_tokens][head_dim/block][2] holding the
- *            E4M3 (scale, zero-point) pair for OKV_QUANT_ASYM3.
+ *            E4M3 (scale, zero-point) pair for OKV_QUANT_ASYM.
  *   k, v     [batch][n_new][num_kv_heads][head_dim] in the input type.
  *   q        [batch][num_q_heads][head_dim] in the input type.
  *   out      float32 [batch][num_q_heads][head_dim].
@@ -75,7 +80,7 @@
 extern "C" {
 #endif
 
-#define OKV_ABI_VERSION 1
+#define OKV_ABI_VERSION 2
 
 typedef enum okv_status {
   OKV_OK = 0,
@@ -86,7 +91,12 @@ typedef enum okv_status {
   OKV_E_HIP = 5           /* HIP runtime or launch error */
 } okv_status;
 
-typedef enum okv_quant { OKV_QUANT_SYM3 = 0, OKV_QUANT_ASYM3 = 1 } okv_quant;
+typedef enum okv_quant {
+  OKV_QUANT_SYM = 0,
+  OKV_QUANT_ASYM = 1,
+  OKV_QUANT_SYM3 = OKV_QUANT_SYM,    /* the names of the 3-bit method */
+  OKV_QUANT_ASYM3 = OKV_QUANT_ASYM
+} okv_quant;
 
 typedef enum okv_dtype {
   OKV_DT_F32 = 0,
@@ -104,13 +114,14 @@ typedef struct okv_config {
   int32_t num_kv_heads;  /* >= 1 */
   int32_t head_dim;      /* d: power of two, 4 | d; this build: 128 or 256 */
   int32_t max_tokens;    /* cache capacity per sequence, multiple of 32; this build:
-                          * (max_tokens + 128) * 3 * head_dim / 8 < 2^32 */
+                          * (max_tokens + 128) * bits * head_dim / 8 < 2^32 */
   int32_t block;         /* quantisation block m: m | d, 8 | m; this build: 32 or 64 */
   int32_t quant;         /* okv_quant */
-  int32_t scale_dtype;   /* OKV_DT_F32 or OKV_DT_F16 (SYM3); OKV_DT_E4M3 (ASYM3) */
+  int32_t scale_dtype;   /* OKV_DT_F32 or OKV_DT_F16 (SYM); OKV_DT_E4M3 (ASYM) */
   int32_t in_dtype;      /* OKV_DT_F32 or OKV_DT_BF16: type of k, v and q */
   int32_t rotation;      /* okv_rotation */
-  float eps;             /* SYM3 scale offset, finite, >= 0 (1e-6 is usual) */
+  int32_t bits;          /* code width b: 2, 3 or 4 */
+  float eps;             /* SYM scale offset, finite, >= 0 (1e-6 is usual) */
   /* Host pointer, copied at okv_create.  OKV_ROT_SIGN: head_dim values, each +1
    * or -1 (the diagonal of D).  OKV_ROT_SO4: (head_dim/4) row-major 4x4 float32
    * matrices R_i (rotation matrices: R^T R = I within 1e-3). */

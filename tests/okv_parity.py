@@ -26,7 +26,7 @@ def make_cache(wl, max_tokens, params32):
     return okv.OkvCache(batch=wl.batch, num_q_heads=wl.hq, num_kv_heads=wl.hkv, head_dim=wl.d,
                         max_tokens=max_tokens, block=wl.block, quant=wl.quant,
                         scale_dtype=wl.scale_dtype, in_dtype=wl.in_dtype, rotation=wl.rotation,
-                        eps=wl.eps, rot_params=params32, device="cuda")
+                        eps=wl.eps, rot_params=params32, device="cuda", bits=wl.bits)
 
 
 def params_of(wl):
@@ -45,6 +45,7 @@ def compare_unit(cache, wl, b, h, t, ref):
     Returns a dict of mismatch counts (all must be 0)."""
     ntile = -(-t // 32)
     kc = cache.k_codes[b, h, :t].cpu().numpy()
+    bits = oracle.bits_of(wl)
     vc = cache.v_codes[b, h, :ntile].cpu().numpy()
     km = cache.k_meta[b, h, :t].cpu().numpy()
     vm = cache.v_meta[b, h, :t].cpu().numpy()
@@ -56,8 +57,8 @@ def compare_unit(cache, wl, b, h, t, ref):
     }
     if res["k_codes"] or res["v_codes"]:
         # code-level detail for the report
-        gk = oracle.unpack_rows(kc, wl.d)
-        gv = oracle.unpack_vtiles(vc, t)
+        gk = oracle.unpack_rows(kc, wl.d, bits)
+        gv = oracle.unpack_vtiles(vc, t, bits)
         res["k_code_mismatch"] = int(np.count_nonzero(gk != ref["k_u"]))
         res["v_code_mismatch"] = int(np.count_nonzero(gv != ref["v_u"]))
     return res

@@ -32,6 +32,11 @@ def base(**kw):
     return okv.make_config(**args)
 
 
+def test_largest_slice_is_accepted_4bit():
+    st, lay = okv.okv_layout(base(max_tokens=67108704, bits=4))   # (67108704 + 128) x 64 < 2^32
+    assert st == okv.OKV_OK and lay.k_codes_bytes == 2 * 2 * 67108704 * 64
+
+
 def test_largest_slice_is_accepted():
     st, lay = okv.okv_layout(base(max_tokens=89478336))   # (89478336 + 128) x 48 < 2^32
     assert st == okv.OKV_OK and lay.k_codes_bytes == 2 * 2 * 89478336 * 48   # batch 2 x 2 KV heads
@@ -47,6 +52,12 @@ def test_layout_sizes():
     assert st == okv.OKV_OK and lay.k_meta_bytes == rows * 2 * 2
     st, lay = okv.okv_layout(base(scale_dtype="f32", head_dim=256, rot_params=[1.0] * 256))
     assert st == okv.OKV_OK and lay.k_codes_bytes == rows * 96 and lay.k_meta_bytes == rows * 8 * 4
+    # code widths 2 and 4: b d / 8 bytes per row, 4 b bytes per value group
+    for bits in (2, 4):
+        st, lay = okv.okv_layout(base(bits=bits))
+        assert st == okv.OKV_OK
+        assert lay.k_codes_bytes == rows * bits * 16 and lay.v_codes_bytes == rows * bits * 16
+        assert lay.k_meta_bytes == rows * 4 * 2
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -60,6 +71,9 @@ def test_layout_sizes():
     (dict(quant=5), okv.OKV_E_INVALID),
     (dict(in_dtype="f16"), okv.OKV_E_INVALID),
     (dict(rotation=3), okv.OKV_E_INVALID),
+    (dict(bits=1), okv.OKV_E_INVALID),
+    (dict(bits=5), okv.OKV_E_INVALID),
+    (dict(bits=8), okv.OKV_E_INVALID),
     (dict(eps=-1.0), okv.OKV_E_INVALID),
     (dict(eps=float("nan")), okv.OKV_E_INVALID),
     (dict(scale_dtype="bf16"), okv.OKV_E_INVALID),
@@ -70,6 +84,7 @@ def test_layout_sizes():
     # one (sequence, KV head) slice of packed codes must stay below 4 GiB
     (dict(max_tokens=89478368), okv.OKV_E_UNSUPPORTED),   # 48 B rows: (89478368 + 128) x 48 > 2^32
     (dict(max_tokens=44739264, head_dim=256, rot_params=[1.0] * 256), okv.OKV_E_UNSUPPORTED),
+    (dict(max_tokens=67108736, bits=4), okv.OKV_E_UNSUPPORTED),   # 64 B rows: (67108736 + 128) x 64 >= 2^32
 ])
 def test_rejections(kw, status):
     cfg = base(**{k: v for k, v in kw.items() if k != "abi_version"})

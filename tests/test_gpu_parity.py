@@ -106,6 +106,30 @@ def test_write_decode_reduced(name, kernel):
     run_case(wl, t, chunks, steps=2 if name == "gqa_h32kv8_t32k" else 0, kernel=kernel)
 
 
+# code widths 2 and 4 (b = 3 above): every format, both decode kernels
+WIDTH_CASES = [(n, b, k) for b in (2, 4) for n, k in (
+    ("tiny_d128_t256", "auto"), ("mha_b4h32_t128k", "auto"), ("gqa_h32kv8_t32k", "auto"),
+    ("gqa_h32kv8_t32k", "per_head"), ("gqa_b16h64kv8_t128k_asym", "auto"),
+    ("gqa_b16h64kv8_t128k_asym", "per_head"), ("so4_d256_b32_t8k", "auto"))]
+
+
+@pytest.mark.parametrize("name,bits,kernel", WIDTH_CASES)
+def test_code_widths(name, bits, kernel):
+    over, t, chunks = REDUCED[name]
+    wl = okv_synth.workload(name).with_(bits=bits, **over)
+    run_case(wl, t, chunks, steps=1 if name == "gqa_h32kv8_t32k" else 0, kernel=kernel)
+
+
+@pytest.mark.parametrize("bits,d,block,quant", [(2, 128, 128, "sym"), (4, 256, 128, "asym"),
+                                                (4, 128, 64, "sym"), (2, 256, 256, "asym")])
+def test_code_width_block_sizes(bits, d, block, quant):
+    meta = "e4m3" if quant == "asym" else "f32"
+    rot = "so4" if d == 256 else "sign"
+    wl = okv_synth.workload("so4_d256_b32_t8k").with_(
+        batch=1, hq=2, hkv=2, d=d, block=block, quant=quant, scale_dtype=meta, rotation=rot, bits=bits)
+    run_case(wl, 161, [100, 61], kernel="per_head")
+
+
 @pytest.mark.parametrize("splits", [1, 3, 16])
 def test_split_count_invariance(splits):
     wl = okv_synth.workload("mha_b4h32_t128k").with_(batch=1, hq=4, hkv=4)
@@ -168,11 +192,13 @@ def test_degenerate_inputs(kernel):
     cache.close()
 
 
-@pytest.mark.parametrize("d,block,quant,hq,kernel", [
-    (128, 128, "sym", 1, "per_head"), (256, 256, "sym", 2, "per_head"),
-    (128, 64, "asym", 8, "grouped"), (128, 64, "asym", 1, "per_head"),
+@pytest.mark.parametrize("d,block,quant,hq,kernel,bits", [
+    (128, 128, "sym", 1, "per_head", 3), (256, 256, "sym", 2, "per_head", 3),
+    (128, 64, "asym", 8, "grouped", 3), (128, 64, "asym", 1, "per_head", 3),
+    (128, 128, "sym", 1, "per_head", 4), (128, 64, "asym", 8, "grouped", 4),
+    (128, 64, "asym", 1, "per_head", 4), (128, 32, "sym", 4, "grouped", 4),
 ])
-def test_fixed_point_headroom_aligned(d, block, quant, hq, kernel):
+def test_fixed_point_headroom_aligned(d, block, quant, hq, kernel, bits):
     # worst case of the int32 sums of q times codes: the rotated query is constant
     # (every fixed-point element at its limit) and each rotated key block sits at its
     # top code (symmetric: all +-a; asymmetric: 63 of 64 at +a, one at -a), half of
@@ -182,7 +208,7 @@ def test_fixed_point_headroom_aligned(d, block, quant, hq, kernel):
     meta = "e4m3" if quant == "asym" else "f16"
     wl = okv_synth.workload("gqa_h32kv8_t32k").with_(
         batch=1, hq=hq, hkv=1, d=d, block=block, quant=quant, scale_dtype=meta, rotation="sign",
-        in_dtype="f32")
+        in_dtype="f32", bits=bits)
     p32, u = params_of(wl)
     t = 96
     yk = np.ones((t, d))
@@ -200,7 +226,7 @@ def test_fixed_point_headroom_aligned(d, block, quant, hq, kernel):
     k = torch.from_numpy(kx).reshape(1, t, 1, d).cuda()
     v = torch.from_numpy(vx).reshape(1, t, 1, d).cuda()
     q = torch.from_numpy(qx).reshape(1, hq, d).cuda()
-    say("headroom okv_write/okv_decode_attn", d, block, quant, kernel)
+    say("headroom okv_write/okv_decode_attn", d, block, quant, kernel, "bits", bits)
     cache.write(k, v)
     out = cache.decode_attn(q).cpu().numpy()
     ref = oracle.write_unit(kx, vx, wl, p32)

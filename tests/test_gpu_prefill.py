@@ -58,6 +58,13 @@ CASES = [
     ("gqa_b16h64kv8_t128k_asym", dict(batch=1, hq=16, hkv=2), 190, [123, 67], 67),
     ("so4_d256_b32_t8k", dict(batch=1, hq=4, hkv=1), 160, [160], 160),
     ("so4_d256_b32_t8k", dict(batch=1, hq=4, hkv=1, quant="asym", block=64, scale_dtype="e4m3"), 99, [60, 39], 39),
+    # code widths 2 and 4
+    ("gqa_h32kv8_t32k", dict(hq=8, hkv=2, bits=4), 200, [150, 50], 50),
+    ("gqa_h32kv8_t32k", dict(hq=8, hkv=2, bits=2), 130, [130], 130),
+    ("gqa_b16h64kv8_t128k_asym", dict(batch=1, hq=16, hkv=2, bits=4), 150, [150], 70),
+    ("gqa_b16h64kv8_t128k_asym", dict(batch=1, hq=16, hkv=2, bits=2), 100, [64, 36], 36),
+    ("so4_d256_b32_t8k", dict(batch=1, hq=4, hkv=1, bits=4), 96, [96], 96),
+    ("tiny_d128_t256", dict(bits=2), 256, [256], 256),
 ]
 
 
