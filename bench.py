@@ -11,7 +11,8 @@ Prints one JSON line.  `value` is decode-attention GB/s over the algorithmic byt
 of the packed cache (codes + scales read, q read, output written), timed over
 whole steps.  A second leg times chunked-prefill attention over the packed cache
 (okv_prefill_attn: the last 2,048 positions of a 32,768-token GQA context attend
-causally) and reports it under "prefill_attn".
+causally) and reports it under "prefill_attn"; "code_widths" times the decode kernel
+at 2- and 4-bit codes on the same workload (the pages' method is 3-bit).
 """
 from __future__ import annotations
 
@@ -110,6 +111,50 @@ def prefill_attn_leg(name, rows, reps=5):
     }
 
 
+def width_leg(wl, bits, calls=10):
+    """Decode at code width `bits` on the same workload: write the context, then time
+    `calls` decode calls at full length with HIP events on the attention kernel's own
+    dispatch.  Returns the kernel's average and its algorithmic GB/s."""
+    import numpy as np
+    import torch
+
+    import decode_attention_okv_amd as okv
+    import okv_synth
+    wb = wl.with_(bits=bits)
+    t = wb.tokens
+    p32 = okv_synth.rotation_params(wb, dtype=np.float32)
+    cache = okv.OkvCache(batch=wb.batch, num_q_heads=wb.hq, num_kv_heads=wb.hkv, head_dim=wb.d,
+                         max_tokens=t, block=wb.block, quant=wb.quant, scale_dtype=wb.scale_dtype,
+                         in_dtype=wb.in_dtype, rotation=wb.rotation, eps=wb.eps, rot_params=p32,
+                         device="cuda", bits=bits)
+    step = 16384
+    for pos in range(0, t, step):
+        k, v = okv_synth.kv_tokens(wb, pos, min(step, t - pos), device="cuda")
+        cache.write(k, v)
+    del k, v
+    q = okv_synth.queries(wb, 0, device="cuda")
+    out = torch.empty((wb.batch, wb.hq, wb.d), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        cache.decode_attn(q, out)
+    torch.cuda.synchronize()
+    cache.timing(True)
+    for _ in range(calls):
+        cache.decode_attn(q, out)
+    torch.cuda.synchronize()
+    n, attn_ms, red_ms = cache.timing_read()
+    cache.timing(False)
+    assert n == calls and torch.isfinite(out).all()
+    kern = cache.decode_kernel()
+    cache.close()
+    torch.cuda.empty_cache()
+    byt = sum(algorithmic_decode_bytes(wb, t)[:2])
+    us = 1e3 * attn_ms / calls
+    return {"bits": bits, "decode_kernel": kern, "decode_kernel_us": round(us, 2),
+            "reduce_kernel_us": round(1e3 * red_ms / calls, 2), "bytes_per_call": byt,
+            "achieved_GBs": round(byt / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, target_s=12.0):
     """Time the CPU oracle's decode on (sequence, KV head) units of the workload at
     its full context length (same distributions; values drawn on the host)."""
@@ -159,6 +204,8 @@ def main():
     ap.add_argument("--prefill-workload", default="gqa_h32kv8_t32k",
                     help="workload of the chunked-prefill attention leg ('' to skip)")
     ap.add_argument("--prefill-rows", type=int, default=2048)
+    ap.add_argument("--widths", default="2,4",
+                    help="other code widths to time decode at on the same workload ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -288,6 +335,8 @@ def main():
     cache.close()
     del cache, news, qs, out
     torch.cuda.empty_cache()
+    if args.widths:
+        res["code_widths"] = [width_leg(wl, int(b)) for b in args.widths.split(",")]
     if args.prefill_workload:
         res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows)
     if not args.no_cpu_baseline:
