@@ -12,7 +12,8 @@ of the packed cache (codes + scales read, q read, output written), timed over
 whole steps.  A second leg times chunked-prefill attention over the packed cache
 (okv_prefill_attn: the last 2,048 positions of a 32,768-token GQA context attend
 causally) and reports it under "prefill_attn"; "code_widths" times the decode kernel
-at 2- and 4-bit codes on the same workload (the pages' method is 3-bit).
+at 2- and 4-bit codes on the same workload (the pages' method is 3-bit), and
+"rotations" the unrotated per-token variant and U = B H (SO(4) after the transform).
 """
 from __future__ import annotations
 
@@ -111,27 +112,33 @@ def prefill_attn_leg(name, rows, reps=5):
     }
 
 
-def width_leg(wl, bits, calls=10):
-    """Decode at code width `bits` on the same workload: write the context, then time
-    `calls` decode calls at full length with HIP events on the attention kernel's own
-    dispatch.  Returns the kernel's average and its algorithmic GB/s."""
+def variant_leg(wl, calls=10, **over):
+    """One variant of the workload (another code width, rotation or block): write the
+    context (timed with events around all write calls), then time `calls` decode calls
+    at full length with HIP events on the attention kernel's own dispatch."""
     import numpy as np
     import torch
 
     import decode_attention_okv_amd as okv
     import okv_synth
-    wb = wl.with_(bits=bits)
+    wb = wl.with_(**over)
     t = wb.tokens
     p32 = okv_synth.rotation_params(wb, dtype=np.float32)
     cache = okv.OkvCache(batch=wb.batch, num_q_heads=wb.hq, num_kv_heads=wb.hkv, head_dim=wb.d,
                          max_tokens=t, block=wb.block, quant=wb.quant, scale_dtype=wb.scale_dtype,
                          in_dtype=wb.in_dtype, rotation=wb.rotation, eps=wb.eps, rot_params=p32,
-                         device="cuda", bits=bits)
+                         device="cuda", bits=wb.bits)
     step = 16384
-    for pos in range(0, t, step):
-        k, v = okv_synth.kv_tokens(wb, pos, min(step, t - pos), device="cuda")
+    chunks = [okv_synth.kv_tokens(wb, pos, min(step, t - pos), device="cuda") for pos in range(0, t, step)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k, v in chunks:
         cache.write(k, v)
-    del k, v
+    e1.record()
+    torch.cuda.synchronize()
+    write_ms = e0.elapsed_time(e1)
+    del chunks
     q = okv_synth.queries(wb, 0, device="cuda")
     out = torch.empty((wb.batch, wb.hq, wb.d), dtype=torch.float32, device="cuda")
     for _ in range(3):
@@ -149,10 +156,12 @@ def width_leg(wl, bits, calls=10):
     torch.cuda.empty_cache()
     byt = sum(algorithmic_decode_bytes(wb, t)[:2])
     us = 1e3 * attn_ms / calls
-    return {"bits": bits, "decode_kernel": kern, "decode_kernel_us": round(us, 2),
+    return {**over, "decode_kernel": kern, "decode_kernel_us": round(us, 2),
             "reduce_kernel_us": round(1e3 * red_ms / calls, 2), "bytes_per_call": byt,
             "achieved_GBs": round(byt / (us * 1e-6) / 1e9, 1),
-            "frac_hbm_peak": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "write_ms": round(write_ms, 3),
+            "write_GBs": round(write_bytes_per_position(wb) * t / (write_ms * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(wl, target_s=12.0):
@@ -206,6 +215,8 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=2048)
     ap.add_argument("--widths", default="2,4",
                     help="other code widths to time decode at on the same workload ('' to skip)")
+    ap.add_argument("--rotations", type=int, default=1,
+                    help="also time the unrotated per-token variant and U = B H (0 to skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -336,7 +347,11 @@ def main():
     del cache, news, qs, out
     torch.cuda.empty_cache()
     if args.widths:
-        res["code_widths"] = [width_leg(wl, int(b)) for b in args.widths.split(",")]
+        res["code_widths"] = [variant_leg(wl, bits=int(b)) for b in args.widths.split(",")]
+    if args.rotations:
+        # the unrotated per-token baseline and U = B H (the Hadamard-only variant is the
+        # sign rotation with D = I: same kernels and bytes as the headline)
+        res["rotations"] = [variant_leg(wl, rotation="none", block=wl.d), variant_leg(wl, rotation="so4")]
     if args.prefill_workload:
         res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows)
     if not args.no_cpu_baseline:

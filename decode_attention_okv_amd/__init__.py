@@ -31,7 +31,7 @@ OKV_ABI_VERSION = 2
 OKV_OK, OKV_E_INVALID, OKV_E_ALIGN, OKV_E_CAPACITY, OKV_E_UNSUPPORTED, OKV_E_HIP = range(6)
 QUANT = {"sym": 0, "asym": 1}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
-ROTATION = {"sign": 0, "so4": 1}
+ROTATION = {"sign": 0, "so4": 1, "none": 2}
 DECODE_KERNEL = {"auto": 0, "per_head": 1, "grouped": 2}
 
 EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror",

@@ -120,18 +120,20 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
   // the digit-3 rows of the weight planes stay zero
   for (int e = tid; e < 4 * NQ * WPLANE / 4; e += 256) reinterpret_cast<uint32_t*>(&wq_s[0][0][0])[e] = 0u;
   __syncthreads();
-  lds_fwht<D>(q_s);
+  if (p.rotation != kRotNone) lds_fwht<D>(q_s);   // uniform over the workgroup
   const float cn = rsqrtf(static_cast<float>(D));
   float yq = 0.0f;
   if (tid < D) {
-    if (p.rotation == kRotSo4) {
+    if (p.rotation == kRotNone) {
+      yq = q_s[tid];
+    } else if (p.rotation == kRotSo4) {
       const float* R = p.rot + 16 * (tid >> 2) + 4 * (tid & 3);
       const float* xs = q_s + (tid & ~3);
       yq = R[0] * xs[0] + R[1] * xs[1] + R[2] * xs[2] + R[3] * xs[3];
     } else {
       yq = q_s[tid];
     }
-    yq *= cn;
+    if (p.rotation != kRotNone) yq *= cn;
   }
   float amax_q = wave_max(fabsf(yq));
   if (lane == 0) red_s[wave] = amax_q;

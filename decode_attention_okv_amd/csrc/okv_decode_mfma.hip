@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   }
   if (tid < G) qam_s[tid] = 0u;
   __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
+  for (int hs = 1; hs < D && p.rotation != kRotNone; hs <<= 1) {   // U = I: no transform
     for (int e = tid; e < G * D / 2; e += 256) {
       const int h = e / (D / 2), pi = e % (D / 2);
       const int i = (pi / hs) * 2 * hs + (pi % hs);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
     } else {
       y = q_s[h][jd];
     }
-    yq[u] = y * cn;
+    yq[u] = p.rotation == kRotNone ? y : y * cn;
     const float am = wave_max_fast(fabsf(yq[u]));
     if (lane == 0) atomicMax(&qam_s[h], __float_as_uint(am));
   }

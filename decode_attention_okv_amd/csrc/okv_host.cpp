@@ -49,7 +49,9 @@ int validate_shape(const okv_config* c) {
   if (c->max_tokens < 1 || c->max_tokens % 32 != 0) return OKV_E_INVALID;
   if (c->quant != OKV_QUANT_SYM && c->quant != OKV_QUANT_ASYM) return OKV_E_INVALID;
   if (c->in_dtype != OKV_DT_F32 && c->in_dtype != OKV_DT_BF16) return OKV_E_INVALID;
-  if (c->rotation != OKV_ROT_SIGN && c->rotation != OKV_ROT_SO4) return OKV_E_INVALID;
+  if (c->rotation != OKV_ROT_SIGN && c->rotation != OKV_ROT_SO4 && c->rotation != OKV_ROT_NONE) {
+    return OKV_E_INVALID;
+  }
   if (c->bits < 2 || c->bits > 4) return OKV_E_INVALID;
   if (c->quant == OKV_QUANT_SYM) {
     if (c->scale_dtype != OKV_DT_F32 && c->scale_dtype != OKV_DT_F16) {
@@ -173,20 +175,23 @@ int okv_create(const okv_config* cfg, okv_handle** out) {
   *out = nullptr;
   int st = validate_shape(cfg);
   if (st != OKV_OK) return st;
-  if (cfg->rot_params == nullptr) return OKV_E_INVALID;
+  if (cfg->rot_params == nullptr && cfg->rotation != OKV_ROT_NONE) return OKV_E_INVALID;
   if (!cfg->k_codes || !cfg->v_codes || !cfg->k_meta || !cfg->v_meta) return OKV_E_INVALID;
   if (!aligned16(cfg->k_codes) || !aligned16(cfg->v_codes) || !aligned16(cfg->k_meta) ||
       !aligned16(cfg->v_meta)) {
     return OKV_E_ALIGN;
   }
   const int d = cfg->head_dim;
-  const size_t nrot = cfg->rotation == OKV_ROT_SIGN ? static_cast<size_t>(d) : static_cast<size_t>(4) * d;
-  const float* rp = cfg->rot_params;
+  const size_t nrot = cfg->rotation == OKV_ROT_SO4 ? static_cast<size_t>(4) * d : static_cast<size_t>(d);
+  // no rotation: the device copy holds d ones (never read by the kernels)
+  std::vector<float> ones;
+  if (cfg->rotation == OKV_ROT_NONE) ones.assign(d, 1.0f);
+  const float* rp = cfg->rotation == OKV_ROT_NONE ? ones.data() : cfg->rot_params;
   if (cfg->rotation == OKV_ROT_SIGN) {
     for (int i = 0; i < d; ++i) {
       if (rp[i] != 1.0f && rp[i] != -1.0f) return OKV_E_INVALID;
     }
-  } else {
+  } else if (cfg->rotation == OKV_ROT_SO4) {
     for (int r = 0; r < d / 4; ++r) {
       const float* R = rp + 16 * r;
       for (int a = 0; a < 4; ++a) {

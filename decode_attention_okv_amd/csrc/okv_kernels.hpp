@@ -12,7 +12,7 @@ constexpr int kGroup = 32;  // codes per 12-byte packed group
 
 enum : int { kQuantSym = 0, kQuantAsym = 1 };
 enum : int { kScaleF32 = 0, kScaleF16 = 1, kScaleE4M3 = 3 };
-enum : int { kRotSign = 0, kRotSo4 = 1 };
+enum : int { kRotSign = 0, kRotSo4 = 1, kRotNone = 2 };  // kRotNone: U = I
 
 struct WriteParams {
   const void* k;         // [B][n_new][Hkv][D] input type

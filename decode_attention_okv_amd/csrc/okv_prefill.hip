@@ -160,9 +160,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   const int pos_last = pos_first + nrows - 1;
 
   // ---- query rows: q1 = U q, prescaled by log2(e) / sqrt(D) (base-2 logits); the
-  // transform below is unnormalised, so the prescale is log2(e) / D
+  // transform below is unnormalised, so the prescale is log2(e) / D (U = I: no transform)
   float* qs = reinterpret_cast<float*>(u_s);          // [kQT][D]
-  const float qscale = kLog2e / static_cast<float>(D);
+  const bool rot = p.rotation != kRotNone;            // uniform
+  const float qscale = rot ? kLog2e / static_cast<float>(D) : kLog2e * rsqrtf(static_cast<float>(D));
   for (int e = tid; e < kQT * D; e += 256) {
     const int r = e / D, dim = e % D;
     float x = 0.0f;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     qs[e] = x * qscale;
   }
   __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
+  for (int hs = 1; hs < D && rot; hs <<= 1) {
     for (int e = tid; e < kQT * D / 2; e += 256) {
       const int r = e / (D / 2), pi = e % (D / 2);
       const int i = (pi / hs) * 2 * hs + (pi % hs);
@@ -505,6 +506,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     for (int r = 0; r < 4; ++r) ys[(16 * wave + 4 * lq + r) * D + 16 * nt + j] = acc[nt][r] * inv_l[r];
   __syncthreads();
   // ---- y = U^T y1: B^T then the transform (SO(4)), or the transform then the signs
+  // (U = I: y = y1)
   if (p.rotation == kRotSo4) {
     float t[kQT * D / 256];
 #pragma unroll
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     for (int u = 0; u < kQT * D / 256; ++u) ys[tid + 256 * u] = t[u];
     __syncthreads();
   }
-  for (int hs = 1; hs < D; hs <<= 1) {
+  for (int hs = 1; hs < D && rot; hs <<= 1) {
     for (int e = tid; e < kQT * D / 2; e += 256) {
       const int r = e / (D / 2), pi = e % (D / 2);
       const int i = (pi / hs) * 2 * hs + (pi % hs);
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     }
     __syncthreads();
   }
-  const float cn = rsqrtf(static_cast<float>(D));
+  const float cn = rot ? rsqrtf(static_cast<float>(D)) : 1.0f;
   for (int e = tid; e < nrows * D; e += 256) {
     const int r = e / D, dim = e % D;
     float y = ys[e] * cn;

@@ -80,6 +80,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(const ReduceParams p) {
     }
   }
   __syncthreads();
+  if (p.rotation == kRotNone) {   // U = I: y = y1 (uniform over the workgroup)
+    if (tid < D) p.out[(static_cast<size_t>(b) * p.hq + hq) * D + tid] = y_s[tid];
+    return;
+  }
   lds_fwht<D>(t_s);
   if (tid < D) {
     const int j = tid;

@@ -149,6 +149,8 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         x[4 * i] *= g.x; x[4 * i + 1] *= g.y; x[4 * i + 2] *= g.z; x[4 * i + 3] *= g.w;
       }
     }
+    const bool rotated = p.rotation != kRotNone;   // U = I: y = x (uniform)
+    if (rotated) {
     // butterfly stages of stride 1 .. EPL/2 inside the lane
 #pragma unroll
     for (int hs = 1; hs < EPL; hs <<= 1) {
@@ -173,13 +175,14 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg2, dpp<kXor2>(x[e]), x[e]);
     }
+    }
     const float cnorm = (D == 128) ? __uint_as_float(0x3DB504F3u) : 0.0625f;  // RN32(1/sqrt(D))
     const float sc = ((r ^ (r >> 1)) & 1) ? -cnorm : cnorm;   // sigma * c
     // Symmetric codes with the sign-flip rotation use the unnormalised values: the
     // block maximum of |RN(x c)| is RN(max|x| c) (rounding is monotone), and the
     // code quotient folds c in.  Otherwise y = RN(x c) is formed here.
     const bool normalized = ASYM || p.rotation == kRotSo4;
-    if (normalized) {
+    if (normalized && rotated) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = x[e] * sc;
     }
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         }
       }
     }
-    const float xs = normalized ? 1.0f : sc;    // y = RN(x xs) for every element
+    const float xs = (normalized || !rotated) ? 1.0f : sc;    // y = RN(x xs) for every element
 
     // ---- block statistics, scales and metadata
     const size_t row = unit * p.tcap + pos;
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         for (int e = 0; e < BE; ++e) amax = fmaxf(amax, fabsf(x[bb * BE + e]));
         if constexpr (LPB >= 2) amax = fmaxf(amax, dpp<kXor1>(amax));
         if constexpr (LPB >= 4) amax = fmaxf(amax, dpp<kXor2>(amax));
-        if (!normalized) amax = amax * cnorm;
+        if (!normalized && rotated) amax = amax * cnorm;
         const float s32 = (amax + p.eps) / static_cast<float>(LEV);
         float s;
         if (p.scale_dtype == kScaleF16) {

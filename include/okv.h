@@ -105,7 +105,9 @@ typedef enum okv_dtype {
   OKV_DT_E4M3 = 3
 } okv_dtype;
 
-typedef enum okv_rotation { OKV_ROT_SIGN = 0, OKV_ROT_SO4 = 1 } okv_rotation;
+/* OKV_ROT_NONE: U = I, the unrotated baseline of the ablations (per-token or
+ * per-block 3-bit codes of the raw vectors); rot_params is ignored and may be NULL. */
+typedef enum okv_rotation { OKV_ROT_SIGN = 0, OKV_ROT_SO4 = 1, OKV_ROT_NONE = 2 } okv_rotation;
 
 typedef struct okv_config {
   int32_t abi_version;   /* must be OKV_ABI_VERSION */
@@ -123,7 +125,7 @@ typedef struct okv_config {
   int32_t bits;          /* code width b: 2, 3 or 4 */
   float eps;             /* SYM scale offset, finite, >= 0 (1e-6 is usual) */
   /* Host pointer, copied at okv_create.  OKV_ROT_SIGN: head_dim values, each +1
-   * or -1 (the diagonal of D).  OKV_ROT_SO4: (head_dim/4) row-major 4x4 float32
+   * or -1 (the diagonal of D; all +1 is the Hadamard-only variant).  OKV_ROT_SO4: (head_dim/4) row-major 4x4 float32
    * matrices R_i (rotation matrices: R^T R = I within 1e-3). */
   const float* rot_params;
   /* Caller-owned device buffers (layouts above), 16-byte aligned. */

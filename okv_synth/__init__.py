@@ -57,7 +57,7 @@ class Workload:
     quant: str            # 'sym' | 'asym'
     block: int            # quantisation block m
     scale_dtype: str      # 'f32' | 'f16' | 'e4m3'
-    rotation: str         # 'sign' (U = H_d D) | 'so4' (U = B H_d)
+    rotation: str         # 'sign' (U = H_d D) | 'so4' (U = B H_d) | 'none' (U = I)
     outlier_frac: float
     key_decay: bool
     decode_steps: int     # append-one-then-decode steps after the prefill
@@ -135,6 +135,8 @@ def rotation_params(wl: Workload, seed: int = 0, dtype=np.float64) -> np.ndarray
     R = L(qL) R(conj(qR)) with qL, qR unit quaternions (normalised N(0, I_4); x0 is
     the real part), so R x is the quaternion product qL * x * conj(qR).
     """
+    if wl.rotation == "none":              # U = I: no parameters (d ones, unused)
+        return np.ones(wl.d, dtype=dtype)
     rng = _rng(wl, _S_ROT, seed)
     if wl.rotation == "sign":
         return np.where(rng.random(wl.d) < 0.5, -1.0, 1.0).astype(dtype)

@@ -5,7 +5,7 @@ HIP library.
 
 A "spec" argument is any object with the attributes ``d``, ``block``, ``quant``
 ('sym' | 'asym'), ``scale_dtype`` ('f32' | 'f16' | 'e4m3'), ``eps`` and
-``rotation`` ('sign' | 'so4'), and optionally ``bits`` (the code width b: 2, 3 or
+``rotation`` ('sign' | 'so4' | 'none'), and optionally ``bits`` (the code width b: 2, 3 or
 4; 3 when absent).
 
 Readings of points the pages leave open are marked READING; the list of all of
@@ -22,6 +22,7 @@ __all__ = [
     "G32_BIT_POSITIONS", "group_bit_positions", "pack_g32", "unpack_g32", "pack_rows", "unpack_rows",
     "pack_vtiles", "unpack_vtiles",
     "write_unit", "meta_values", "attend_unit", "attend_exact", "attend_prefill_unit",
+    "gini", "channel_gini", "block_max_stats", "attention_rel_rmse",
 ]
 
 F32 = np.float32
@@ -69,7 +70,11 @@ def rotation_matrix(rotation: str, params, d: int) -> np.ndarray:
     FWHT(D k), i.e. the sign flip first, then the transform.
     'so4':  U = B H_d with B = diag(R_1, ..., R_{d/4}) -- the idea card,
     Mathematical statement and Key formulas.
+    'none': U = I, the unrotated baseline the idea card's Implementation notes
+    compare against (per-token 3-bit KV); params are ignored.
     """
+    if rotation == "none":
+        return np.eye(d)
     h = hadamard(d)
     p = np.asarray(params, dtype=np.float64)
     if rotation == "sign":
@@ -125,8 +130,11 @@ def rotate_f32(x, rotation: str, params32) -> np.ndarray:
     of the output
     y_r = ((R_r0 x_0 + R_r1 x_1) + R_r2 x_2) + R_r3 x_3, every product and sum
     rounded separately (READING: this order, no fused multiply-add).
+    'none': y = x.
     """
     x = np.asarray(x, dtype=F32)
+    if rotation == "none":
+        return x.copy()
     d = x.shape[-1]
     p = np.asarray(params32, dtype=F32)
     if rotation == "sign":
@@ -513,3 +521,58 @@ def attend_prefill_unit(q, positions, k_codes, k_meta, v_codes, v_meta, spec, u_
         q1 = q[i] @ u_mat.T
         out[i] = attend_exact(q1, k_hat[:pos + 1], v_hat[:pos + 1]) @ u_mat
     return out
+
+
+# ---------------------------------------------------------------------------
+# Quality diagnostics of the ablation variants (float64)
+# ---------------------------------------------------------------------------
+
+def gini(x) -> float:
+    """Gini coefficient of the magnitudes |x| (all elements): the mean absolute
+    difference of two draws over twice the mean, sum_ij |a_i - a_j| / (2 n^2 mean a).
+    0 for equal magnitudes, (n - 1) / n for one nonzero among n.  The OIQ report,
+    Section 6.1, measures it on key tensors before and after the transform."""
+    a = np.sort(np.abs(np.asarray(x, dtype=np.float64)).ravel())
+    n = a.size
+    tot = a.sum()
+    if n == 0 or tot == 0.0:
+        return 0.0
+    # sum_ij |a_i - a_j| = 2 sum_i (2 i - n + 1) a_(i) over the ascending order (i from 0)
+    i = np.arange(n, dtype=np.float64)
+    return float(2.0 * np.sum((2.0 * i - n + 1.0) * a) / (2.0 * n * tot))
+
+
+def channel_gini(x) -> float:
+    """Gini coefficient of the per-channel magnitudes of a (T, d) tensor: the RMS of
+    each channel over the T rows.  READING: the OIQ report, Section 6.1, measures "the
+    Gini coefficient of key tensor magnitude distribution" before and after the
+    transform; outlier channels concentrate that distribution and the transform
+    spreads their energy over all channels, so the per-channel magnitudes are taken."""
+    x = np.asarray(x, dtype=np.float64)
+    return gini(np.sqrt(np.mean(x.reshape(-1, x.shape[-1]) ** 2, axis=0)))
+
+
+def block_max_stats(y, block: int) -> dict:
+    """Block maxima of |y| over blocks of `block` values along the last axis: the
+    worst one and the mean one, also relative to the RMS of y (the quantity the
+    scale follows; the idea card's Verification reports the worst block maximum)."""
+    y = np.asarray(y, dtype=np.float64)
+    d = y.shape[-1]
+    bm = np.abs(y.reshape(y.shape[:-1] + (d // block, block))).max(axis=-1)
+    rms = float(np.sqrt(np.mean(y ** 2)))
+    return {"worst": float(bm.max()), "mean": float(bm.mean()),
+            "worst_over_rms": float(bm.max()) / rms if rms > 0 else 0.0,
+            "mean_over_rms": float(bm.mean()) / rms if rms > 0 else 0.0}
+
+
+def attention_rel_rmse(q, k, v, spec, params32) -> float:
+    """||y_cache - y_exact|| / ||y_exact|| (Frobenius over the query heads) of one
+    (sequence, KV head): y_cache is the read path over the packed cache written from
+    k, v (write_unit, attend_unit), y_exact the unquantised attention of the raw
+    vectors (idea card, Key formulas).  q: (G, d), k, v: (T, d) float32."""
+    u = rotation_matrix(spec.rotation, np.asarray(params32, dtype=np.float64), spec.d)
+    ref = write_unit(k, v, spec, params32)
+    t = np.asarray(k).shape[0]
+    y_c = attend_unit(q, ref["k_codes"], ref["k_meta"], ref["v_codes"], ref["v_meta"], t, spec, u)
+    y_e = attend_exact(q, k, v)
+    return float(np.linalg.norm(y_c - y_e) / np.linalg.norm(y_e))

@@ -95,6 +95,14 @@ def test_rejections(kw, status):
     assert st == status and not h.value
 
 
+def test_rotation_none_layout():
+    # U = I: no rotation parameters needed; layout as for any rotation
+    cfg = base(rotation="none", block=128)
+    cfg.rot_params = None
+    st, lay = okv.okv_layout(cfg)
+    assert st == okv.OKV_OK and lay.k_meta_bytes == 2 * 2 * 1024 * 1 * 2
+
+
 def test_create_rejects_bad_pointers_and_params_before_gpu():
     st, h = okv.okv_create(base(k_codes=0))
     assert st == okv.OKV_E_INVALID

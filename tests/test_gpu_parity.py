@@ -130,6 +130,22 @@ def test_code_width_block_sizes(bits, d, block, quant):
     run_case(wl, 161, [100, 61], kernel="per_head")
 
 
+# the unrotated baseline (U = I): per-token blocks (m = d) and blocks of 32/64, both
+# decode kernels
+@pytest.mark.parametrize("name,over,kernel", [
+    ("mha_b4h32_t128k", dict(rotation="none", block=128), "per_head"),
+    ("mha_b4h32_t128k", dict(rotation="none"), "per_head"),
+    ("gqa_h32kv8_t32k", dict(rotation="none"), "auto"),
+    ("gqa_b16h64kv8_t128k_asym", dict(rotation="none"), "auto"),
+    ("so4_d256_b32_t8k", dict(rotation="none", block=256), "per_head"),
+    ("tiny_d128_t256", dict(rotation="none", bits=4), "auto"),
+])
+def test_rotation_none(name, over, kernel):
+    base, t, chunks = REDUCED[name]
+    wl = okv_synth.workload(name).with_(**base).with_(**over)
+    run_case(wl, t, chunks, kernel=kernel)
+
+
 @pytest.mark.parametrize("splits", [1, 3, 16])
 def test_split_count_invariance(splits):
     wl = okv_synth.workload("mha_b4h32_t128k").with_(batch=1, hq=4, hkv=4)

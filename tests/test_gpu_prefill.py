@@ -65,6 +65,9 @@ CASES = [
     ("gqa_b16h64kv8_t128k_asym", dict(batch=1, hq=16, hkv=2, bits=2), 100, [64, 36], 36),
     ("so4_d256_b32_t8k", dict(batch=1, hq=4, hkv=1, bits=4), 96, [96], 96),
     ("tiny_d128_t256", dict(bits=2), 256, [256], 256),
+    # no rotation (U = I)
+    ("gqa_h32kv8_t32k", dict(hq=8, hkv=2, rotation="none"), 140, [100, 40], 40),
+    ("so4_d256_b32_t8k", dict(batch=1, hq=4, hkv=1, rotation="none", block=256), 90, [90], 90),
 ]
 
 
