@@ -38,10 +38,10 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "workload", "channel_model", "rotation_params",
-           "kv_tokens", "queries"]
+           "kv_tokens", "queries", "query_rows", "so4_candidates"]
 
 # stream ids of the SeedSequence
-_S_ROT, _S_KCH, _S_VCH, _S_K, _S_V, _S_Q, _S_STEP, _S_QROWS = range(8)
+_S_ROT, _S_KCH, _S_VCH, _S_K, _S_V, _S_Q, _S_STEP, _S_QROWS, _S_CAL = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -149,6 +149,25 @@ def rotation_params(wl: Workload, seed: int = 0, dtype=np.float64) -> np.ndarray
         qr_conj = qr * np.array([1.0, -1.0, -1.0, -1.0])
         mats.append(_quat_left(ql) @ _quat_right(qr_conj))
     return np.stack(mats).astype(dtype)
+
+
+def so4_candidates(d: int, sweeps: int, n_cand: int, sigma: float = 0.15, seed: int = 0) -> np.ndarray:
+    """Candidate perturbations for the SO(4) calibration search, drawn once:
+    (sweeps, d/4, n_cand, 4, 4) float64 rotations; candidate 0 is the identity, the
+    others are L(a) R(conj(b)) for unit quaternions a, b near 1 (real part 1, imaginary
+    parts sigma * N(0, 1), normalised)."""
+    rng = np.random.default_rng(np.random.SeedSequence([_S_CAL, d, sweeps, n_cand, seed]))
+    out = np.zeros((sweeps, d // 4, n_cand, 4, 4))
+    for s in range(sweeps):
+        for g in range(d // 4):
+            out[s, g, 0] = np.eye(4)
+            for c in range(1, n_cand):
+                a = np.concatenate([[1.0], sigma * rng.standard_normal(3)])
+                b = np.concatenate([[1.0], sigma * rng.standard_normal(3)])
+                a /= np.linalg.norm(a)
+                b /= np.linalg.norm(b)
+                out[s, g, c] = _quat_left(a) @ _quat_right(b * np.array([1.0, -1.0, -1.0, -1.0]))
+    return out
 
 
 def channel_model(wl: Workload, tensor: str, head: int):

@@ -20,4 +20,8 @@ Fast Hadamard Transforms Enable Lossless 3-Bit KV-Cache Compression at 128K
 Context Without Perplexity Drift" (below: "the news item").
 """
 from .okv_ref import *  # noqa: F401,F403
-from .okv_ref import __all__  # noqa: F401
+from .okv_ref import __all__ as _ref_all
+from .okv_calib import *  # noqa: F401,F403
+from .okv_calib import __all__ as _calib_all
+
+__all__ = list(_ref_all) + list(_calib_all)
