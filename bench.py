@@ -13,7 +13,8 @@ whole steps.  A second leg times chunked-prefill attention over the packed cache
 (okv_prefill_attn: the last 2,048 positions of a 32,768-token GQA context attend
 causally) and reports it under "prefill_attn"; "code_widths" times the decode kernel
 at 2- and 4-bit codes on the same workload (the pages' method is 3-bit), and
-"rotations" the unrotated per-token variant and U = B H (SO(4) after the transform).
+"rotations" the unrotated per-token variant and U = B H (SO(4) after the transform);
+"so4_calibration" times the SO(4) calibration search on 16,384 key vectors.
 """
 from __future__ import annotations
 
@@ -164,6 +165,34 @@ def variant_leg(wl, calls=10, **over):
             "write_GBs": round(write_bytes_per_position(wb) * t / (write_ms * 1e-3) / 1e9, 1)}
 
 
+def calibration_leg(name="so4_d256_b32_t8k", n=16384, sweeps=4, n_cand=16):
+    """SO(4) calibration (okv_so4_calibrate) on n key vectors of the workload (KV head 0
+    of sequences 0, 1, ...): wall time of the call, which runs sweeps x d/4 search steps
+    of n_cand candidate evaluations over all n vectors, and the error it removes."""
+    import numpy as np
+    import torch
+
+    import decode_attention_okv_amd as okv
+    import okv_synth
+    wl = okv_synth.workload(name)
+    t = min(n, wl.tokens)
+    k, _ = okv_synth.kv_tokens(wl.with_(batch=-(-n // t)), 0, t, device="cuda")
+    x = k[:, :, 0].float().reshape(-1, wl.d)[:n].contiguous()
+    del k
+    rot0 = okv_synth.rotation_params(wl.with_(rotation="so4"))
+    cand = okv_synth.so4_candidates(wl.d, sweeps, n_cand)
+    okv.so4_calibrate(x, rot0, cand[:1, :, :2], block=wl.block, bits=wl.bits, eps=wl.eps)   # load
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, trace = okv.so4_calibrate(x, rot0, cand, block=wl.block, bits=wl.bits, eps=wl.eps)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0)
+    steps = sweeps * wl.d // 4
+    return {"workload": wl.name, "vectors": n, "head_dim": wl.d, "block": wl.block, "sweeps": sweeps,
+            "candidates": n_cand, "ms": round(ms, 2), "us_per_step": round(1e3 * ms / steps, 1),
+            "error_before": round(float(trace[0]), 1), "error_after": round(float(trace[-1]), 1)}
+
+
 def cpu_baseline(wl, target_s=12.0):
     """Time the CPU oracle's decode on (sequence, KV head) units of the workload at
     its full context length (same distributions; values drawn on the host)."""
@@ -215,6 +244,8 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=2048)
     ap.add_argument("--widths", default="2,4",
                     help="other code widths to time decode at on the same workload ('' to skip)")
+    ap.add_argument("--calibration", type=int, default=1,
+                    help="also time the SO(4) calibration on 16,384 key vectors (0 to skip)")
     ap.add_argument("--rotations", type=int, default=1,
                     help="also time the unrotated per-token variant and U = B H (0 to skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -354,6 +385,8 @@ def main():
         res["rotations"] = [variant_leg(wl, rotation="none", block=wl.d), variant_leg(wl, rotation="so4")]
     if args.prefill_workload:
         res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows)
+    if args.calibration:
+        res["so4_calibration"] = calibration_leg()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

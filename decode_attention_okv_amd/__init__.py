@@ -37,7 +37,8 @@ DECODE_KERNEL = {"auto": 0, "per_head": 1, "grouped": 2}
 EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror",
            "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
            "okv_get_splits", "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel",
-           "okv_get_decode_kernel", "okv_last_hip_error", "okv_prefill_attn")
+           "okv_get_decode_kernel", "okv_last_hip_error", "okv_prefill_attn", "okv_so4_calibrate",
+           "okv_so4_eval")
 
 
 class OkvConfig(ctypes.Structure):
@@ -101,6 +102,8 @@ def _load():
         "okv_timing_read": (i32, [vp, P(i32), P(ctypes.c_double), P(ctypes.c_double)]),
         "okv_set_decode_kernel": (i32, [vp, i32]),
         "okv_get_decode_kernel": (i32, [vp, P(i32)]),
+        "okv_so4_calibrate": (i32, [vp, i32, i32, i32, i32, ctypes.c_float, vp, vp, i32, i32, vp, vp]),
+        "okv_so4_eval": (i32, [vp, i32, i32, i32, i32, ctypes.c_float, vp, vp, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(so, name)
@@ -161,6 +164,60 @@ def okv_decode_attn(h, q_ptr: int, out_ptr: int, stream=None) -> int:
 
 def okv_prefill_attn(h, q_ptr: int, n_q: int, out_ptr: int, stream=None) -> int:
     return lib.okv_prefill_attn(h, ctypes.c_void_p(q_ptr), n_q, ctypes.c_void_p(out_ptr), _stream_ptr(stream))
+
+
+def okv_so4_calibrate(x_ptr: int, n: int, d: int, block: int, bits: int, eps: float, rot_ptr: int,
+                      cand_ptr: int, sweeps: int, n_cand: int, trace_ptr: int, stream=None) -> int:
+    return lib.okv_so4_calibrate(ctypes.c_void_p(x_ptr), n, d, block, bits, eps, ctypes.c_void_p(rot_ptr),
+                                 ctypes.c_void_p(cand_ptr), sweeps, n_cand, ctypes.c_void_p(trace_ptr),
+                                 _stream_ptr(stream))
+
+
+def okv_so4_eval(x_ptr: int, n: int, d: int, block: int, bits: int, eps: float, rot_ptr: int, cand_ptr: int,
+                 n_cand: int, group: int, err_ptr: int, stream=None) -> int:
+    return lib.okv_so4_eval(ctypes.c_void_p(x_ptr), n, d, block, bits, eps, ctypes.c_void_p(rot_ptr),
+                            ctypes.c_void_p(cand_ptr), n_cand, group, ctypes.c_void_p(err_ptr),
+                            _stream_ptr(stream))
+
+
+def _so4_args(x, rot, block, bits):
+    import numpy as np
+    import torch
+    if x.dtype != torch.float32 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x: contiguous float32 [n][head_dim] on the GPU")
+    n, d = x.shape
+    r = np.ascontiguousarray(np.asarray(rot, dtype=np.float32).reshape(d // 4, 4, 4))
+    return n, d, r
+
+
+def so4_calibrate(x, rot, cand, block=32, bits=3, eps=1e-6, stream=None):
+    """Calibrate the SO(4) blocks of U = B H on the calibration vectors x (device
+    float32 [n][d]).  rot: start rotations (d/4, 4, 4); cand: candidate perturbations
+    (sweeps, d/4, n_cand, 4, 4) with the identity first.  Returns (rot, trace) as
+    NumPy arrays: the calibrated rotations and the total error before and after each
+    sweep.  All the work runs in libokv's kernels and its native search loop."""
+    import numpy as np
+    n, d, r = _so4_args(x, rot, block, bits)
+    c = np.ascontiguousarray(np.asarray(cand, dtype=np.float32))
+    sweeps, n_cand = c.shape[0], c.shape[2]
+    if c.shape != (sweeps, d // 4, n_cand, 4, 4):
+        raise ValueError(f"cand: expected (sweeps, {d // 4}, n_cand, 4, 4), got {c.shape}")
+    trace = np.zeros(sweeps + 1, dtype=np.float64)
+    _check(okv_so4_calibrate(x.data_ptr(), n, d, block, bits, eps, r.ctypes.data, c.ctypes.data, sweeps,
+                             n_cand, trace.ctypes.data, stream), "okv_so4_calibrate")
+    return r, trace
+
+
+def so4_eval(x, rot, cand, group, block=32, bits=3, eps=1e-6, stream=None):
+    """Errors of the quantisation block holding `group` for each candidate
+    (n_cand, 4, 4) applied to R_group (one step of the search)."""
+    import numpy as np
+    n, d, r = _so4_args(x, rot, block, bits)
+    c = np.ascontiguousarray(np.asarray(cand, dtype=np.float32).reshape(-1, 4, 4))
+    err = np.zeros(c.shape[0], dtype=np.float64)
+    _check(okv_so4_eval(x.data_ptr(), n, d, block, bits, eps, r.ctypes.data, c.ctypes.data, c.shape[0], group,
+                        err.ctypes.data, stream), "okv_so4_eval")
+    return err
 
 
 def okv_destroy(h) -> int:

@@ -179,6 +179,35 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream);
  * len, else OKV_E_INVALID.  Asynchronous on hip_stream. */
 int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void* hip_stream);
 
+/* SO(4) calibration (the idea card, Implementation notes: start from fixed random
+ * rotations and calibrate them on representative vectors by minimising the
+ * reconstruction MSE after 3-bit quantisation, each SO(4) block a quaternion pair).
+ * Objective: the summed squared error of y = B (H x) after symmetric b-bit
+ * quantisation (s = (max|y| + eps) / (2^(b-1) - 1) per block of `block` dims, codes
+ * round-half-even, clipped) over the n calibration vectors x.  Search: sweeps over the
+ * groups g = 0 .. head_dim/4 - 1 in order; candidate c of (sweep, g) gives
+ * R_g' = cand[s][g][c] R_g, and R_g takes the candidate with the smallest error of
+ * the quantisation block holding g (the first one on ties; candidate 0 should be the
+ * identity, so the error never increases).
+ *   x      device float32 [n][head_dim], 16-byte aligned (e.g. keys in input space)
+ *   rot    host float32 [head_dim/4][4][4] row-major: in the start, out the result
+ *   cand   host float32 [sweeps][head_dim/4][n_cand][4][4]
+ *   trace  host double [sweeps + 1] (NULL allowed): total error before and after each
+ *          sweep
+ * head_dim 128 or 256; 4 | block, block | head_dim; bits 2..4; eps finite >= 0;
+ * 1 <= n_cand <= 1024; n * head_dim < 2^31.  Allocates and frees its own device
+ * workspace; runs on hip_stream and returns when done. */
+int okv_so4_calibrate(const float* x, int32_t n, int32_t head_dim, int32_t block, int32_t bits, float eps,
+                      float* rot, const float* cand, int32_t sweeps, int32_t n_cand, double* trace,
+                      void* hip_stream);
+
+/* One step of that search: err[c] (host double [n_cand]) = error of the quantisation
+ * block holding group `group` with R_group replaced by cand[c] R_group (cand: host
+ * float32 [n_cand][4][4]; rot as above, not changed).  Synchronous. */
+int okv_so4_eval(const float* x, int32_t n, int32_t head_dim, int32_t block, int32_t bits, float eps,
+                 const float* rot, const float* cand, int32_t n_cand, int32_t group, double* err,
+                 void* hip_stream);
+
 /* Free the handle's device memory (not the caller's buffers).  NULL is OK. */
 int okv_destroy(okv_handle* h);
 

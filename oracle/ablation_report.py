@@ -11,6 +11,8 @@ Hadamard-only 3-bit KV and Hadamard-plus-SO(4) 3-bit KV; the OIQ report, Section
   H (D = I)           U = H_d, blocks of 32
   H D                 U = H_d D with random signs, blocks of 32
   B H                 U = B H_d with random SO(4) blocks, blocks of 32
+  B H calibrated      the same blocks after the coordinate search (3 sweeps, 12
+                      candidates) on held-out keys of the same head
 For each: the Gini coefficient of the keys' per-channel magnitudes after U (the
 OIQ report, Section 6.1), the worst block maximum of U k relative to its RMS (the
 idea card's Verification), the relative reconstruction error of the keys, and the
@@ -36,6 +38,7 @@ VARIANTS = [
     ("H (D = I)", dict(rotation="sign", block=32), "ones"),
     ("H D", dict(rotation="sign", block=32), "seeded"),
     ("B H", dict(rotation="so4", block=32), "seeded"),
+    ("B H calibrated", dict(rotation="so4", block=32), "calibrated"),
 ]
 
 
@@ -49,12 +52,25 @@ def unit_data(wl, tokens):
             okv_synth.host_f32(q)[0, :, 0])
 
 
+def calibrated(wl, tokens, sweeps=3, n_cand=12):
+    """SO(4) blocks calibrated by the coordinate search on held-out keys (positions
+    tokens .. 2 tokens - 1 of the same KV head), starting from the seeded rotations."""
+    w = wl.with_(rotation="so4")
+    k, _ = okv_synth.kv_tokens(w, tokens, tokens)
+    x = okv_synth.host_f32(k)[0, :, 0]
+    rot, _, _ = oracle.calibrate_so4(x, okv_synth.rotation_params(w), okv_synth.so4_candidates(w.d, sweeps, n_cand),
+                                     32, w.eps, 3)
+    return rot.astype(np.float32)
+
+
 def row(name, wl, tokens, over, params, bits=3):
     w = wl.with_(rotation=over["rotation"], block=over["block"] or wl.d, bits=bits,
                  scale_dtype="f16", quant="sym")
     k, v, q = unit_data(wl, tokens)
     if params == "ones":
         p32 = np.ones(w.d, np.float32)
+    elif params == "calibrated":
+        p32 = calibrated(wl, tokens)
     else:
         p32 = okv_synth.rotation_params(w, dtype=np.float32)
     y = oracle.rotate_f32(k, w.rotation, p32)

@@ -131,3 +131,29 @@ def test_null_handle_calls():
     assert okv.okv_get_decode_kernel(null)[0] == okv.OKV_E_INVALID
     assert okv.okv_prefill_attn(null, 16, 1, 16, 0) == okv.OKV_E_INVALID
     assert okv.okv_strerror(okv.OKV_E_CAPACITY) == "cache capacity exceeded"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), okv.OKV_E_INVALID),
+    (dict(n=0), okv.OKV_E_INVALID),
+    (dict(x=20), okv.OKV_E_ALIGN),
+    (dict(bits=5), okv.OKV_E_INVALID),
+    (dict(eps=-1.0), okv.OKV_E_INVALID),
+    (dict(block=48), okv.OKV_E_INVALID),          # does not divide 128
+    (dict(d=96, block=32), okv.OKV_E_UNSUPPORTED),
+    (dict(n_cand=0), okv.OKV_E_INVALID),
+    (dict(n_cand=2000), okv.OKV_E_INVALID),
+    (dict(n=1 << 24), okv.OKV_E_UNSUPPORTED),     # n * d >= 2^31
+])
+def test_so4_calibration_rejects_before_gpu(kw, status):
+    import numpy as np
+    a = dict(x=256, n=64, d=128, block=32, bits=3, eps=1e-6, n_cand=4)
+    a.update(kw)
+    rot = np.tile(np.eye(4, dtype=np.float32), (32, 1, 1))
+    cand = np.tile(np.eye(4, dtype=np.float32), (32 * a["n_cand"] if a["n_cand"] > 0 else 1, 1, 1))
+    trace = np.zeros(2)
+    assert okv.okv_so4_calibrate(a["x"], a["n"], a["d"], a["block"], a["bits"], a["eps"], rot.ctypes.data,
+                                 cand.ctypes.data, 1, a["n_cand"], trace.ctypes.data, 0) == status
+    err = np.zeros(max(a["n_cand"], 1))
+    assert okv.okv_so4_eval(a["x"], a["n"], a["d"], a["block"], a["bits"], a["eps"], rot.ctypes.data,
+                            cand.ctypes.data, a["n_cand"], 0, err.ctypes.data, 0) == status
