@@ -24,6 +24,8 @@
 // same reduce kernel as the per-head path.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "okv_decode_common.hpp"
 #include "okv_kernels.hpp"
 
@@ -37,6 +39,18 @@ constexpr int kStep = 64;                 // tokens per wave step (two value til
 constexpr int kW7 = (1 << 21) - 1;        // P.V weights: 21-bit integers per step and row
 
 __device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
+
+// Four consecutive metadata values of LDS as floats (float32 or float16 rows).
+__device__ __forceinline__ void meta4(const float* m, float v[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(m);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+__device__ __forceinline__ void meta4(const _Float16* m, float v[4]) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 x = *reinterpret_cast<const h4*>(m);
+  v[0] = static_cast<float>(x[0]); v[1] = static_cast<float>(x[1]);
+  v[2] = static_cast<float>(x[2]); v[3] = static_cast<float>(x[3]);
+}
 __device__ __forceinline__ int xor16i(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
 __device__ __forceinline__ int xor32i(int v) { return __shfl_xor(v, 32, 64); }
 
@@ -125,12 +139,15 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
   // padded LDS row of one block's metadata floats: consecutive blocks start 16 banks
   // apart, so the four-token reads of a quad's blocks never share a bank
   constexpr int MST = ASYM ? 72 : 80;
+  // E4M3 and fp16 scales are exact in float16: half-size metadata rows (the smaller
+  // LDS footprint lets three workgroups share a CU)
+  using MT = typename std::conditional<FMT == kFmtSymF32, float, _Float16>::type;
   using Raw = StepRaw<NQ, DPL, MDW, BITS>;
 
   // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
   __shared__ __align__(16) uint8_t u_s[UB];
   __shared__ __align__(16) uint8_t wq_s[4][NQ][3][16][kStep];   // weight digits per row
-  __shared__ __align__(16) float mf_s[4][2][NBLK][NS][MST];     // [key/value][block][s, z][token]
+  __shared__ __align__(16) MT mf_s[4][2][NBLK][NS][MST];        // [key/value][block][s, z][token]
   __shared__ int32_t wsum_s[4][NQ][16];
   __shared__ float wsig_s[4][NQ][16];
   __shared__ float alpha_s[4][G];
@@ -279,7 +296,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
                                               static_cast<uint32_t>(ntiles) * D * GB);
   const uint32_t koff = static_cast<uint32_t>(j * ROWB + GB * lq);
   uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
-  float(*mf)[NBLK][NS][MST] = mf_s[wave];
+  MT(*mf)[NBLK][NS][MST] = mf_s[wave];
 
   // key groups of 16-token group hf
   auto load_k = [&](Raw& r, int st, int hf) {
@@ -332,11 +349,11 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
     for (int bb = 0; bb < NBLK; ++bb) {
       float s, z;
       meta_entry<FMT>(r.km, bb, s, z);
-      mf[0][bb][0][lane] = s;
-      if constexpr (ASYM) mf[0][bb][1][lane] = z;
+      mf[0][bb][0][lane] = static_cast<MT>(s);
+      if constexpr (ASYM) mf[0][bb][1][lane] = static_cast<MT>(z);
       meta_entry<FMT>(r.vm, bb, s, z);
-      mf[1][bb][0][lane] = s;
-      if constexpr (ASYM) mf[1][bb][1][lane] = z;
+      mf[1][bb][0][lane] = static_cast<MT>(s);
+      if constexpr (ASYM) mf[1][bb][1][lane] = static_cast<MT>(z);
     }
     load_m(r, nx);
     // values of the first quad go to LDS at once, so their registers refill early
@@ -366,11 +383,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
           c[d] = mfma64(a1, qb[qd][1][d], c[d]);
         }
         const int blk = qd * BPQ + bq;
-        const float4 s4 = *reinterpret_cast<const float4*>(&mf[0][blk][0][16 * hf + 4 * lq]);
-        float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (ASYM) z4 = *reinterpret_cast<const float4*>(&mf[0][blk][NS - 1][16 * hf + 4 * lq]);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-        const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
+        float sv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        meta4(&mf[0][blk][0][16 * hf + 4 * lq], sv);
+        if constexpr (ASYM) meta4(&mf[0][blk][NS - 1][16 * hf + 4 * lq], zv);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           // sum over the block of q (u - 2^(b-1)) (symmetric) or q u (asymmetric), exact
@@ -440,13 +455,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       float wm = 0.0f;
 #pragma unroll
       for (int hf = 0; hf < 4; ++hf) {
-        const float4 s4 = *reinterpret_cast<const float4*>(&mf[1][blk][0][16 * hf + 4 * lq]);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-        float zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (ASYM) {
-          const float4 z4 = *reinterpret_cast<const float4*>(&mf[1][blk][NS - 1][16 * hf + 4 * lq]);
-          zv[0] = z4.x; zv[1] = z4.y; zv[2] = z4.z; zv[3] = z4.w;
-        }
+        float sv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        meta4(&mf[1][blk][0][16 * hf + 4 * lq], sv);
+        if constexpr (ASYM) meta4(&mf[1][blk][NS - 1][16 * hf + 4 * lq], zv);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           w[hf][rr] = pr[hf][rr] * sv[rr];          // zero past T (scale reads as zero)

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -18,6 +19,8 @@ namespace {
 constexpr int kMaxSplits = 256;      // split-K workspace capacity per (sequence, query head)
 constexpr int kTargetGroups = 2048;  // workgroups the automatic split count aims for
 constexpr int kMinSplitSteps = 16;   // automatic splits keep >= 4 64-token steps per wave
+constexpr int kFillGroups = 512;     // workgroups that fill the GPU once (2 per CU)
+constexpr int kLongSplitSteps = 64;  // >= 16 steps per wave once the GPU is filled
 constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -128,6 +131,10 @@ int choose_splits(const okv_handle* h, int32_t T) {
     s = (kTargetGroups + units - 1) / units;
     const int cap = nsteps / kMinSplitSteps;   // short caches: fewer, longer splits
     if (s > cap) s = cap;
+    // once the grid fills the GPU, longer splits beat more rounds of short ones (each
+    // workgroup pays the query prologue and the wave combine once)
+    const int fill = (kFillGroups + units - 1) / units;
+    if (s > fill) s = std::max(fill, std::min(s, nsteps / kLongSplitSteps));
   }
   if (s > kMaxSplits) s = kMaxSplits;
   if (s > nsteps) s = nsteps;
