@@ -117,6 +117,14 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   const bool active = slot >= s_lo && slot < s_hi;    // uniform over the four lanes
   uint32_t* vdst = reinterpret_cast<uint32_t*>(&vt[slot][EPL * r]);
 
+  // SO(4) matrices of B: staged in LDS once per workgroup (every lane reads those of
+  // its dims for each vector)
+  __shared__ __align__(16) float rot_s[4 * D];
+  if (p.rotation == kRotSo4) {                        // uniform over the workgroup
+    for (int e = tid; e < 4 * D; e += 256) rot_s[e] = p.rot[e];
+    __syncthreads();
+  }
+
   if (active) {
     const int pos = tile_base + slot;
     const size_t src = ((static_cast<size_t>(b) * p.n_new + (pos - p.len)) * p.hkv + h) * D + EPL * r;
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
       // y_row = ((R_row0 x0 + R_row1 x1) + R_row2 x2) + R_row3 x3 per 4-block
 #pragma unroll
       for (int q4 = 0; q4 < EPL / 4; ++q4) {
-        const float4* R = reinterpret_cast<const float4*>(p.rot + 16 * (EPL / 4 * r + q4));
+        const float4* R = reinterpret_cast<const float4*>(rot_s + 16 * (EPL / 4 * r + q4));
         const float x0 = x[4 * q4], x1 = x[4 * q4 + 1], x2 = x[4 * q4 + 2], x3 = x[4 * q4 + 3];
 #pragma unroll
         for (int row = 0; row < 4; ++row) {
