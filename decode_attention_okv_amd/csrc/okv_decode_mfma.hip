@@ -9,7 +9,7 @@
 //    (head, block) columns keep the per-block scales separable.  Three instruction
 //    chains take the three balanced digits of the 24-bit fixed-point query and
 //    combine exactly in int32.
-//  * P.V: A = the step's weights p s as 21-bit integers in three 7-bit digits, rows
+//  * P.V: A = the step's weights p s as 21-bit integers in three balanced int8 digits, rows
 //    (head, block); B = value codes of 64 tokens x 16 dims, decoded once per step
 //    into LDS; C = int32 [rows x dims].  Only rows whose block holds the 16 dims are
 //    kept, scaled back to float once per step.
@@ -37,6 +37,12 @@ using namespace dec;
 
 constexpr int kStep = 64;                 // tokens per wave step (two value tiles)
 constexpr int kW7 = (1 << 21) - 1;        // P.V weights: 21-bit integers per step and row
+// 2^23 + 0x8080: for 0 <= x < 2^21, x + kDigitBias lies in [2^23, 2^24), where floats are
+// spaced by 1, so the sum rounds x to the nearest integer wi and its low 23 bits are
+// wi + 0x8080.  Bytes 0-2 of those bits, xor 0x80 each, are the balanced base-256 digits
+// of wi as int8 (wi = 65536 d2 + 256 d1 + d0, d0 and d1 in [-128, 127], 0 <= d2 < 128).
+constexpr float kDigitBias = 8421504.0f;
+constexpr uint32_t kDigitBiasBits = 0x4B008080u;
 
 __device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
 
@@ -60,11 +66,6 @@ __device__ __forceinline__ void digits_q(int q, int& hi, int& mi, int& lo) {
   const int q2 = (q - lo) >> 8;
   mi = ((q2 + 128) & 255) - 128;
   hi = (q2 - mi) >> 8;
-}
-
-// Byte b of the result = the low byte of x_b.
-__device__ __forceinline__ uint32_t bytes4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
-  return (x3 << 24) | (x2 << 16) | (x1 << 8) | x0;   // v_lshl_or_b32 chain
 }
 
 template <int MDW>
@@ -110,10 +111,17 @@ struct StepRaw {
   uint32_t vm[MDW];       // value metadata row of token `lane`
 };
 
+// Resident waves per SIMD the register allocation aims for: three where the LDS
+// footprint lets three workgroups share a CU (d = 128, b <= 3, except the float32 and
+// E4M3 metadata rows of 32-blocks), else no constraint.
+template <int D, int FMT, int BLOCK, int BITS>
+constexpr int kWavesPerEu = (D == 128 && BITS <= 3 && !(BLOCK == 32 && FMT != kFmtSymF16)) ? 3 : 1;
+
 // One workgroup = one (split, KV head, sequence) and all G query heads of that KV
 // head; its four waves take the split's 64-token steps in turn.
 template <int D, int FMT, int BLOCK, int G, int BITS>
-__global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<D, FMT, BLOCK, BITS>)))
+void decode_grouped_kernel(const DecodeParams p) {
   constexpr int NQ = D / 128;          // quads of four 32-dim groups (128 dims each)
   constexpr int BPQ = 128 / BLOCK;     // quantisation blocks per quad
   constexpr int NBLK = D / BLOCK;
@@ -404,6 +412,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       }
     }
     if (tail) {
+      // a real branch: the empty volatile asm keeps the compiler from turning the
+      // masking into selects executed on every step
+      asm volatile("");
 #pragma unroll
       for (int hf = 0; hf < 4; ++hf)
 #pragma unroll
@@ -467,28 +478,33 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
       }
       wm = fmaxf(wm, swz_xor16(wm));
       wm = fmaxf(wm, xor32f(wm));
-      // w winv + 1/2 stays below WMAX (rcp is within an ulp), so truncation rounds
+      // w winv <= WMAX - 1 up to an ulp of rcp; integer wi and its three digits from
+      // one float addition (kDigitBias)
       const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
-      int ws = 0;
+      uint32_t bsum = 0u;   // sum of the float bits: 16 kDigitBiasBits + sum of wi (mod 2^32)
 #pragma unroll
       for (int hf = 0; hf < 4; ++hf) {
-        uint32_t wi[4];
+        uint32_t f[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          wi[rr] = static_cast<uint32_t>(__builtin_fmaf(w[hf][rr], winv, 0.5f));
-          if constexpr (!ASYM) ws += static_cast<int>(wi[rr]);
+          const uint32_t bits = __float_as_uint(__builtin_fmaf(w[hf][rr], winv, kDigitBias));
+          if constexpr (!ASYM) bsum += bits;
+          f[rr] = bits ^ 0x8080u;
         }
+        // byte transpose: digit plane k gets byte k of the four tokens' words
+        const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
+        const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
+        const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
+        const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
         uint8_t* row = &wq_s[wave][qd][0][j][0];
         const int off = 16 * slot16(hf, j) + 4 * lq;
-        *reinterpret_cast<uint32_t*>(row + off) =
-            bytes4(wi[0] >> 14, wi[1] >> 14, wi[2] >> 14, wi[3] >> 14);
-        *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) =
-            bytes4(__builtin_amdgcn_ubfe(wi[0], 7, 7), __builtin_amdgcn_ubfe(wi[1], 7, 7),
-                   __builtin_amdgcn_ubfe(wi[2], 7, 7), __builtin_amdgcn_ubfe(wi[3], 7, 7));
-        *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) =
-            bytes4(wi[0] & 127u, wi[1] & 127u, wi[2] & 127u, wi[3] & 127u);
+        *reinterpret_cast<uint32_t*>(row + off) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);               // d2
+        *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) = __builtin_amdgcn_perm(x23, x01, 0x07060302u);  // d1
+        *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) = __builtin_amdgcn_perm(x23, x01, 0x05040100u);  // d0
       }
+      int ws = 0;
       if constexpr (!ASYM) {
+        ws = static_cast<int>(bsum - 16u * kDigitBiasBits);
         ws += xor16i(ws);
         ws += xor32i(ws);
       }
@@ -535,7 +551,7 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(const DecodeParams 
 #pragma unroll
         for (int u = 0; u < UPB; ++u) {
           const int rr = u * BPQ + bqn;             // C row 4 lq + rr = (head, block bqn)
-          const int ai = static_cast<int>(static_cast<uint32_t>(combine3<14, 7>(e0[rr], e1[rr], e2[rr])) -
+          const int ai = static_cast<int>(static_cast<uint32_t>(combine3<16, 8>(e0[rr], e1[rr], e2[rr])) -
                                           static_cast<uint32_t>(wcen[bqn][u]));
           acc[qd][nb][u] = __builtin_fmaf(wsg[bqn][u], static_cast<float>(ai), acc[qd][nb][u]);
         }
