@@ -39,8 +39,9 @@ constexpr int kStep = 64;                 // tokens per wave step (two value til
 constexpr int kW7 = (1 << 21) - 1;        // P.V weights: 21-bit integers per step and row
 // 2^23 + 0x8080: for 0 <= x < 2^21, x + kDigitBias lies in [2^23, 2^24), where floats are
 // spaced by 1, so the sum rounds x to the nearest integer wi and its low 23 bits are
-// wi + 0x8080.  Bytes 0-2 of those bits, xor 0x80 each, are the balanced base-256 digits
-// of wi as int8 (wi = 65536 d2 + 256 d1 + d0, d0 and d1 in [-128, 127], 0 <= d2 < 128).
+// wi + 0x8080.  Bytes 0 and 1 of those bits with bit 7 flipped, and byte 2 as it is, are
+// the balanced base-256 digits of wi as int8: wi = 65536 d2 + 256 d1 + d0 with d0, d1 in
+// [-128, 127] and 0 <= d2 < 128.
 constexpr float kDigitBias = 8421504.0f;
 constexpr uint32_t kDigitBiasBits = 0x4B008080u;
 
@@ -471,7 +472,9 @@ void decode_grouped_kernel(const DecodeParams p) {
         if constexpr (ASYM) meta4(&mf[1][blk][NS - 1][16 * hf + 4 * lq], zv);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          w[hf][rr] = pr[hf][rr] * sv[rr];          // zero past T (scale reads as zero)
+          // zero past T (scale reads as zero); an fma, so that the float16 scale enters
+          // v_fma_mix_f32 without a separate conversion
+          w[hf][rr] = __builtin_fmaf(pr[hf][rr], sv[rr], 0.0f);
           if constexpr (ASYM) ob[qd] = __builtin_fmaf(pr[hf][rr], zv[rr], ob[qd]);
           wm = fmaxf(wm, w[hf][rr]);
         }
@@ -487,20 +490,22 @@ void decode_grouped_kernel(const DecodeParams p) {
         uint32_t f[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t bits = __float_as_uint(__builtin_fmaf(w[hf][rr], winv, kDigitBias));
-          if constexpr (!ASYM) bsum += bits;
-          f[rr] = bits ^ 0x8080u;
+          f[rr] = __float_as_uint(__builtin_fmaf(w[hf][rr], winv, kDigitBias));
+          if constexpr (!ASYM) bsum += f[rr];
         }
-        // byte transpose: digit plane k gets byte k of the four tokens' words
+        // byte transpose: digit plane k gets byte k of the four tokens' words; planes 0
+        // and 1 then flip bit 7 of every byte (the xor 0x80 of the digit rule)
         const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
         const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
         const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
         const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
         uint8_t* row = &wq_s[wave][qd][0][j][0];
         const int off = 16 * slot16(hf, j) + 4 * lq;
-        *reinterpret_cast<uint32_t*>(row + off) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);               // d2
-        *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) = __builtin_amdgcn_perm(x23, x01, 0x07060302u);  // d1
-        *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) = __builtin_amdgcn_perm(x23, x01, 0x05040100u);  // d0
+        *reinterpret_cast<uint32_t*>(row + off) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);   // d2
+        *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) =
+            __builtin_amdgcn_perm(x23, x01, 0x07060302u) ^ 0x80808080u;                            // d1
+        *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) =
+            __builtin_amdgcn_perm(x23, x01, 0x05040100u) ^ 0x80808080u;                            // d0
       }
       int ws = 0;
       if constexpr (!ASYM) {
