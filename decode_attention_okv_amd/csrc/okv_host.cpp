@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kMaxSplits = 256;      // split-K workspace capacity per (sequence, query head)
 constexpr int kTargetGroups = 2048;  // workgroups the automatic split count aims for
-constexpr int kMinSplitSteps = 16;   // automatic splits keep >= 4 64-token steps per wave
+constexpr int kMinSplitSteps = 8;    // automatic splits keep >= 2 64-token steps per wave
 constexpr int kFillGroups = 512;     // workgroups that fill the GPU once (2 per CU)
 constexpr int kLongSplitSteps = 64;  // >= 16 steps per wave once the GPU is filled
 constexpr int kTimingSlots = 8192;   // event triples kept for okv_timing_read
