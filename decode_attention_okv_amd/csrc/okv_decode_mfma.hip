@@ -3,16 +3,19 @@
 // heads and both contractions run on int8 MFMA (v_mfma_i32_16x16x64_i8).  A wave
 // works on steps of 64 tokens (two 32-token value tiles):
 //
-//  * Q.K: A = key codes of 16 tokens (rows) x 64 dims, B = 16 columns (head h,
-//    block b) holding one int8 digit of q_h restricted to block b (zero elsewhere).
-//    A lane decodes one whole 32-code key group and feeds two instructions; the
-//    (head, block) columns keep the per-block scales separable.  Three instruction
+//  * Q.K as C = Q K^T: A = 16 rows (head h, block b) holding one int8 digit of q_h
+//    restricted to block b (zero elsewhere), B = key codes of 16 tokens (columns) x 64
+//    dims.  A lane decodes one whole 32-code key group and feeds two instructions; the
+//    (head, block) rows keep the per-block scales separable.  Three instruction
 //    chains take the three balanced digits of the 24-bit fixed-point query and
-//    combine exactly in int32.
+//    combine exactly in int32.  Each lane ends with whole logits (every block of its
+//    heads) of four consecutive tokens, so the softmax runs once per (token, head).
 //  * P.V: A = the step's weights p s as 21-bit integers in three balanced int8 digits, rows
 //    (head, block); B = value codes of 64 tokens x 16 dims, decoded once per step
 //    into LDS; C = int32 [rows x dims].  Only rows whose block holds the 16 dims are
-//    kept, scaled back to float once per step.
+//    kept, scaled back to float once per step.  The C rows a lane keeps are the
+//    (head, block) rows whose weights it made, so the per-row scale and the softmax
+//    rescaling stay in registers.
 //
 // Block metadata is decoded once per (token, block) into LDS as floats.  With the
 // asymmetric quantiser the zero-point enters directly (s u + z); with the symmetric
@@ -43,9 +46,16 @@ constexpr int kW7 = (1 << 21) - 1;        // P.V weights: 21-bit integers per st
 // the balanced base-256 digits of wi as int8: wi = 65536 d2 + 256 d1 + d0 with d0, d1 in
 // [-128, 127] and 0 <= d2 < 128.
 constexpr float kDigitBias = 8421504.0f;
-constexpr uint32_t kDigitBiasBits = 0x4B008080u;
 
-__device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+// Maximum over the 16 lanes of each row (quad xor 1 and 2, then row rotations by 4 and 8).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true)));
+  v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true)));
+  v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x124, 0xF, 0xF, true)));
+  return umax(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true)));
+}
 
 // Four consecutive metadata values of LDS as floats (float32 or float16 rows).
 __device__ __forceinline__ void meta4(const float* m, float v[4]) {
@@ -58,8 +68,6 @@ __device__ __forceinline__ void meta4(const _Float16* m, float v[4]) {
   v[0] = static_cast<float>(x[0]); v[1] = static_cast<float>(x[1]);
   v[2] = static_cast<float>(x[2]); v[3] = static_cast<float>(x[3]);
 }
-__device__ __forceinline__ int xor16i(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
-__device__ __forceinline__ int xor32i(int v) { return __shfl_xor(v, 32, 64); }
 
 // Balanced base-256 digits: q = 65536 hi + 256 mi + lo, each in [-128, 127].
 __device__ __forceinline__ void digits_q(int q, int& hi, int& mi, int& lo) {
@@ -134,7 +142,7 @@ void decode_grouped_kernel(const DecodeParams p) {
   constexpr int MDW = NBLK * MB / 4;                 // metadata dwords per token
   constexpr int NBQ = 8;               // 16-dim output blocks per quad
   constexpr int DPL = D / 64;          // value groups per lane and tile
-  constexpr int UPB = 4 / BPQ;         // useful P.V rows per lane and 16-dim block
+  constexpr int HPL = 4 / BPQ;         // heads per lane (C rows 4 lq .. 4 lq + 3)
   constexpr int NU = G * D / 256;      // query elements per thread in the prologue
   // fixed-point limit that keeps every int32 block sum exact (see q_limit)
   constexpr int QMAX = q_limit(BLOCK, code_max(FMT == kFmtAsym, BITS));
@@ -157,13 +165,14 @@ void decode_grouped_kernel(const DecodeParams p) {
   __shared__ __align__(16) uint8_t u_s[UB];
   __shared__ __align__(16) uint8_t wq_s[4][NQ][3][16][kStep];   // weight digits per row
   __shared__ __align__(16) MT mf_s[4][2][NBLK][NS][MST];        // [key/value][block][s, z][token]
-  __shared__ int32_t wsum_s[4][NQ][16];
-  __shared__ float wsig_s[4][NQ][16];
-  __shared__ float alpha_s[4][G];
   __shared__ float cm_s[4][G], cl_s[4][G];
   __shared__ float cob_s[4][G][NBLK];
   __shared__ int32_t qds_s[G][NBLK][4];              // per (head, block): sum q, hi, mid, lo
   __shared__ uint32_t qam_s[G];                      // per head: max |q1| (float bits)
+  // d = 256: the Q operands of both quads wait in LDS (in registers they would leave
+  // room for only one wave per SIMD); the same for every wave, indexed by lane
+  constexpr bool QB_LDS = NQ > 1;
+  __shared__ __align__(16) v4i qbs_s[QB_LDS ? NQ : 1][2][3][64];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y;
@@ -245,52 +254,83 @@ void decode_grouped_kernel(const DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- lane roles
-  const int j = lane & 15;             // QK column (head, block) / P.V row or dim
+  // ---- lane roles.  Q.K runs as C = Q K^T: C rows are the (head, block) pairs, C
+  // columns 16 tokens.  Column j of 16-token group hf is token 4 j + hf of the step, so
+  // lane (j, lq) ends with the logits of four consecutive tokens for C rows 4 lq .. 4 lq
+  // + 3: heads lq HPL .. lq HPL + HPL - 1, every block of the quad.  A head's logit is
+  // then summed over its blocks inside the lane, and the P.V rows the lane accumulates
+  // (C rows 4 lq + u of the same instruction shape) are the same (head, block) pairs.
+  const int j = lane & 15;             // Q row (head, block) / token column / P.V row or dim
   const int lq = lane >> 4;            // k-chunk of the MFMA operands
-  const int h = j / BPQ;               // head of this lane's QK column
-  const int bq = j % BPQ;              // block (within a quad) of this lane's QK column
-  const float am_h = __uint_as_float(qam_s[h]);
-  // base-2 logit per integer unit (kept positive: a zero query has all-zero logits)
-  const float c_logit = fmaxf((am_h / static_cast<float>(QMAX)) * kLog2e * cn, 1.0e-30f);
-  // QK B operands: digit d of q_h at dims 32 (4 qd + lq) + 16 c + e (e < 16), zero
-  // outside the column's block
-  v4i qb[NQ][2][3];
-  int cinit[NQ][3];
-  float qsum_f[NQ];
+  const int hA = j / BPQ;              // head of Q operand row j
+  const int bA = j % BPQ;              // block (within a quad) of Q operand row j
+  // base-2 logit per integer unit of head lq HPL + hl (kept positive: a zero query has
+  // all-zero logits)
+  float c_logit[HPL];
+#pragma unroll
+  for (int hl = 0; hl < HPL; ++hl) {
+    const float am = __uint_as_float(qam_s[lq * HPL + hl]);
+    c_logit[hl] = fmaxf((am / static_cast<float>(QMAX)) * kLog2e * cn, 1.0e-30f);
+  }
+  // Q operand rows: digit d of q_hA at dims 32 (4 qd + lq) + 16 c + e (e < 16), zero
+  // outside the row's block
+  v4i qb[QB_LDS ? 1 : NQ][2][3];
+  v4i cinit[NQ];       // initial value of the low-digit chain per C row
+  float qsum_f[NQ][4];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    const int blk = qd * BPQ + bq;
+    const int blk = qd * BPQ + bA;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int dim0 = 32 * (4 * qd + lq) + 16 * c;
       const bool in_blk = dim0 / BLOCK == blk;       // 16 dims never straddle a block
 #pragma unroll
       for (int d = 0; d < 3; ++d) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&qd_s[d][h][dim0]);
-        qb[qd][c][d] = in_blk ? v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
-                                    static_cast<int>(w.w)}
-                              : v4i{0, 0, 0, 0};
+        const uint4 w = *reinterpret_cast<const uint4*>(&qd_s[d][hA][dim0]);
+        const v4i x = in_blk ? v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                                   static_cast<int>(w.w)}
+                             : v4i{0, 0, 0, 0};
+        if constexpr (QB_LDS) {
+          if (wave == 0) qbs_s[qd][c][d][lane] = x;
+        } else {
+          qb[qd][c][d] = x;
+        }
       }
     }
-    // symmetric codes are centred (u - 2^(b-1)) by the accumulator's initial value
+    // C row 4 lq + rr = (head lq HPL + rr / BPQ, block qd BPQ + rr % BPQ); symmetric codes
+    // are centred (u - 2^(b-1)) by the low-digit chain's initial value -2^(b-1) sum(q)
+    // (the digit combination wraps in int32; only the centred total must fit)
 #pragma unroll
-    for (int d = 0; d < 3; ++d) cinit[qd][d] = ASYM ? 0 : -EXC * qds_s[h][blk][1 + d];
-    qsum_f[qd] = static_cast<float>(qds_s[h][blk][0]);
+    for (int rr = 0; rr < 4; ++rr) {
+      const int hr = lq * HPL + rr / BPQ, br = qd * BPQ + rr % BPQ;
+      cinit[qd][rr] = ASYM ? 0 : static_cast<int>(static_cast<uint32_t>(-EXC) * static_cast<uint32_t>(qds_s[hr][br][0]));
+      qsum_f[qd][rr] = static_cast<float>(qds_s[hr][br][0]);
+    }
   }
   __syncthreads();   // u_s is reused for value rows below
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  float ob[NQ];
+  float m_run[HPL], l_run[HPL];
 #pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) ob[qd] = 0.0f;
-  float acc[NQ][NBQ][UPB];
+  for (int hl = 0; hl < HPL; ++hl) {
+    m_run[hl] = -INFINITY;
+    l_run[hl] = 0.0f;
+  }
+  float ob[NQ][4];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) ob[qd][rr] = 0.0f;
+  float acc[NQ][NBQ][HPL];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
-      for (int u = 0; u < UPB; ++u) acc[qd][nb][u] = 0.0f;
+      for (int u = 0; u < HPL; ++u) acc[qd][nb][u] = 0.0f;
+  // P.V centring of symmetric codes: the byte -2^(b-1) in every lane of a B operand
+  // (a product with it gives -2^(b-1) times each weight row's sum)
+  const int exc_b = static_cast<int>(0x01010101u * static_cast<uint32_t>((256 - EXC) & 255));
+  const v4i excv = {exc_b, exc_b, exc_b, exc_b};
 
   const int T = p.T;
   const int ntiles = (T + kTile - 1) / kTile;
@@ -303,16 +343,16 @@ void decode_grouped_kernel(const DecodeParams p) {
       reinterpret_cast<const uint8_t*>(p.v_meta) + unit * p.tcap * NBLK * MB, static_cast<uint32_t>(T) * NBLK * MB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * GB,
                                               static_cast<uint32_t>(ntiles) * D * GB);
-  const uint32_t koff = static_cast<uint32_t>(j * ROWB + GB * lq);
+  const uint32_t koff = static_cast<uint32_t>(4 * j * ROWB + GB * lq);
   uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
   MT(*mf)[NBLK][NS][MST] = mf_s[wave];
 
-  // key groups of 16-token group hf
+  // key groups of token 4 j + hf of the step (one per 16-token group hf)
   auto load_k = [&](Raw& r, int st, int hf) {
     const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      buf_group<BITS>(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
+      buf_group<BITS>(rk, tok0 * ROWB + koff + (hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
     }
   };
   // value groups of quad qd (dims 128 qd + lane + 64 kk) of both tiles
@@ -370,13 +410,31 @@ void decode_grouped_kernel(const DecodeParams p) {
     load_v(r, nx, 0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
-    // ---- logits (integer units of c_logit): lane holds head h, tokens 16 hf + 4 lq + rr
-    float L[4][4];
+    // ---- logits (integer units of c_logit[hl]): head lq HPL + hl, token 4 j + hf
+    float L[HPL][4];
 #pragma unroll
-    for (int hf = 0; hf < 4; ++hf) {
-      float val[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int hl = 0; hl < HPL; ++hl)
 #pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
+      for (int hf = 0; hf < 4; ++hf) L[hl][hf] = 0.0f;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      v4i qq[2][3];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          if constexpr (QB_LDS) qq[c][d] = qbs_s[qd][c][d][lane];
+          else qq[c][d] = qb[qd][c][d];
+        }
+      // key scales (and zero-points) of the lane's four tokens, every block of the quad
+      float sk[BPQ][4], zk[BPQ][4];
+#pragma unroll
+      for (int bq = 0; bq < BPQ; ++bq) {
+        meta4(&mf[0][qd * BPQ + bq][0][4 * j], sk[bq]);
+        if constexpr (ASYM) meta4(&mf[0][qd * BPQ + bq][NS - 1][4 * j], zk[bq]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 4; ++hf) {
         uint32_t dk[8];
         group_to_bytes<BITS>(r.kw[hf][qd], dk);
         if (qd == NQ - 1) load_k(r, nx, hf);
@@ -387,29 +445,18 @@ void decode_grouped_kernel(const DecodeParams p) {
         v4i c[3];
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
-          c[d] = v4i{cinit[qd][d], cinit[qd][d], cinit[qd][d], cinit[qd][d]};
-          c[d] = mfma64(a0, qb[qd][0][d], c[d]);
-          c[d] = mfma64(a1, qb[qd][1][d], c[d]);
+          c[d] = mfma64(qq[0][d], a0, d == 2 ? cinit[qd] : v4i{0, 0, 0, 0});
+          c[d] = mfma64(qq[1][d], a1, c[d]);
         }
-        const int blk = qd * BPQ + bq;
-        float sv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        meta4(&mf[0][blk][0][16 * hf + 4 * lq], sv);
-        if constexpr (ASYM) meta4(&mf[0][blk][NS - 1][16 * hf + 4 * lq], zv);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
+          const int hl = rr / BPQ, bq = rr % BPQ;
           // sum over the block of q (u - 2^(b-1)) (symmetric) or q u (asymmetric), exact
           const int comb = combine3<16, 8>(c[0][rr], c[1][rr], c[2][rr]);
-          float v = __builtin_fmaf(sv[rr], static_cast<float>(comb), val[rr]);
-          if constexpr (ASYM) v = __builtin_fmaf(zv[rr], qsum_f[qd], v);
-          val[rr] = v;
+          float v = __builtin_fmaf(sk[bq][hf], static_cast<float>(comb), L[hl][hf]);
+          if constexpr (ASYM) v = __builtin_fmaf(zk[bq][hf], qsum_f[qd][rr], v);
+          L[hl][hf] = v;
         }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float v = val[rr];
-        v += dpp_xor1(v);                 // sum over the head's blocks (adjacent columns)
-        if constexpr (BPQ == 4) v += dpp_xor2(v);
-        L[hf][rr] = v;
       }
     }
     if (tail) {
@@ -417,107 +464,91 @@ void decode_grouped_kernel(const DecodeParams p) {
       // masking into selects executed on every step
       asm volatile("");
 #pragma unroll
-      for (int hf = 0; hf < 4; ++hf)
+      for (int hl = 0; hl < HPL; ++hl)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (base + 16 * hf + 4 * lq + rr >= T) L[hf][rr] = -INFINITY;
+        for (int hf = 0; hf < 4; ++hf)
+          if (base + 4 * j + hf >= T) L[hl][hf] = -INFINITY;
     }
     // ---- online softmax per head (base 2), lazy maximum
-    float tmax = L[0][0];
+    float tm[HPL];
+    bool up = false;
 #pragma unroll
-    for (int hf = 0; hf < 4; ++hf)
+    for (int hl = 0; hl < HPL; ++hl) {
+      float t = fmaxf(fmaxf(L[hl][0], L[hl][1]), fmaxf(L[hl][2], L[hl][3]));
+      t = row16_max(t) * c_logit[hl];      // finite: every step holds a valid token
+      tm[hl] = t;
+      up = up || t > m_run[hl] + 8.0f;
+    }
+    if (__any(up)) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) tmax = fmaxf(tmax, L[hf][rr]);
-    tmax = fmaxf(tmax, swz_xor16(tmax));
-    tmax = fmaxf(tmax, xor32f(tmax));
-    tmax *= c_logit;                      // finite: every step holds a valid token
-    if (__any(tmax > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int hl = 0; hl < HPL; ++hl) {
+        const float m_new = fmaxf(m_run[hl], tm[hl]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[hl] - m_new);
+        l_run[hl] *= alpha;
 #pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) ob[qd] *= alpha;
-      m_run = m_new;
-      if (lq == 0 && bq == 0) alpha_s[wave][h] = alpha;
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_wave_barrier();
-      // P.V row 4 lq + u BPQ + (block) belongs to head (4 lq + u BPQ) / BPQ
+        for (int qd = 0; qd < NQ; ++qd) {
 #pragma unroll
-      for (int u = 0; u < UPB; ++u) {
-        const float al = alpha_s[wave][(4 * lq + u * BPQ) / BPQ];
+          for (int bq = 0; bq < BPQ; ++bq) ob[qd][hl * BPQ + bq] *= alpha;
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-          for (int nb = 0; nb < NBQ; ++nb) acc[qd][nb][u] *= al;
+          for (int nb = 0; nb < NBQ; ++nb) acc[qd][nb][hl] *= alpha;
+        }
+        m_run[hl] = m_new;
       }
     }
-    float pr[4][4];
+    float pr[HPL][4];
 #pragma unroll
-    for (int hf = 0; hf < 4; ++hf)
+    for (int hl = 0; hl < HPL; ++hl)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        pr[hf][rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[hf][rr], c_logit, -m_run));
-        l_run += pr[hf][rr];
+      for (int hf = 0; hf < 4; ++hf) {
+        pr[hl][hf] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[hl][hf], c_logit[hl], -m_run[hl]));
+        l_run[hl] += pr[hl][hf];
       }
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      // ---- weights w = p s_v of row (h, bq) as 21-bit integers, 7-bit digits
-      const int blk = qd * BPQ + bq;
-      float w[4][4];
-      float wm = 0.0f;
+      // ---- weights w = p s_v of C row (head, block) as 21-bit integers, byte digits
+      float sv[BPQ][4], zv[BPQ][4];
 #pragma unroll
-      for (int hf = 0; hf < 4; ++hf) {
-        float sv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        meta4(&mf[1][blk][0][16 * hf + 4 * lq], sv);
-        if constexpr (ASYM) meta4(&mf[1][blk][NS - 1][16 * hf + 4 * lq], zv);
+      for (int bq = 0; bq < BPQ; ++bq) {
+        meta4(&mf[1][qd * BPQ + bq][0][4 * j], sv[bq]);
+        if constexpr (ASYM) meta4(&mf[1][qd * BPQ + bq][NS - 1][4 * j], zv[bq]);
+      }
+      float wsg[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
+      for (int rr = 0; rr < 4; ++rr) {
+        const int hl = rr / BPQ, bq = rr % BPQ;
+        float w[4];
+#pragma unroll
+        for (int hf = 0; hf < 4; ++hf) {
           // zero past T (scale reads as zero); an fma, so that the float16 scale enters
           // v_fma_mix_f32 without a separate conversion
-          w[hf][rr] = __builtin_fmaf(pr[hf][rr], sv[rr], 0.0f);
-          if constexpr (ASYM) ob[qd] = __builtin_fmaf(pr[hf][rr], zv[rr], ob[qd]);
-          wm = fmaxf(wm, w[hf][rr]);
+          w[hf] = __builtin_fmaf(pr[hl][hf], sv[bq][hf], 0.0f);
+          if constexpr (ASYM) ob[qd][rr] = __builtin_fmaf(pr[hl][hf], zv[bq][hf], ob[qd][rr]);
         }
-      }
-      wm = fmaxf(wm, swz_xor16(wm));
-      wm = fmaxf(wm, xor32f(wm));
-      // w winv <= WMAX - 1 up to an ulp of rcp; integer wi and its three digits from
-      // one float addition (kDigitBias)
-      const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
-      uint32_t bsum = 0u;   // sum of the float bits: 16 kDigitBiasBits + sum of wi (mod 2^32)
-#pragma unroll
-      for (int hf = 0; hf < 4; ++hf) {
+        // row maximum over the step's 64 tokens; w >= 0, so the float bits order as
+        // unsigned integers (an integer maximum needs no NaN quieting)
+        const float wm = __uint_as_float(row16_max_u32(
+            umax(umax(__float_as_uint(w[0]), __float_as_uint(w[1])), umax(__float_as_uint(w[2]), __float_as_uint(w[3])))));
+        // w winv <= WMAX - 1 up to an ulp of rcp; integer wi and its three digits from
+        // one float addition (kDigitBias)
+        const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
+        wsg[rr] = wm * (1.0f / static_cast<float>(WMAX - 1));
         uint32_t f[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          f[rr] = __float_as_uint(__builtin_fmaf(w[hf][rr], winv, kDigitBias));
-          if constexpr (!ASYM) bsum += f[rr];
-        }
+        for (int hf = 0; hf < 4; ++hf) f[hf] = __float_as_uint(__builtin_fmaf(w[hf], winv, kDigitBias));
         // byte transpose: digit plane k gets byte k of the four tokens' words; planes 0
         // and 1 then flip bit 7 of every byte (the xor 0x80 of the digit rule)
         const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
         const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
         const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
         const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
-        uint8_t* row = &wq_s[wave][qd][0][j][0];
-        const int off = 16 * slot16(hf, j) + 4 * lq;
+        const int prow = 4 * lq + rr;
+        uint8_t* row = &wq_s[wave][qd][0][prow][0];
+        const int off = 16 * slot16(j >> 2, prow) + 4 * (j & 3);
         *reinterpret_cast<uint32_t*>(row + off) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);   // d2
         *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) =
             __builtin_amdgcn_perm(x23, x01, 0x07060302u) ^ 0x80808080u;                            // d1
         *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) =
             __builtin_amdgcn_perm(x23, x01, 0x05040100u) ^ 0x80808080u;                            // d0
-      }
-      int ws = 0;
-      if constexpr (!ASYM) {
-        ws = static_cast<int>(bsum - 16u * kDigitBiasBits);
-        ws += xor16i(ws);
-        ws += xor32i(ws);
-      }
-      if (lq == 0) {
-        // centring of (u - 2^(b-1)) (unused when asymmetric); unsigned: only the centred
-        // sum must fit in int32
-        wsum_s[wave][qd][j] = static_cast<int>(static_cast<uint32_t>(EXC) * static_cast<uint32_t>(ws));
-        wsig_s[wave][qd][j] = wm * (1.0f / static_cast<float>(WMAX - 1));
       }
       if (qd > 0) {
         // the previous quad's P.V is done with the value rows
@@ -527,38 +558,28 @@ void decode_grouped_kernel(const DecodeParams p) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_wave_barrier();
       // ---- P.V: rows (head, block), K = the step's 64 tokens, 16 dims per instruction
-      v4i a[3];
+      v4i a[3], c0[3];
 #pragma unroll
       for (int d = 0; d < 3; ++d) {
         const uint4 x = *reinterpret_cast<const uint4*>(&wq_s[wave][qd][d][j][16 * slot16(lq, j)]);
         a[d] = v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
+        // symmetric: start each chain at -2^(b-1) times the row's digit sum
+        c0[d] = ASYM ? v4i{0, 0, 0, 0} : mfma64(a[d], excv, v4i{0, 0, 0, 0});
       }
-      int wcen[BPQ][UPB];
-      float wsg[BPQ][UPB];
-#pragma unroll
-      for (int bb = 0; bb < BPQ; ++bb)
-#pragma unroll
-        for (int u = 0; u < UPB; ++u) {
-          const int prow = 4 * lq + u * BPQ + bb;
-          wcen[bb][u] = ASYM ? 0 : wsum_s[wave][qd][prow];
-          wsg[bb][u] = wsig_s[wave][qd][prow];
-        }
 #pragma unroll
       for (int nb = 0; nb < NBQ; ++nb) {
         const int bqn = (16 * nb) / BLOCK;          // block (within the quad) of these dims
         const int rrow = 16 * nb + j;
         const uint4 x = *reinterpret_cast<const uint4*>(vrow + rrow * 64 + 16 * slot16(lq, rrow));
         const v4i bv = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
-        const v4i z = {0, 0, 0, 0};
-        const v4i e0 = mfma64(a[0], bv, z);
-        const v4i e1 = mfma64(a[1], bv, z);
-        const v4i e2 = mfma64(a[2], bv, z);
+        const v4i e0 = mfma64(a[0], bv, c0[0]);
+        const v4i e1 = mfma64(a[1], bv, c0[1]);
+        const v4i e2 = mfma64(a[2], bv, c0[2]);
 #pragma unroll
-        for (int u = 0; u < UPB; ++u) {
-          const int rr = u * BPQ + bqn;             // C row 4 lq + rr = (head, block bqn)
-          const int ai = static_cast<int>(static_cast<uint32_t>(combine3<16, 8>(e0[rr], e1[rr], e2[rr])) -
-                                          static_cast<uint32_t>(wcen[bqn][u]));
-          acc[qd][nb][u] = __builtin_fmaf(wsg[bqn][u], static_cast<float>(ai), acc[qd][nb][u]);
+        for (int u = 0; u < HPL; ++u) {
+          const int rr = u * BPQ + bqn;             // C row 4 lq + rr = (head lq HPL + u, block bqn)
+          const int ai = combine3<16, 8>(e0[rr], e1[rr], e2[rr]);
+          acc[qd][nb][u] = __builtin_fmaf(wsg[rr], static_cast<float>(ai), acc[qd][nb][u]);
         }
       }
       // the next quad or step overwrites this wave's LDS rows
@@ -585,33 +606,35 @@ void decode_grouped_kernel(const DecodeParams p) {
   }
   for (; st < s_end; st += sstr) compute_step(r, st, st + sstr < s_end ? st + sstr : s_end);
 
-  // ---- combine the four waves; partials per query head
-  l_run += swz_xor16(l_run);
-  l_run += xor32f(l_run);
+  // ---- combine the four waves; partials per query head (sums over the 16 token
+  // columns of each lane row)
 #pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) {
-    ob[qd] += swz_xor16(ob[qd]);
-    ob[qd] += xor32f(ob[qd]);
+  for (int hl = 0; hl < HPL; ++hl) l_run[hl] = row16_sum(l_run[hl]);
+  if constexpr (ASYM) {
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ob[qd][rr] = row16_sum(ob[qd][rr]);
   }
   __syncthreads();   // every wave is done with its value rows
   float* cacc = reinterpret_cast<float*>(u_s);      // [4][G][D]
-  if (lq == 0 && bq == 0) {
-    cm_s[wave][h] = m_run;
-    cl_s[wave][h] = l_run;
-  }
-  if (lq == 0) {
+  if (j == 0) {
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) cob_s[wave][h][qd * BPQ + bq] = ob[qd];
+    for (int hl = 0; hl < HPL; ++hl) {
+      cm_s[wave][lq * HPL + hl] = m_run[hl];
+      cl_s[wave][lq * HPL + hl] = l_run[hl];
+    }
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) cob_s[wave][lq * HPL + rr / BPQ][qd * BPQ + rr % BPQ] = ob[qd][rr];
   }
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
-      for (int u = 0; u < UPB; ++u) {
-        const int hh = (4 * lq + u * BPQ) / BPQ;
-        cacc[(wave * G + hh) * D + 128 * qd + 16 * nb + j] = acc[qd][nb][u];
-      }
+      for (int u = 0; u < HPL; ++u) cacc[(wave * G + lq * HPL + u) * D + 128 * qd + 16 * nb + j] = acc[qd][nb][u];
   __syncthreads();
   for (int e = tid; e < G * D; e += 256) {
     const int hh = e / D, dim = e % D;
