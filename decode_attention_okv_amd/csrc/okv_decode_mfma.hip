@@ -57,6 +57,10 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   return umax(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true)));
 }
 
+// Storage row of weight row r (16 rows of 64 bytes): rows keep their group of four and
+// rotate inside it by r / 4.
+__device__ __forceinline__ int wrow(int r) { return (r & ~3) | ((r + (r >> 2)) & 3); }
+
 // Four consecutive metadata values of LDS as floats (float32 or float16 rows).
 __device__ __forceinline__ void meta4(const float* m, float v[4]) {
   const float4 x = *reinterpret_cast<const float4*>(m);
@@ -163,7 +167,9 @@ void decode_grouped_kernel(const DecodeParams p) {
 
   // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
   __shared__ __align__(16) uint8_t u_s[UB];
-  __shared__ __align__(16) uint8_t wq_s[4][NQ][3][16][kStep];   // weight digits per row
+  // weight digits per row; row r is stored at wrow(r), which moves the four rows r with
+  // the same r % 4 (written by one instruction from the four lane rows) to different banks
+  __shared__ __align__(16) uint8_t wq_s[4][NQ][3][16][kStep];
   __shared__ __align__(16) MT mf_s[4][2][NBLK][NS][MST];        // [key/value][block][s, z][token]
   __shared__ float cm_s[4][G], cl_s[4][G];
   __shared__ float cob_s[4][G][NBLK];
@@ -469,20 +475,22 @@ void decode_grouped_kernel(const DecodeParams p) {
         for (int hf = 0; hf < 4; ++hf)
           if (base + 4 * j + hf >= T) L[hl][hf] = -INFINITY;
     }
-    // ---- online softmax per head (base 2), lazy maximum
-    float tm[HPL];
+    // ---- online softmax per head (base 2), lazy maximum: the running maximum moves
+    // only when a logit exceeds it by more than 8, which each lane can test on its own
+    // tokens; the step maximum over the 16 token columns is needed only then
+    float tl[HPL];
     bool up = false;
 #pragma unroll
     for (int hl = 0; hl < HPL; ++hl) {
-      float t = fmaxf(fmaxf(L[hl][0], L[hl][1]), fmaxf(L[hl][2], L[hl][3]));
-      t = row16_max(t) * c_logit[hl];      // finite: every step holds a valid token
-      tm[hl] = t;
+      const float t = fmaxf(fmaxf(L[hl][0], L[hl][1]), fmaxf(L[hl][2], L[hl][3])) * c_logit[hl];
+      tl[hl] = t;
       up = up || t > m_run[hl] + 8.0f;
     }
     if (__any(up)) {
 #pragma unroll
       for (int hl = 0; hl < HPL; ++hl) {
-        const float m_new = fmaxf(m_run[hl], tm[hl]);
+        // finite: every step holds a valid token
+        const float m_new = fmaxf(m_run[hl], row16_max(tl[hl]));
         const float alpha = __builtin_amdgcn_exp2f(m_run[hl] - m_new);
         l_run[hl] *= alpha;
 #pragma unroll
@@ -542,7 +550,7 @@ void decode_grouped_kernel(const DecodeParams p) {
         const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
         const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
         const int prow = 4 * lq + rr;
-        uint8_t* row = &wq_s[wave][qd][0][prow][0];
+        uint8_t* row = &wq_s[wave][qd][0][wrow(prow)][0];
         const int off = 16 * slot16(j >> 2, prow) + 4 * (j & 3);
         *reinterpret_cast<uint32_t*>(row + off) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);   // d2
         *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) =
@@ -561,7 +569,7 @@ void decode_grouped_kernel(const DecodeParams p) {
       v4i a[3], c0[3];
 #pragma unroll
       for (int d = 0; d < 3; ++d) {
-        const uint4 x = *reinterpret_cast<const uint4*>(&wq_s[wave][qd][d][j][16 * slot16(lq, j)]);
+        const uint4 x = *reinterpret_cast<const uint4*>(&wq_s[wave][qd][d][wrow(j)][16 * slot16(lq, j)]);
         a[d] = v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
         // symmetric: start each chain at -2^(b-1) times the row's digit sum
         c0[d] = ASYM ? v4i{0, 0, 0, 0} : mfma64(a[d], excv, v4i{0, 0, 0, 0});
