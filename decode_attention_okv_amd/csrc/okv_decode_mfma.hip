@@ -124,11 +124,12 @@ struct StepRaw {
   uint32_t vm[MDW];       // value metadata row of token `lane`
 };
 
-// Resident waves per SIMD the register allocation aims for: three where the LDS
-// footprint lets three workgroups share a CU (d = 128, b <= 3, except the float32 and
-// E4M3 metadata rows of 32-blocks), else no constraint.
+// Resident waves per SIMD the register allocation aims for: four where the LDS
+// footprint (<= 40 KB) lets four workgroups share a CU (d = 128, b <= 3, except the
+// float32 and E4M3 metadata rows of 32-blocks), else no constraint.  The kernel streams
+// one step ahead per wave, so resident waves set the bytes in flight.
 template <int D, int FMT, int BLOCK, int BITS>
-constexpr int kWavesPerEu = (D == 128 && BITS <= 3 && !(BLOCK == 32 && FMT != kFmtSymF16)) ? 3 : 1;
+constexpr int kWavesPerEu = (D == 128 && BITS <= 3 && !(BLOCK == 32 && FMT != kFmtSymF16)) ? 4 : 1;
 
 // One workgroup = one (split, KV head, sequence) and all G query heads of that KV
 // head; its four waves take the split's 64-token steps in turn.
@@ -151,7 +152,7 @@ void decode_grouped_kernel(const DecodeParams p) {
   // fixed-point limit that keeps every int32 block sum exact (see q_limit)
   constexpr int QMAX = q_limit(BLOCK, code_max(FMT == kFmtAsym, BITS));
   constexpr int WMAX = w_limit(code_max(FMT == kFmtAsym, BITS), kW7);
-  constexpr int UB0 = 4 * 128 * 64;    // per-wave value rows of one quad
+  constexpr int UB0 = 4 * 64 * 64;     // per-wave value rows of half a quad
   constexpr int UB1 = 4 * G * D * 4;   // wave partials in the final combine
   constexpr int UB = UB0 > UB1 ? UB0 : UB1;
   static_assert(G * D * 7 <= UB, "prologue buffers fit the shared region");
@@ -175,9 +176,9 @@ void decode_grouped_kernel(const DecodeParams p) {
   __shared__ float cob_s[4][G][NBLK];
   __shared__ int32_t qds_s[G][NBLK][4];              // per (head, block): sum q, hi, mid, lo
   __shared__ uint32_t qam_s[G];                      // per head: max |q1| (float bits)
-  // d = 256: the Q operands of both quads wait in LDS (in registers they would leave
-  // room for only one wave per SIMD); the same for every wave, indexed by lane
-  constexpr bool QB_LDS = NQ > 1;
+  // The Q operands wait in LDS (in registers they would cost a resident wave per SIMD);
+  // the same for every wave, indexed by lane
+  constexpr bool QB_LDS = true;
   __shared__ __align__(16) v4i qbs_s[QB_LDS ? NQ : 1][2][3][64];
 
   const int split = blockIdx.x;
@@ -350,7 +351,7 @@ void decode_grouped_kernel(const DecodeParams p) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_codes + unit * p.ntile_cap * static_cast<size_t>(D) * GB,
                                               static_cast<uint32_t>(ntiles) * D * GB);
   const uint32_t koff = static_cast<uint32_t>(4 * j * ROWB + GB * lq);
-  uint8_t* vrow = u_s + wave * (128 * 64);       // this wave's value rows [128 dims][64 tokens]
+  uint8_t* vrow = u_s + wave * (64 * 64);        // this wave's value rows [64 dims][64 tokens]
   MT(*mf)[NBLK][NS][MST] = mf_s[wave];
 
   // key groups of token 4 j + hf of the step (one per 16-token group hf)
@@ -361,31 +362,24 @@ void decode_grouped_kernel(const DecodeParams p) {
       buf_group<BITS>(rk, tok0 * ROWB + koff + (hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
     }
   };
-  // value groups of quad qd (dims 128 qd + lane + 64 kk) of both tiles
-  auto load_v = [&](Raw& r, int st, int qd) {
+  // value groups of dim 128 qd + 64 kk + lane of both tiles
+  auto load_v = [&](Raw& r, int st, int qd, int kk) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * GB;
-#pragma unroll
-      for (int k = 2 * qd; k < 2 * qd + 2; ++k) {
-        buf_group<BITS>(rv, tv + GB * lane + 64 * GB * k, r.vw[tt][k]);
-      }
+      buf_group<BITS>(rv, tv + GB * lane + 64 * GB * (2 * qd + kk), r.vw[tt][2 * qd + kk]);
     }
   };
-  // value rows of quad qd to LDS: [dim][64 tokens] bytes, 16-byte chunks rotated
-  auto decode_v = [&](const Raw& r, int qd) {
+  // value rows of dims 128 qd + 64 kk .. + 63 to LDS: [dim][64 tokens] bytes, 16-byte
+  // chunks rotated
+  auto decode_v = [&](const Raw& r, int qd, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int rrow = lane + 64 * kk;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        uint32_t dv[8];
-        group_to_bytes<BITS>(r.vw[tt][2 * qd + kk], dv);
-        *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt, rrow)) =
-            make_uint4(dv[0], dv[1], dv[2], dv[3]);
-        *reinterpret_cast<uint4*>(vrow + rrow * 64 + 16 * slot16(2 * tt + 1, rrow)) =
-            make_uint4(dv[4], dv[5], dv[6], dv[7]);
-      }
+    for (int tt = 0; tt < 2; ++tt) {
+      uint32_t dv[8];
+      group_to_bytes<BITS>(r.vw[tt][2 * qd + kk], dv);
+      *reinterpret_cast<uint4*>(vrow + lane * 64 + 16 * slot16(2 * tt, lane)) = make_uint4(dv[0], dv[1], dv[2], dv[3]);
+      *reinterpret_cast<uint4*>(vrow + lane * 64 + 16 * slot16(2 * tt + 1, lane)) =
+          make_uint4(dv[4], dv[5], dv[6], dv[7]);
     }
   };
   auto load_m = [&](Raw& r, int st) {
@@ -411,9 +405,9 @@ void decode_grouped_kernel(const DecodeParams p) {
       if constexpr (ASYM) mf[1][bb][1][lane] = static_cast<MT>(z);
     }
     load_m(r, nx);
-    // values of the first quad go to LDS at once, so their registers refill early
-    decode_v(r, 0);
-    load_v(r, nx, 0);
+    // the first value rows go to LDS at once, so their registers refill early
+    decode_v(r, 0, 0);
+    load_v(r, nx, 0, 0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
     // ---- logits (integer units of c_logit[hl]): head lq HPL + hl, token 4 j + hf
@@ -560,8 +554,8 @@ void decode_grouped_kernel(const DecodeParams p) {
       }
       if (qd > 0) {
         // the previous quad's P.V is done with the value rows
-        decode_v(r, qd);
-        load_v(r, nx, qd);
+        decode_v(r, qd, 0);
+        load_v(r, nx, qd, 0);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_wave_barrier();
@@ -576,8 +570,17 @@ void decode_grouped_kernel(const DecodeParams p) {
       }
 #pragma unroll
       for (int nb = 0; nb < NBQ; ++nb) {
+        if (nb == NBQ / 2) {
+          // second half of the quad's dims: rows of the first half are done
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_wave_barrier();
+          decode_v(r, qd, 1);
+          load_v(r, nx, qd, 1);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_wave_barrier();
+        }
         const int bqn = (16 * nb) / BLOCK;          // block (within the quad) of these dims
-        const int rrow = 16 * nb + j;
+        const int rrow = 16 * (nb % (NBQ / 2)) + j;
         const uint4 x = *reinterpret_cast<const uint4*>(vrow + rrow * 64 + 16 * slot16(lq, rrow));
         const v4i bv = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
         const v4i e0 = mfma64(a[0], bv, c0[0]);
@@ -608,7 +611,10 @@ void decode_grouped_kernel(const DecodeParams p) {
   if (st < s_end) {
     load_m(r, st);
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) load_v(r, st, qd);
+    for (int qd = 0; qd < NQ; ++qd) {
+      load_v(r, st, qd, 0);
+      load_v(r, st, qd, 1);
+    }
 #pragma unroll
     for (int hf = 0; hf < 4; ++hf) load_k(r, st, hf);
   }
