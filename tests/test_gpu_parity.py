@@ -146,12 +146,20 @@ def test_rotation_none(name, over, kernel):
     run_case(wl, t, chunks, kernel=kernel)
 
 
-@pytest.mark.parametrize("splits", [1, 3, 16])
-def test_split_count_invariance(splits):
+# split counts that reach every load-batch size of the merge (2, 4, 8, 16 and 32 splits
+# per thread; 70 and 40 take two batches), at d = 128 (two threads per output) and 256
+@pytest.mark.parametrize("t,splits", [(1111, 1), (1111, 3), (1111, 6), (1111, 16), (1111, 32), (4500, 70)])
+def test_split_count_invariance(t, splits):
     wl = okv_synth.workload("mha_b4h32_t128k").with_(batch=1, hq=4, hkv=4)
-    run_case(wl, 1111, [1111], splits=splits)
+    run_case(wl, t, [t], splits=splits)
     wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=8, hkv=2)
-    run_case(wl, 1111, [1111], splits=splits, kernel="grouped")
+    run_case(wl, t, [t], splits=splits, kernel="grouped")
+
+
+@pytest.mark.parametrize("splits", [5, 40])
+def test_split_count_invariance_d256(splits):
+    wl = okv_synth.workload("so4_d256_b32_t8k").with_(batch=1)
+    run_case(wl, 2700, [2700], splits=splits, kernel="grouped")
 
 
 @pytest.mark.parametrize("d,block,quant", [
