@@ -118,7 +118,7 @@ __device__ __forceinline__ void meta_entry(const uint32_t* w, int bb, float& s, 
 
 template <int NQ, int DPL, int MDW, int BITS>
 struct StepRaw {
-  uint32_t kw[4][NQ][BITS];  // token 16 hf + (lane % 16) of the step, key group 4 qd + lane / 16
+  uint32_t kw[4][NQ][BITS];  // token 4 (lane % 16) + hf of the step, key group 4 qd + lane / 16
   uint32_t vw[2][DPL][BITS]; // value tile tt of the step, dims lane + 64 k
   uint32_t km[MDW];       // key metadata row of token `lane` of the step
   uint32_t vm[MDW];       // value metadata row of token `lane`
@@ -139,7 +139,7 @@ void decode_grouped_kernel(const DecodeParams p) {
   constexpr int NQ = D / 128;          // quads of four 32-dim groups (128 dims each)
   constexpr int BPQ = 128 / BLOCK;     // quantisation blocks per quad
   constexpr int NBLK = D / BLOCK;
-  static_assert(G * BPQ == 16, "one 16-column (head, block) set per quad");
+  static_assert(G * BPQ == 16, "one 16-row (head, block) set per quad");
   constexpr int ROWB = BITS * D / 8;    // bytes per key row
   constexpr int GB = 4 * BITS;         // bytes per 32-code group
   constexpr int EXC = 1 << (BITS - 1); // excess of symmetric codes
