@@ -220,6 +220,14 @@ def cpu_baseline(wl, target_s=12.0):
         if el >= target_s or n >= 64:
             break
     unit_bytes = 2 * unit.tokens * unit.row_bytes()
+    # write path: the oracle's bit-exact float32 rotation, quantisation and packing of
+    # the first nw key and value vectors of the unit
+    nw = min(4096, unit.tokens)
+    kh, vh = okv_synth.host_f32(k)[0, :nw, 0], okv_synth.host_f32(v)[0, :nw, 0]
+    tw = time.perf_counter()
+    oracle.write_unit(kh, vh, unit, p32)
+    elw = time.perf_counter() - tw
+    hv_s = 2 * nw / elw                      # head vectors (keys and values) per second
     return {
         "value": round(n * unit_bytes / el / 1e9, 4),
         "unit": "GB/s",
@@ -228,6 +236,11 @@ def cpu_baseline(wl, target_s=12.0):
         "sample": f"{n} decode call(s) of one (sequence, KV head) unit: {unit.group} query head(s) "
                   f"over {unit.tokens} tokens (NumPy, float64 attention from packed codes), "
                   f"{el:.1f} s; BLAS threads {threads}, unpack/dequantise single-threaded",
+        "write_head_vectors_per_s": round(hv_s, 1),
+        "write_tokens_per_s": round(hv_s / (2 * wl.hkv), 2),
+        "write_sample": f"okv_write of {nw} key and {nw} value vectors of one unit (NumPy float32 "
+                        f"bit-exact path, {elw:.2f} s); a token is one position of one sequence: "
+                        f"tokens/s = head vectors/s / (2 x {wl.hkv} KV heads)",
     }
 
 
@@ -362,6 +375,7 @@ def main():
         "decode_kernel_us": round(1e3 * attn_ms / K, 2),
         "reduce_kernel_us": round(1e3 * red_ms / K, 2),
         "write_tokens_per_s": round(write_tok_s, 1),
+        "write_head_vectors_per_s": round(write_tok_s * 2 * wl.hkv, 1),
         "write_prefill_ms": round(prefill_ms, 3),
         "write_prefill_GBs": round(write_bytes_per_position(wl) * T0 / (prefill_ms * 1e-3) / 1e9, 2),
         "decode_kernel": kernel,
