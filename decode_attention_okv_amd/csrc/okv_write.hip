@@ -89,8 +89,13 @@ __device__ __forceinline__ void keep_mask(int n, uint32_t* m) {
 // quantised; key rows are stored straight from the lanes; value codes go through LDS
 // to be regrouped per dimension (old codes of earlier tokens are kept, slots after
 // the new tokens stay zero).
-template <int D, int BLOCK, bool ASYM, int BITS>
+//
+// SIGN_BF16: the sign-flip rotation with bfloat16 inputs, fixed at compile time, so that
+// the other rotations' and float32 inputs' code leaves this variant.
+template <int D, int BLOCK, bool ASYM, int BITS, bool SIGN_BF16>
 __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
+  const int rotation = SIGN_BF16 ? static_cast<int>(kRotSign) : p.rotation;
+  const bool in_bf16 = SIGN_BF16 || p.in_bf16 != 0;
   constexpr int EPL = D / 4;                          // elements per lane
   constexpr int GPL = EPL / 32;                       // 32-code groups per lane
   constexpr int BPL = EPL >= BLOCK ? EPL / BLOCK : 1; // quantisation blocks per lane
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   // SO(4) matrices of B: staged in LDS once per workgroup (every lane reads those of
   // its dims for each vector)
   __shared__ __align__(16) float rot_s[4 * D];
-  if (p.rotation == kRotSo4) {                        // uniform over the workgroup
+  if (rotation == kRotSo4) {                          // uniform over the workgroup
     for (int e = tid; e < 4 * D; e += 256) rot_s[e] = p.rot[e];
     __syncthreads();
   }
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
     const int pos = tile_base + slot;
     const size_t src = ((static_cast<size_t>(b) * p.n_new + (pos - p.len)) * p.hkv + h) * D + EPL * r;
     float x[EPL];
-    if (p.in_bf16) {
+    if (in_bf16) {
       const uint4* s4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(tensor ? p.v : p.k) + src);
 #pragma unroll
       for (int i = 0; i < EPL / 8; ++i) {
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         x[4 * i] = w.x; x[4 * i + 1] = w.y; x[4 * i + 2] = w.z; x[4 * i + 3] = w.w;
       }
     }
-    if (p.rotation == kRotSign) {
+    if (rotation == kRotSign) {
       const float4* sg = reinterpret_cast<const float4*>(p.rot + EPL * r);
 #pragma unroll
       for (int i = 0; i < EPL / 4; ++i) {
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         x[4 * i] *= g.x; x[4 * i + 1] *= g.y; x[4 * i + 2] *= g.z; x[4 * i + 3] *= g.w;
       }
     }
-    const bool rotated = p.rotation != kRotNone;   // U = I: y = x (uniform)
+    const bool rotated = rotation != kRotNone;     // U = I: y = x (uniform)
     if (rotated) {
     // butterfly stages of stride 1 .. EPL/2 inside the lane
 #pragma unroll
@@ -189,12 +194,12 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
     // Symmetric codes with the sign-flip rotation use the unnormalised values: the
     // block maximum of |RN(x c)| is RN(max|x| c) (rounding is monotone), and the
     // code quotient folds c in.  Otherwise y = RN(x c) is formed here.
-    const bool normalized = ASYM || p.rotation == kRotSo4;
+    const bool normalized = ASYM || rotation == kRotSo4;
     if (normalized && rotated) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = x[e] * sc;
     }
-    if (p.rotation == kRotSo4) {
+    if (rotation == kRotSo4) {
       // y_row = ((R_row0 x0 + R_row1 x1) + R_row2 x2) + R_row3 x3 per 4-block
 #pragma unroll
       for (int q4 = 0; q4 < EPL / 4; ++q4) {
@@ -363,8 +368,14 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
 
 template <int D, int BLOCK, int BITS>
 void launch_b(const WriteParams& p, dim3 grid, hipStream_t s) {
-  if (p.quant == kQuantAsym) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS>), grid, dim3(256), 0, s, p);
+  const bool sb = p.rotation == kRotSign && p.in_bf16;
+  if (p.quant == kQuantAsym) {
+    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, false>), grid, dim3(256), 0, s, p);
+  }
 }
 
 template <int D, int BLOCK>
