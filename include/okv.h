@@ -157,7 +157,11 @@ int okv_create(const okv_config* cfg, okv_handle** out);
  * U, quantise it blockwise, pack the codes and store codes and scales at positions
  * len .. len+n_new-1 (the write path of the idea card's Implementation notes).
  * k, v: device, [batch][n_new][kv][d] in the input type, 16-byte aligned.
- * Asynchronous on hip_stream; len advances by n_new at once (host side). */
+ * Asynchronous on hip_stream; len advances by n_new at once (host side).
+ * It writes positions len .. len+n_new-1 only (and rewrites the earlier codes of the
+ * current 32-token value tile unchanged), while okv_decode_attn reads positions below
+ * its own len: so a write may run on another stream concurrently with a decode
+ * enqueued before it; the next decode must be ordered after the write. */
 int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* hip_stream);
 
 /* One decode step: for every (sequence, query head) attend over all len cached

@@ -288,3 +288,42 @@ def test_error_paths():
     assert np.isfinite(out.cpu().numpy()).all()
     cache.close()
     assert okv.okv_destroy(ctypes.c_void_p()) == okv.OKV_OK
+
+
+def test_append_overlaps_previous_decode():
+    """One-token appends on a second stream, running concurrently with the previous
+    decode (as the benchmark schedules them), give the same outputs bit for bit as the
+    same steps on one stream: an append writes position len only and rewrites the
+    earlier codes of the current value tile unchanged, and a decode reads positions
+    below len.  The steps cross a 32-token tile boundary."""
+    _need_gpu()
+    for name, over in (("mha_b4h32_t128k", dict(batch=2, hq=4, hkv=4)),
+                       ("gqa_b16h64kv8_t128k_asym", dict(batch=2, hq=16, hkv=2))):
+        wl = okv_synth.workload(name).with_(**over)
+        p32, _ = params_of(wl)
+        t0, steps = 1000, 40
+        k, v = okv_synth.kv_tokens(wl, 0, t0, device="cuda")
+        news = [okv_synth.kv_tokens(wl, t0 + i, 1, device="cuda", step=i + 1) for i in range(steps)]
+        qs = [okv_synth.queries(wl, i + 1, device="cuda") for i in range(steps)]
+        results = []
+        for two_streams in (False, True):
+            cache = make_cache(wl, round_up(t0 + steps + 1, 32), p32)
+            cache.write(k, v)
+            main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+            say(name, "appends on", "two streams" if two_streams else "one stream")
+            outs = []
+            for i in range(steps):
+                if two_streams:
+                    done = torch.cuda.Event()
+                    with torch.cuda.stream(side):
+                        cache.write(*news[i])
+                        done.record(side)
+                    main.wait_event(done)
+                else:
+                    cache.write(*news[i])
+                outs.append(cache.decode_attn(qs[i]))
+            torch.cuda.synchronize()
+            results.append(torch.stack(outs).cpu())
+            cache.close()
+            free_gpu()
+        assert torch.equal(results[0], results[1]), name
