@@ -200,7 +200,8 @@ int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void
  *          sweep
  * head_dim 128 or 256; 4 | block, block | head_dim; bits 2..4; eps finite >= 0;
  * 1 <= n_cand <= 1024; n * head_dim < 2^31.  Allocates and frees its own device
- * workspace; runs on hip_stream and returns when done. */
+ * workspace and a pinned host staging buffer for rot and cand; runs on hip_stream and
+ * returns when done. */
 int okv_so4_calibrate(const float* x, int32_t n, int32_t head_dim, int32_t block, int32_t bits, float eps,
                       float* rot, const float* cand, int32_t sweeps, int32_t n_cand, double* trace,
                       void* hip_stream);
