@@ -14,7 +14,10 @@
 //    the squared error of the block, y computed group by group from hx twice (block
 //    maximum, then error), with group g's matrix replaced by cand_c R_g.  Partial sums
 //    per (candidate, chunk) are added in a fixed order (chunk ascending, in double).
-//  * select_kernel (one workgroup, after each search evaluation) takes the step's
+//  * Steps in different quantisation blocks are independent (a group's error and update
+//    touch its own block only), so step k of every block runs in one launch, the block
+//    on grid z; each block still takes its groups in ascending order.
+//  * select_kernel (a workgroup per block, after each search evaluation) takes the step's
 //    decision (first minimum over the candidates) and sets R_g <- P_best R_g in double,
 //    with its float32 copy for the next evaluation; trace_kernel adds a block's error to
 //    a trace entry (the blocks' errors in ascending order).  The search is queued on the
@@ -86,6 +89,7 @@ struct EvalParams {
   const float* cand;    // [n_cand][16] perturbations of group `group`
   float* part;          // [n_cand][nchunk] partial error sums
   int n, d, block, group, nchunk, lev, n_cand;
+  int cand_zstride;     // floats from the candidates of grid-z block z to z + 1 (0: shared)
   float eps;
 };
 
@@ -106,13 +110,17 @@ __device__ __forceinline__ double cand_error(const float* part, int nchunk, int 
   return t;
 }
 
-// One search step's decision, by one workgroup: the candidate with the smallest error
-// (the first one on ties) replaces R_g by P_best R_g (double: rd; float32 copy: rf).
-// n_cand <= 1024.
+// One search step's decision, by one workgroup per quantisation block z (group
+// group + z zgroups, its partials and candidates at z times their strides): the
+// candidate with the smallest error (the first one on ties) replaces R_g by P_best R_g
+// (double: rd; float32 copy: rf).  n_cand <= 1024.
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ part, int nchunk, int n_cand,
-                                                     const float* __restrict__ cand_g, int group, double* rd,
-                                                     float* rf) {
+                                                     const float* __restrict__ cand_g, int group, int zgroups,
+                                                     int cand_zstride, double* rd, float* rf) {
   __shared__ double err_s[1024];
+  part += static_cast<size_t>(blockIdx.x) * n_cand * nchunk;
+  cand_g += static_cast<size_t>(blockIdx.x) * cand_zstride;
+  group += static_cast<int>(blockIdx.x) * zgroups;
   for (int c = threadIdx.x; c < n_cand; c += blockDim.x) err_s[c] = cand_error(part, nchunk, c);
   __syncthreads();
   if (threadIdx.x != 0) return;
@@ -139,8 +147,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ p
 // One thread per calibration vector: the vector's block of H x is read once, the
 // outputs of the block's other groups are formed once, and every candidate then
 // replaces group g's four outputs (block maximum, then the squared error of the block,
-// groups in ascending order).  Partial sums per (candidate, chunk).  Grid z > 1 (one
-// candidate only): z-th quantisation block after group g's, partials block-major.
+// groups in ascending order).  Partial sums per (candidate, chunk).  Grid z: the z-th
+// quantisation block after group g's (group g + z block/4), partials block-major.
 template <int NGB>
 __global__ __launch_bounds__(kEvalThreads) void eval_kernel(const EvalParams p) {
   constexpr int NCMAX = 64;                // candidates per launch (more: several launches)
@@ -150,10 +158,11 @@ __global__ __launch_bounds__(kEvalThreads) void eval_kernel(const EvalParams p) 
   const int c0 = blockIdx.y * NCMAX;
   const int group = p.group + static_cast<int>(blockIdx.z) * (p.block / 4);
   float* part = p.part + static_cast<size_t>(blockIdx.z) * p.n_cand * p.nchunk;
+  const float* cand = p.cand + static_cast<size_t>(blockIdx.z) * p.cand_zstride;
   const int nc = min(NCMAX, p.n_cand - c0);
   for (int e = tid; e < nc * 16; e += kEvalThreads) {
     const int c = e / 16, r = (e % 16) / 4, col = e % 4;
-    const float* P = p.cand + 16 * (c0 + c);
+    const float* P = cand + 16 * (c0 + c);
     const float* R = p.rot + 16 * group;
     mg[c][4 * r + col] = P[4 * r] * R[col] + P[4 * r + 1] * R[4 + col] + P[4 * r + 2] * R[8 + col] +
                          P[4 * r + 3] * R[12 + col];
@@ -257,7 +266,7 @@ struct Work {
 
 // Launch of eval_kernel for n_cand candidates of group `group` (partials in w.part).
 int launch_eval(const Work& w, int32_t n, int32_t d, int32_t block, int32_t bits, float eps, const float* dev_cand,
-                int32_t n_cand, int32_t group, hipStream_t s, int nblk = 1) {
+                int32_t n_cand, int32_t group, hipStream_t s, int nblk = 1, int cand_zstride = 0) {
   EvalParams p{};
   p.hx = w.hx;
   p.rot = w.rot;
@@ -271,6 +280,7 @@ int launch_eval(const Work& w, int32_t n, int32_t d, int32_t block, int32_t bits
   p.lev = (1 << (bits - 1)) - 1;
   p.eps = eps;
   p.n_cand = n_cand;
+  p.cand_zstride = cand_zstride;
   const dim3 grid(p.nchunk, (n_cand + 63) / 64, nblk);
   switch (block / 4) {   // groups per quantisation block
     case 1: hipLaunchKernelGGL(eval_kernel<1>, grid, dim3(kEvalThreads), 0, s, p); break;
@@ -295,13 +305,14 @@ int check_args(const float* x, int32_t n, int32_t d, int32_t block, int32_t bits
   return OKV_OK;
 }
 
-int setup(Work& w, const float* x, int32_t n, int32_t d, int32_t n_cand, size_t cand_floats, hipStream_t s) {
+// nz: quantisation blocks evaluated in one launch (partials for n_cand x nz x chunks)
+int setup(Work& w, const float* x, int32_t n, int32_t d, int32_t n_cand, int nz, size_t cand_floats,
+          hipStream_t s) {
   const int nchunk = (n + kEvalThreads - 1) / kEvalThreads;
   if (!hip_ok(hipMalloc(&w.hx, static_cast<size_t>(n) * d * sizeof(float))) ||
       !hip_ok(hipMalloc(&w.rot, static_cast<size_t>(d) * 4 * sizeof(float))) ||
       !hip_ok(hipMalloc(&w.cand, cand_floats * sizeof(float))) ||
-      // partials: n_cand candidates of one block, or one candidate of each of <= d/4 blocks
-      !hip_ok(hipMalloc(&w.part, static_cast<size_t>(n_cand > d / 4 ? n_cand : d / 4) * nchunk * sizeof(float)))) {
+      !hip_ok(hipMalloc(&w.part, static_cast<size_t>(n_cand) * nz * nchunk * sizeof(float)))) {
     return OKV_E_HIP;
   }
   const dim3 grid((n + kVec - 1) / kVec);
@@ -345,7 +356,7 @@ int okv_so4_eval(const float* x, int32_t n, int32_t head_dim, int32_t block, int
   }
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   okv::Work w;
-  st = okv::setup(w, x, n, head_dim, n_cand, static_cast<size_t>(n_cand) * 16, s);
+  st = okv::setup(w, x, n, head_dim, n_cand, 1, static_cast<size_t>(n_cand) * 16, s);
   if (st != OKV_OK) return st;
   if (!okv::hip_ok(hipMemcpyAsync(w.rot, rot, static_cast<size_t>(head_dim) * 4 * sizeof(float),
                                   hipMemcpyHostToDevice, s)) ||
@@ -368,7 +379,7 @@ int okv_so4_calibrate(const float* x, int32_t n, int32_t head_dim, int32_t block
   const size_t cand_floats = static_cast<size_t>(sweeps) * ng * per_group + 16;   // + identity
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   okv::Work w;
-  st = okv::setup(w, x, n, head_dim, n_cand, cand_floats, s);
+  st = okv::setup(w, x, n, head_dim, n_cand, head_dim / block, cand_floats, s);
   if (st != OKV_OK) return st;
   static const float kIdentity[16] = {1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1};
   float* dev_identity = w.cand + cand_floats - 16;
@@ -414,11 +425,15 @@ int okv_so4_calibrate(const float* x, int32_t n, int32_t head_dim, int32_t block
   };
   if (trace != nullptr && (st = total(0)) != OKV_OK) return st;
   for (int sw = 0; sw < sweeps; ++sw) {
-    for (int g = 0; g < ng; ++g) {
-      const float* dc = w.cand + (static_cast<size_t>(sw) * ng + g) * per_group;
-      st = okv::launch_eval(w, n, head_dim, block, bits, eps, dc, n_cand, g, s);
+    // step k of every block at once: groups k, k + gpb, k + 2 gpb, ...
+    const int gpb = block / 4;
+    const int zstride = static_cast<int>(gpb * per_group);
+    for (int k = 0; k < gpb; ++k) {
+      const float* dc = w.cand + (static_cast<size_t>(sw) * ng + k) * per_group;
+      st = okv::launch_eval(w, n, head_dim, block, bits, eps, dc, n_cand, k, s, nblk, zstride);
       if (st != OKV_OK) return st;
-      hipLaunchKernelGGL(okv::select_kernel, dim3(1), dim3(256), 0, s, w.part, nchunk, n_cand, dc, g, w.rd, w.rot);
+      hipLaunchKernelGGL(okv::select_kernel, dim3(nblk), dim3(256), 0, s, w.part, nchunk, n_cand, dc, k, gpb,
+                         zstride, w.rd, w.rot);
       if (!okv::hip_ok(hipGetLastError())) return OKV_E_HIP;
     }
     if (trace != nullptr && (st = total(sw + 1)) != OKV_OK) return st;
