@@ -67,14 +67,23 @@ def test_so4_calibrate_recovers_planted_rotations():
         assert np.allclose(rot[8 * b + 1], planted[b], atol=1e-6)
 
 
-@pytest.mark.parametrize("name,d,block,bits", [("so4_d256_b32_t8k", 256, 32, 3), ("mha_b4h32_t128k", 128, 32, 4)])
-def test_so4_calibrate_matches_oracle(name, d, block, bits):
+# The search runs step k of every quantisation block in one launch: block 4 (one group
+# per block, 32 blocks at once), block = head_dim (one block of 32 or 64 groups), a
+# vector count that leaves a partial chunk, and 70 candidates (two candidate tiles).
+@pytest.mark.parametrize("name,d,block,bits,n,n_cand", [
+    ("so4_d256_b32_t8k", 256, 32, 3, 1024, 8),
+    ("mha_b4h32_t128k", 128, 32, 4, 1024, 8),
+    ("mha_b4h32_t128k", 128, 4, 3, 1000, 8),
+    ("mha_b4h32_t128k", 128, 128, 3, 777, 70),
+    ("so4_d256_b32_t8k", 256, 256, 3, 1000, 8),
+])
+def test_so4_calibrate_matches_oracle(name, d, block, bits, n, n_cand):
     _need_gpu()
     import decode_attention_okv_amd as okv
-    wl, x = keys(name, 1024)
+    wl, x = keys(name, n)
     rot0 = okv_synth.rotation_params(wl.with_(rotation="so4"))
-    cand = okv_synth.so4_candidates(d, 2, 8)
-    say("okv_so4_calibrate", name, bits)
+    cand = okv_synth.so4_candidates(d, 2, n_cand)
+    say("okv_so4_calibrate", name, "block", block, "bits", bits, "n", n, "candidates", n_cand)
     rot, trace = okv.so4_calibrate(torch.from_numpy(np.ascontiguousarray(x)).cuda(), rot0, cand,
                                    block=block, bits=bits, eps=1e-6)
     rot_o, trace_o, _ = oracle.calibrate_so4(x, rot0, cand, block, 1e-6, bits)
