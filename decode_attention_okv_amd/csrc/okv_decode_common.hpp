@@ -138,21 +138,26 @@ __device__ __forceinline__ int combine3(int a, int b, int c) {
 // order by bits 2-3 of the row spreads 16 consecutive rows over all 64 banks.
 __device__ __forceinline__ int slot16(int c, int r) { return (c ^ (r >> 2)) & 3; }
 
+// Cache policy (the loads' aux bits) for data read once per call: non-temporal.  The
+// per-head decode reads every code and scale exactly once and gains from it; kernels
+// that re-read the cache (prefill) or that measured no gain (grouped decode) keep 0.
+constexpr int kStreamAux = 2;
+
 // One b-bit code group (4 b bytes) at byte offset voff of a buffer resource; zero past
-// the resource's range.
-template <int BITS>
+// the resource's range.  AUX: cache policy of the load.
+template <int BITS, int AUX = 0>
 __device__ __forceinline__ void buf_group(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* w) {
   if constexpr (BITS == 2) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, AUX);
     w[0] = x[0];
     w[1] = x[1];
   } else if constexpr (BITS == 3) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, AUX);
     w[0] = x[0];
     w[1] = x[1];
     w[2] = x[2];
   } else {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX);
     w[0] = x[0];
     w[1] = x[1];
     w[2] = x[2];
@@ -164,10 +169,10 @@ __device__ __forceinline__ void buf_group(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // or u <= 2^b - 1 (asymmetric).
 constexpr int code_max(bool asym, int bits) { return asym ? (1 << bits) - 1 : (1 << (bits - 1)) - 1; }
 
-template <int FMT>
+template <int FMT, int AUX = 0>
 __device__ __forceinline__ uint32_t buf_meta(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (FMT == kFmtSymF32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-  else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  if constexpr (FMT == kFmtSymF32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX);
 }
 
 }  // namespace dec

@@ -65,8 +65,12 @@ __device__ __forceinline__ void meta_sz(uint32_t raw, float& s, float& z) {
 
 // One workgroup = one (split, query head, sequence); its four waves take the split's
 // 64-token steps in turn.
-template <int D, int FMT, int BLOCK, int BITS>
+// STREAM: every code and scale is read by exactly one workgroup (one query head per KV
+// head), so the loads are marked non-temporal; with query groups the heads of a group
+// re-read the same cache lines and keep the default policy.
+template <int D, int FMT, int BLOCK, int BITS, bool STREAM>
 __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) {
+  constexpr int kAux = STREAM ? kStreamAux : 0;
   constexpr int NQ = D / 128;          // 128-dim quads
   constexpr int SEG = BLOCK < 128 ? BLOCK : 128;   // block part inside one quad
   constexpr int BPQ = 128 / SEG;       // segments per quad (1, 2 or 4)
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
     const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      buf_group<BITS>(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
+      buf_group<BITS, kAux>(rk, tok0 * ROWB + koff + (16 * hf * ROWB + 4 * GB * qd), r.kw[hf][qd]);
     }
   };
   auto load_v = [&](Raw& r, int st, int qd) {
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t tv = (2 * static_cast<uint32_t>(st) + tt) * D * GB;
 #pragma unroll
-      for (int k = 2 * qd; k < 2 * qd + 2; ++k) buf_group<BITS>(rv, tv + GB * lane + 64 * GB * k, r.vw[tt][k]);
+      for (int k = 2 * qd; k < 2 * qd + 2; ++k) buf_group<BITS, kAux>(rv, tv + GB * lane + 64 * GB * k, r.vw[tt][k]);
     }
   };
   auto load_m = [&](Meta& m, int st) {
@@ -251,8 +255,8 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
         // block of segment qd BPQ + lq (lanes with lq >= BPQ read a neighbouring
         // entry, or zero past T; unused)
         const uint32_t o = (tok0 + 16 * hf) * (NBLK * MB) + moff + ((qd * BPQ + lq) * SEG / BLOCK) * MB;
-        m.k[hf][qd] = buf_meta<FMT>(rkm, o, 0);
-        m.v[hf][qd] = buf_meta<FMT>(rvm, o, 0);
+        m.k[hf][qd] = buf_meta<FMT, kAux>(rkm, o, 0);
+        m.v[hf][qd] = buf_meta<FMT, kAux>(rvm, o, 0);
       }
   };
   // value rows of quad qd to LDS: [dim][64 tokens] bytes, 16-byte chunks rotated
@@ -465,11 +469,21 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
   }
 }
 
+template <int D, int FMT, int BLOCK, bool STREAM>
+void launch_s(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.bits == 2) {
+    hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 2, STREAM>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  } else if (p.bits == 4) {
+    hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 4, STREAM>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  } else {
+    hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 3, STREAM>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  }
+}
+
 template <int D, int FMT, int BLOCK>
 void launch_t(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (p.bits == 2) hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 2>), grid, dim3(256), 0, s, e0, e1, 0, p);
-  else if (p.bits == 4) hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 4>), grid, dim3(256), 0, s, e0, e1, 0, p);
-  else hipExtLaunchKernelGGL((decode_head_kernel<D, FMT, BLOCK, 3>), grid, dim3(256), 0, s, e0, e1, 0, p);
+  if (p.hq == p.hkv) launch_s<D, FMT, BLOCK, true>(p, grid, s, e0, e1);
+  else launch_s<D, FMT, BLOCK, false>(p, grid, s, e0, e1);
 }
 
 template <int D, int BLOCK>
