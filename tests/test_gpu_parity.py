@@ -292,10 +292,12 @@ def test_error_paths():
 
 def test_append_overlaps_previous_decode():
     """One-token appends on a second stream, running concurrently with the previous
-    decode (as the benchmark schedules them), give the same outputs bit for bit as the
-    same steps on one stream: an append writes position len only and rewrites the
-    earlier codes of the current value tile unchanged, and a decode reads positions
-    below len.  The steps cross a 32-token tile boundary."""
+    decode, give the same outputs bit for bit as the same steps on one stream: an
+    append writes position len only and rewrites the earlier codes of the current
+    value tile unchanged, and a decode reads positions below len.  Writes stay ordered
+    after writes (the side stream waits for the prefill, and its appends follow each
+    other on that one stream), as okv_write requires.  The steps cross a 32-token tile
+    boundary."""
     _need_gpu()
     for name, over in (("mha_b4h32_t128k", dict(batch=2, hq=4, hkv=4)),
                        ("gqa_b16h64kv8_t128k_asym", dict(batch=2, hq=16, hkv=2))):
@@ -310,6 +312,7 @@ def test_append_overlaps_previous_decode():
             cache = make_cache(wl, round_up(t0 + steps + 1, 32), p32)
             cache.write(k, v)
             main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+            side.wait_stream(main)          # write after write: appends follow the prefill
             say(name, "appends on", "two streams" if two_streams else "one stream")
             outs = []
             for i in range(steps):
@@ -327,3 +330,32 @@ def test_append_overlaps_previous_decode():
             cache.close()
             free_gpu()
         assert torch.equal(results[0], results[1]), name
+
+
+def test_asym_zero_point_block_by_hand():
+    """The hand-worked asymmetric block of the CPU pins (minimum -1.03125 stored as the
+    E4M3 zero-point -1.0, an E4M3 scale tie, exact code ties, a difference y - z that
+    float32 rounds onto a tie, and a constant block with scale 0) through okv_write
+    with U = I: the stored key row, value codes and metadata equal the hand-typed
+    values."""
+    _need_gpu()
+    import oracle
+    from test_oracle_quant import asym_pin_block
+    y, codes, meta = asym_pin_block()
+    wl = okv_synth.workload("gqa_b16h64kv8_t128k_asym").with_(
+        batch=1, hq=1, hkv=1, rotation="none", in_dtype="f32")
+    p32, _ = params_of(wl)
+    cache = make_cache(wl, 32, p32)
+    x = torch.from_numpy(y).reshape(1, 1, 1, 128).cuda()
+    say("asym hand-worked block okv_write")
+    cache.write(x, (-x).contiguous())
+    torch.cuda.synchronize()
+    k_u = oracle.unpack_rows(cache.k_codes[0, 0, :1].cpu().numpy(), 128)[0]
+    assert k_u.tolist() == codes
+    assert cache.k_meta[0, 0, 0].cpu().numpy().view(np.uint8).reshape(2, 2).tolist() == meta
+    # the values are -y: a different block, checked against the oracle's quantiser
+    v_u = oracle.unpack_vtiles(cache.v_codes[0, 0, :1].cpu().numpy(), 1)[0]
+    want_u, want_meta = oracle.quantize_f32(-y[None], wl)
+    assert v_u.tolist() == want_u[0].tolist()
+    assert cache.v_meta[0, 0, 0].cpu().numpy().view(np.uint8).reshape(2, 2).tolist() == want_meta[0].tolist()
+    cache.close()

@@ -201,6 +201,56 @@ def test_asym_small_example_by_hand():
     assert u[0, 63] == 7
 
 
+def asym_pin_block():
+    """A hand-worked 128-value vector for the asymmetric quantiser (block 64, E4M3
+    scale and zero-point), the news item's third paragraph: unsigned codes with a
+    scale and a zero-point per 64-element sub-block, both in FP8.
+
+    Block 0: minimum -1.03125 (not an E4M3 value: it stores as -1.0), maximum
+    7.28125, so max - min = 8.3125 and (max - min) / 7 = 1.1875 exactly, the midpoint
+    of the E4M3 neighbours 1.125 (mantissa 001) and 1.25 (mantissa 010): the tie goes
+    to the even mantissa, s = 1.25.  Taking the stored zero-point -1.0 in place of the
+    minimum would give 8.28125 / 7 = 1.183 -> 1.125 instead.
+    Codes u = rne(RN32(y + 1.0) / 1.25), clipped to 0..7:
+      -1.03125 -> t = -0.03125 -> 0;   7.28125 -> t = 8.28125, 6.625 -> 7;
+      2.125 -> t = 3.125, 2.5 (tie) -> 2;   3.375 -> t = 4.375, 3.5 (tie) -> 4;
+      -0.375 -> t = 0.625, 0.5 (tie) -> 0;   7.125 -> t = 8.125, 6.5 (tie) -> 6;
+      -0.375 + 2^-25 -> t = 0.625 + 2^-25 is halfway between two float32 values and
+        rounds to even, t = 0.625, so 0.5 (tie) -> 0; without the float32 rounding of
+        y - z the quotient would exceed 0.5 and give 1;
+      ramp y = -1 + j / 8 (j = 0..56) -> t = j / 8, u = rne(j / 10):
+        j 0-5 -> 0 (j = 5 a tie), 6-14 -> 1, 15-25 -> 2 (15, 25 ties), 26-34 -> 3,
+        35-45 -> 4 (35, 45 ties), 46-54 -> 5, 55-56 -> 6 (55 a tie).
+    With the raw minimum as the zero-point every tie above moves (e.g. 2.125 -> 3).
+    Block 1: 64 x (-0.3): max - min = 0, so s = 0 and every code is 0; z = E4M3(-0.3)
+    = -0.3125 (neighbours 0.28125 and 0.3125 in the binade of spacing 1/32).
+    E4M3 bytes: 1.25 = 0 0111 010 = 0x3A, -1.0 = 1 0111 000 = 0xB8, 0 = 0x00,
+    -0.3125 = 1 0101 010 = 0xAA.
+    """
+    special = np.array([-1.03125, 7.28125, 2.125, 3.375, -0.375, 7.125,
+                        np.float32(-0.375) + np.float32(2.0 ** -25)], np.float32)
+    ramp = (np.float32(-1.0) + np.float32(0.125) * np.arange(57, dtype=np.float32)).astype(np.float32)
+    y = np.empty(128, np.float32)
+    y[:64] = np.concatenate([special, ramp])
+    y[64:] = np.float32(-0.3)
+    codes0 = [0, 7, 2, 4, 0, 6, 0] + [0] * 6 + [1] * 9 + [2] * 11 + [3] * 9 + [4] * 11 + [5] * 9 + [6] * 2
+    codes = codes0 + [0] * 64
+    meta = [[0x3A, 0xB8], [0x00, 0xAA]]
+    return y, codes, meta
+
+
+def test_asym_zero_point_block_by_hand():
+    y, codes, meta_want = asym_pin_block()
+    assert float(y[6]) == -0.375 + 2.0 ** -25        # exact in float32
+    sp = spec(quant="asym", block=64, scale_dtype="e4m3", eps=0.0, rotation="none")
+    u, meta = oracle.quantize_f32(y[None], sp)
+    assert meta.tolist() == [meta_want]
+    assert u[0].tolist() == codes
+    # reconstruction uses the stored pair: s u + z
+    xh = oracle.dequantize(u, meta, sp)[0]
+    assert xh[0] == -1.0 and xh[1] == 7.75 and xh[2] == 1.5 and np.all(xh[64:] == -0.3125)
+
+
 def test_asym_codes_range_and_reconstruction():
     rng = np.random.default_rng(13)
     sp = spec(quant="asym", block=64, scale_dtype="e4m3", eps=0.0)
