@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ p
   for (int c = 1; c < n_cand; ++c) {
     if (err_s[c] < err_s[best]) best = c;
   }
-  if (best == 0) return;
+  // the winner is applied even when it is candidate 0: the interface does not require
+  // candidate 0 to be the identity (when it is, the double products leave R unchanged)
   const float* P = cand_g + 16 * best;
   double* R = rd + 16 * group;
   double rn[16];

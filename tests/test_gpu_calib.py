@@ -67,6 +67,36 @@ def test_so4_calibrate_recovers_planted_rotations():
         assert np.allclose(rot[8 * b + 1], planted[b], atol=1e-6)
 
 
+def test_so4_calibrate_applies_non_identity_candidate_zero():
+    """Candidate 0 need not be the identity: the planted rotations sit at candidate 0
+    of their groups (no identity among those candidates), win, and are applied, as the
+    oracle's search applies every winner."""
+    _need_gpu()
+    import decode_attention_okv_amd as okv
+    d, m, n = 128, 32, 2000
+    rng = np.random.default_rng(11)
+    planted = [oracle.quat_rotation(rng.standard_normal(4), rng.standard_normal(4)) for _ in range(d // m)]
+    g = rng.integers(-3, 4, size=(n, d // m, 4)).astype(np.float64)
+    g[:, :, 0] = 3.0 * np.where(rng.random((n, d // m)) < 0.5, -1.0, 1.0)
+    hx = np.zeros((n, d))
+    for b in range(d // m):
+        grp = 8 * b + 2
+        hx[:, 4 * grp:4 * grp + 4] = (g[:, b] * 0.25) @ planted[b]
+    x = (hx @ oracle.hadamard(d)).astype(np.float32)
+    cand = okv_synth.so4_candidates(d, 1, 4)
+    for b in range(d // m):
+        cand[0, 8 * b + 2, 0] = planted[b]
+    rot0 = np.tile(np.eye(4), (d // 4, 1, 1))
+    say("okv_so4_calibrate non-identity candidate 0")
+    rot, trace = okv.so4_calibrate(torch.from_numpy(x).cuda(), rot0, cand, block=m, bits=3, eps=0.0)
+    rot_o, trace_o, choice = oracle.calibrate_so4(x, rot0, cand, m, 0.0, 3)
+    for b in range(d // m):
+        assert choice[0, 8 * b + 2] == 0
+        assert np.allclose(rot_o[8 * b + 2], planted[b], atol=1e-12)
+    assert np.allclose(rot, rot_o, atol=1e-6)
+    assert np.allclose(trace, trace_o, rtol=2e-5, atol=1e-9 * trace_o[0])
+
+
 # The search runs step k of every quantisation block in one launch: block 4 (one group
 # per block, 32 blocks at once), block = head_dim (one block of 32 or 64 groups), a
 # vector count that leaves a partial chunk, and 70 candidates (two candidate tiles).
