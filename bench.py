@@ -1,22 +1,24 @@
 """Benchmark of the rotated 3-bit KV cache on one MI355X.
 
-A step is one pass of the whole hot path over one batch: okv_write appends one new
-token per sequence (rotate, quantise, pack), then okv_decode_attn attends with one
-query per (sequence, query head) over the whole cache (rotate q, fused unpack /
-scale / dot, online softmax, P.V, split-K reduce, rotate back).  The append may run
-on a second stream, concurrently with the previous step's decode (the warm-up picks
-that schedule or a single stream, whichever is faster; "append_schedule" says which).
+A step is one pass of the whole hot path over one batch, in the order an
+autoregressive decoder runs it: okv_write appends one new token per sequence
+(rotate, quantise, pack), then okv_decode_attn attends with one query per
+(sequence, query head) over the whole cache (rotate q, fused unpack / scale / dot,
+online softmax, P.V, split-K reduce, rotate back).  Both run on one stream, one after
+the other (the next token would depend on this step's output).
 
-Default workload: 7B MHA shape at 128K context (batch 4, 32 heads, d 128,
-131,072 cached tokens per sequence, 8.3 % outlier channels, block 32, fp16 scales).
-Prints one JSON line.  `value` is decode-attention GB/s over the algorithmic bytes
-of the packed cache (codes + scales read, q read, output written), timed over
-whole steps.  A second leg times chunked-prefill attention over the packed cache
-(okv_prefill_attn: the last 2,048 positions of a 32,768-token GQA context attend
-causally) and reports it under "prefill_attn"; "code_widths" times the decode kernel
-at 2- and 4-bit codes on the same workload (the pages' method is 3-bit), and
-"rotations" the unrotated per-token variant and U = B H (SO(4) after the transform);
-"so4_calibration" times the SO(4) calibration search on 16,384 key vectors.
+Default workload: 7B MHA shape at 128K context (batch 4, 32 heads, d 128, 131,072
+cached tokens per sequence, 8.3 % outlier channels, block 32, fp16 scales).  Prints
+one JSON line.  `value` is decode-attention GB/s over the algorithmic bytes of the
+packed cache (codes + scales read, q read, output written), timed over whole serial
+steps (append + decode + merge + launch gaps).  Extra objects on the same line:
+"decode_call" (the decode call alone, back to back), "workloads" (the 70B-shaped
+asymmetric 128K decode, the 32K GQA append-and-decode steps, the SO(4) d = 256
+prefill write and decode, the tiny one-head case), "hbm_read_probe" (a plain
+streaming-read kernel on the same GPU), "prefill_attn" (chunked-prefill attention
+over the packed cache), "code_widths" and "rotations" (2-/4-bit codes, the
+unrotated and SO(4) variants on the headline workload), "so4_calibration" and
+"cpu_baseline" (the CPU oracle on a bounded sample).
 """
 from __future__ import annotations
 
@@ -246,6 +248,204 @@ def cpu_baseline(wl, target_s=12.0):
     }
 
 
+def new_cache(wl, cap, dev, bits=None):
+    import numpy as np
+
+    import decode_attention_okv_amd as okv
+    import okv_synth
+    p32 = okv_synth.rotation_params(wl, dtype=np.float32)
+    return okv.OkvCache(batch=wl.batch, num_q_heads=wl.hq, num_kv_heads=wl.hkv, head_dim=wl.d,
+                        max_tokens=cap, block=wl.block, quant=wl.quant, scale_dtype=wl.scale_dtype,
+                        in_dtype=wl.in_dtype, rotation=wl.rotation, eps=wl.eps, rot_params=p32,
+                        device=dev, bits=wl.bits if bits is None else bits)
+
+
+def timed_prefill(cache, wl, dev):
+    """okv_write of the workload's whole context in one call, timed with events; a
+    first untimed call on the first 32 positions loads the kernel.  Returns ms."""
+    import torch
+
+    import okv_synth
+    k, v = okv_synth.kv_tokens(wl, 0, wl.tokens, device=dev)
+    cache.write(k[:, :32].contiguous(), v[:, :32].contiguous())
+    cache.set_length(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cache.write(k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    del k, v
+    torch.cuda.empty_cache()
+    return e0.elapsed_time(e1)
+
+
+def write_record(wl, ms):
+    """Write-path rates of a prefill of wl.tokens positions per sequence."""
+    pos_s = wl.batch * wl.tokens / (ms * 1e-3)
+    return {"write_prefill_ms": round(ms, 3), "write_tokens_per_s": round(pos_s, 1),
+            "write_head_vectors_per_s": round(pos_s * 2 * wl.hkv, 1),
+            "write_GBs": round(write_bytes_per_position(wl) * wl.tokens / (ms * 1e-3) / 1e9, 1)}
+
+
+def decode_calls(cache, wl, q, out, calls):
+    """`calls` okv_decode_attn calls back to back at the current length: torch events
+    around the loop (whole call: attention + merge + gaps) and the library's HIP events
+    on each kernel's own dispatch.  Returns (call_us, attn_kernel_us, reduce_kernel_us)."""
+    import torch
+    for _ in range(2):
+        cache.decode_attn(q, out)
+    torch.cuda.synchronize()
+    cache.timing(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        cache.decode_attn(q, out)
+    e1.record()
+    torch.cuda.synchronize()
+    n, attn_ms, red_ms = cache.timing_read()
+    cache.timing(False)
+    assert n == calls and torch.isfinite(out).all(), (n, calls)
+    return 1e3 * e0.elapsed_time(e1) / calls, 1e3 * attn_ms / calls, 1e3 * red_ms / calls
+
+
+def decode_record(wl, t, call_us, attn_us, red_us, kernel, splits):
+    cache_b, qb, ob = algorithmic_decode_bytes(wl, t)
+    kern_b = cache_b + qb
+    return {"decode_kernel": kernel, "splits": splits, "context": t,
+            "decode_call_us": round(call_us, 2), "decode_kernel_us": round(attn_us, 2),
+            "reduce_kernel_us": round(red_us, 2),
+            "call_GBs": round((kern_b + ob) / (call_us * 1e-6) / 1e9, 1),
+            "kernel_GBs": round(kern_b / (attn_us * 1e-6) / 1e9, 1),
+            "kernel_frac_hbm_peak": round(kern_b / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "call_frac_hbm_peak": round((kern_b + ob) / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def decode_workload_leg(name, dev, calls=20):
+    """A decode workload at its full size: prefill write (timed), then `calls` decode
+    calls back to back.  Reports write rates, decode call / kernel times, GB/s and the
+    fraction of the HBM peak, and the recorded HBM traffic of the decode kernel."""
+    import torch
+
+    import okv_synth
+    wl = okv_synth.workload(name)
+    print(f"# leg {name}: prefill write", file=sys.stderr, flush=True)
+    cache = new_cache(wl, -(-(wl.tokens + 32) // 32) * 32, dev)
+    ms = timed_prefill(cache, wl, dev)
+    q = okv_synth.queries(wl, 0, device=dev)
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    print(f"# leg {name}: decode x {calls}", file=sys.stderr, flush=True)
+    call_us, attn_us, red_us = decode_calls(cache, wl, q, out, calls)
+    kern = cache.decode_kernel()
+    rec = {"workload": name, "batch": wl.batch, "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.d,
+           "quant": wl.quant, "block": wl.block, "scale_dtype": wl.scale_dtype, "rotation": wl.rotation,
+           **decode_record(wl, wl.tokens, call_us, attn_us, red_us, kern, cache.splits()),
+           "traffic": recorded_traffic(wl, kern), **write_record(wl, ms)}
+    cache.close()
+    del cache, q, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+def steps_leg(name, dev):
+    """The 32K GQA workload as its configuration runs it: prefill write (timed), then
+    wl.decode_steps serial steps of (append one token, decode), timed as a whole."""
+    import torch
+
+    import okv_synth
+    wl = okv_synth.workload(name)
+    n = wl.decode_steps
+    print(f"# leg {name}: prefill write, {n} steps", file=sys.stderr, flush=True)
+    cache = new_cache(wl, -(-(wl.tokens + n + 34) // 32) * 32, dev)
+    ms = timed_prefill(cache, wl, dev)
+    news = [okv_synth.kv_tokens(wl, wl.tokens + i, 1, device=dev, step=i) for i in range(n + 2)]
+    qs = [okv_synth.queries(wl, i, device=dev) for i in range(n + 2)]
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    for i in range(2):                      # warm-up steps (appended tokens stay)
+        cache.write(*news[i])
+        cache.decode_attn(qs[i], out)
+    torch.cuda.synchronize()
+    t_start = cache.length
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(2, n + 2):
+        cache.write(*news[i])
+        cache.decode_attn(qs[i], out)
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    step_ms = e0.elapsed_time(e1) / n
+    byt = sum(sum(algorithmic_decode_bytes(wl, t_start + i + 1)) for i in range(n))
+    call_us, attn_us, red_us = decode_calls(cache, wl, qs[-1], out, 20)
+    rec = {"workload": name, "batch": wl.batch, "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.d,
+           "steps": n, "step_us": round(1e3 * step_ms, 2),
+           "step_GBs": round(byt / (step_ms * 1e-3 * n) / 1e9, 1),
+           **decode_record(wl, cache.length, call_us, attn_us, red_us, cache.decode_kernel(), cache.splits()),
+           "traffic": recorded_traffic(wl, cache.decode_kernel()), **write_record(wl, ms),
+           "note": "the 29 MB cache fits the GPU's last-level cache: not an HBM figure"}
+    cache.close()
+    del cache, news, qs, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+def tiny_leg(dev, reps=20):
+    """The one-head d = 128 case: write its 256 tokens, then one decode; latency of
+    each (median of `reps` repetitions, the cache rewound in between)."""
+    import torch
+
+    import okv_synth
+    wl = okv_synth.workload("tiny_d128_t256")
+    cache = new_cache(wl, 288, dev)
+    k, v = okv_synth.kv_tokens(wl, 0, wl.tokens, device=dev)
+    q = okv_synth.queries(wl, 0, device=dev)
+    out = torch.empty((1, 1, wl.d), dtype=torch.float32, device=dev)
+    wr, dc = [], []
+    for _ in range(reps + 2):
+        cache.set_length(0)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        cache.write(k, v)
+        e[1].record()
+        cache.decode_attn(q, out)
+        e[2].record()
+        torch.cuda.synchronize()
+        wr.append(e[0].elapsed_time(e[1]))
+        dc.append(e[1].elapsed_time(e[2]))
+    cache.close()
+    wr, dc = sorted(wr[2:]), sorted(dc[2:])
+    return {"workload": wl.name, "write_256_us": round(1e3 * wr[len(wr) // 2], 2),
+            "decode_us": round(1e3 * dc[len(dc) // 2], 2), "reps": reps,
+            "note": "latency only (32 KiB cache)"}
+
+
+def read_probe_leg(dev, gib=2, reps=10):
+    """okv_read_probe: a plain streaming-read kernel over `gib` GiB, the HBM read rate
+    a simple kernel reaches on this GPU (best and median of `reps` launches)."""
+    import torch
+
+    import decode_attention_okv_amd as okv
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    okv.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        okv.read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes": n, "launches": reps, "best_GBs": round(n / (ts[0] * 1e-3) / 1e9, 1),
+            "median_GBs": round(n / (ts[len(ts) // 2] * 1e-3) / 1e9, 1),
+            "frac_hbm_peak_best": round(n / (ts[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +454,9 @@ def main():
     ap.add_argument("--workload", default="mha_b4h32_t128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--legs", default="gqa_b16h64kv8_t128k_asym,gqa_h32kv8_t32k,so4_d256_b32_t8k,tiny_d128_t256",
+                    help="other workloads to run at full size ('' to skip)")
+    ap.add_argument("--read-probe", type=int, default=1, help="run the streaming-read probe (0 to skip)")
     ap.add_argument("--prefill-workload", default="gqa_h32kv8_t32k",
                     help="workload of the chunked-prefill attention leg ('' to skip)")
     ap.add_argument("--prefill-rows", type=int, default=2048)
@@ -272,7 +475,6 @@ def main():
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.calib_copy:
@@ -286,116 +488,60 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "copies": 5}))
         return
 
-    import decode_attention_okv_amd as okv
     import okv_synth
 
     wl = okv_synth.workload(args.workload)
     W, K = args.warmup, args.steps
     T0 = wl.tokens
     cap = -(-(T0 + W + K + 1) // 32) * 32
-    p32 = okv_synth.rotation_params(wl, dtype=np.float32)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    cache = okv.OkvCache(batch=wl.batch, num_q_heads=wl.hq, num_kv_heads=wl.hkv, head_dim=wl.d,
-                         max_tokens=cap, block=wl.block, quant=wl.quant, scale_dtype=wl.scale_dtype,
-                         in_dtype=wl.in_dtype, rotation=wl.rotation, eps=wl.eps, rot_params=p32,
-                         device=dev)
+    cache = new_cache(wl, cap, dev)
     if args.splits:
         cache.set_splits(args.splits)
 
-    # ---- prefill (timed separately: okv_write tokens/s).  One untimed prefill loads
-    # the kernels; the cache is then rewound and written again under the timer.
-    k, v = okv_synth.kv_tokens(wl, 0, T0, device=dev)
-    cache.write(k, v)
-    cache.set_length(0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    cache.write(k, v)
-    e1.record()
-    torch.cuda.synchronize()
-    prefill_ms = e0.elapsed_time(e1)
-    del k, v
-    torch.cuda.empty_cache()
+    # ---- prefill (timed separately: okv_write tokens/s)
+    prefill_ms = timed_prefill(cache, wl, dev)
     print(f"# prefill {T0} tokens x {wl.batch} seq: {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
 
-    # ---- decode steps: inputs resident before timing
+    # ---- decode steps: inputs resident before timing.  A step appends one token to
+    # every sequence, then decodes; one stream, in that order.  The library's HIP
+    # events on the attention kernel's own dispatch run during the timed steps, so the
+    # kernel duration behind `roofline` is taken over the same region.
     steps = W + K
     news = [okv_synth.kv_tokens(wl, T0 + i, 1, device=dev, step=i) for i in range(steps)]
     qs = [okv_synth.queries(wl, i, device=dev) for i in range(steps)]
     out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
-    # Two schedules of a step.  "overlapped": the one-token append runs on its own stream,
-    # concurrently with the previous step's decode (the append writes position len only
-    # and rewrites the earlier codes of the current value tile unchanged; the decode
-    # reads positions < len), and the step's decode waits for it.  "serial": both on one
-    # stream.  The overlap hides the append when the GPU is the bottleneck; its extra
-    # event calls cost host time, which bounds short steps.  The warm-up measures the GPU
-    # time of a serial step and the host time to issue an overlapped one, and overlaps
-    # only while the host keeps well ahead of the GPU.  Both streams keep the default
-    # priority.
-    s_main = torch.cuda.current_stream()
-    s_app = torch.cuda.Stream()
-    app_done = [torch.cuda.Event() for _ in range(steps)]
 
-    def step(i, overlapped):
-        if overlapped:
-            cache.write(*news[i], stream=s_app)
-            app_done[i].record(s_app)
-            s_main.wait_event(app_done[i])
-        else:
-            cache.write(*news[i], stream=s_main)
-        cache.decode_attn(qs[i], out, stream=s_main)
+    def step(i):
+        cache.write(*news[i])
+        cache.decode_attn(qs[i], out)
 
-    overlap = False
-    if W >= 4:
-        step(0, False)                  # first uses of both schedules: kernel loading,
-        step(1, True)                   # stream and event set-up
-        half = 2 + (W - 2) // 2
-        torch.cuda.synchronize()
-        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0.record()
-        for i in range(2, half):
-            step(i, False)
-        w1.record()
-        torch.cuda.synchronize()
-        gpu_step_ms = w0.elapsed_time(w1) / (half - 2)
-        h0 = time.perf_counter()
-        for i in range(half, W):
-            step(i, True)
-        host_step_ms = 1e3 * (time.perf_counter() - h0) / (W - half)
-        overlap = host_step_ms < 0.5 * gpu_step_ms
-    else:
-        for i in range(W):
-            step(i, False)
+    for i in range(W):
+        step(i)
     torch.cuda.synchronize()
     splits = cache.splits()
     kernel = cache.decode_kernel()
+    cache.timing(True)
     ts, te = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ts.record()
-    s_app.wait_event(ts)
     for i in range(W, steps):
-        step(i, overlap)
+        step(i)
     te.record()
     torch.cuda.synchronize()
     step_ms_total = ts.elapsed_time(te)
-    assert torch.isfinite(out).all()
-    # attention-kernel duration: K more decode calls back to back at the final
-    # length, with HIP events attached to the kernel's own dispatch
-    t_fin = T0 + steps
-    cache.timing(True)
-    for i in range(K):
-        cache.decode_attn(qs[W + i], out)
-    torch.cuda.synchronize()
     ncalls, attn_ms, red_ms = cache.timing_read()
     cache.timing(False)
     assert ncalls == K, (ncalls, K)
-
+    assert torch.isfinite(out).all()
     lens = [T0 + i + 1 for i in range(W, steps)]
     tot_bytes = sum(sum(algorithmic_decode_bytes(wl, t)) for t in lens)
     value = tot_bytes / (step_ms_total * 1e-3) / 1e9
-    kern_bytes = K * (algorithmic_decode_bytes(wl, t_fin)[0] + algorithmic_decode_bytes(wl, t_fin)[1])
+    kern_bytes = sum(sum(algorithmic_decode_bytes(wl, t)[:2]) for t in lens)
     achieved = kern_bytes / (attn_ms * 1e-3) / 1e9
-    write_tok_s = wl.batch * T0 / (prefill_ms * 1e-3)
+    # the decode call alone, K calls back to back at the final length
+    t_fin = cache.length
+    call_us, c_attn_us, c_red_us = decode_calls(cache, wl, qs[-1], out, K)
 
     res = {
         "metric": METRIC,
@@ -414,14 +560,12 @@ def main():
                    "head_dim": wl.d, "context": T0, "quant": wl.quant, "block": wl.block,
                    "scale_dtype": wl.scale_dtype, "rotation": wl.rotation, "splits": splits},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_schedule": "serial: append 1 token, then decode, one stream",
+        "decode_kernel": kernel,
         "decode_kernel_us": round(1e3 * attn_ms / K, 2),
         "reduce_kernel_us": round(1e3 * red_ms / K, 2),
-        "write_tokens_per_s": round(write_tok_s, 1),
-        "write_head_vectors_per_s": round(write_tok_s * 2 * wl.hkv, 1),
-        "write_prefill_ms": round(prefill_ms, 3),
-        "write_prefill_GBs": round(write_bytes_per_position(wl) * T0 / (prefill_ms * 1e-3) / 1e9, 2),
-        "decode_kernel": kernel,
-        "append_schedule": "overlapped" if overlap else "serial",
+        **write_record(wl, prefill_ms),
+        "decode_call": decode_record(wl, t_fin, call_us, c_attn_us, c_red_us, kernel, cache.splits()),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -434,6 +578,18 @@ def main():
     cache.close()
     del cache, news, qs, out
     torch.cuda.empty_cache()
+    legs = [x for x in args.legs.split(",") if x and x != wl.name]
+    if legs:
+        res["workloads"] = []
+        for name in legs:
+            if name == "gqa_h32kv8_t32k":
+                res["workloads"].append(steps_leg(name, dev))
+            elif name == "tiny_d128_t256":
+                res["workloads"].append(tiny_leg(dev))
+            else:
+                res["workloads"].append(decode_workload_leg(name, dev))
+    if args.read_probe:
+        res["hbm_read_probe"] = read_probe_leg(dev)
     if args.widths:
         res["code_widths"] = [variant_leg(wl, bits=int(b)) for b in args.widths.split(",")]
     if args.rotations:

@@ -21,7 +21,7 @@ __all__ = [
     "okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror", "okv_layout",
     "okv_get_len", "okv_set_len", "okv_set_splits", "okv_get_splits", "okv_max_splits",
     "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel", "okv_get_decode_kernel",
-    "okv_prefill_attn",
+    "okv_prefill_attn", "okv_read_probe", "read_probe",
     "DECODE_KERNEL", "make_config", "OkvCache",
 ]
 
@@ -38,7 +38,7 @@ EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_str
            "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
            "okv_get_splits", "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel",
            "okv_get_decode_kernel", "okv_last_hip_error", "okv_prefill_attn", "okv_so4_calibrate",
-           "okv_so4_eval")
+           "okv_so4_eval", "okv_read_probe")
 
 
 class OkvConfig(ctypes.Structure):
@@ -104,6 +104,7 @@ def _load():
         "okv_get_decode_kernel": (i32, [vp, P(i32)]),
         "okv_so4_calibrate": (i32, [vp, i32, i32, i32, i32, ctypes.c_float, vp, vp, i32, i32, vp, vp]),
         "okv_so4_eval": (i32, [vp, i32, i32, i32, i32, ctypes.c_float, vp, vp, i32, i32, vp, vp]),
+        "okv_read_probe": (i32, [vp, ctypes.c_uint64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(so, name)
@@ -218,6 +219,16 @@ def so4_eval(x, rot, cand, group, block=32, bits=3, eps=1e-6, stream=None):
     _check(okv_so4_eval(x.data_ptr(), n, d, block, bits, eps, r.ctypes.data, c.ctypes.data, c.shape[0], group,
                         err.ctypes.data, stream), "okv_so4_eval")
     return err
+
+
+def okv_read_probe(buf_ptr: int, nbytes: int, sink_ptr: int, stream=None) -> int:
+    return lib.okv_read_probe(ctypes.c_void_p(buf_ptr), nbytes, ctypes.c_void_p(sink_ptr), _stream_ptr(stream))
+
+
+def read_probe(buf, sink, stream=None):
+    """One streaming-read pass over the device tensor buf (okv_read_probe)."""
+    _check(okv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), stream),
+           "okv_read_probe")
 
 
 def okv_destroy(h) -> int:

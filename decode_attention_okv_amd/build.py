@@ -37,6 +37,7 @@ SOURCES = [
     # products are fused only where the source writes fmaf (hi + lo splits stay exact)
     ("okv_prefill.hip", ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("okv_calib.hip", []),
+    ("okv_probe.hip", []),
     ("okv_host.cpp", ["-x", "hip"]),
 ]
 

@@ -67,8 +67,10 @@
  * Errors: every call returns an okv_status.  Arguments are checked before any
  * GPU work is queued; on error nothing is launched and no state changes.  No C++
  * exception crosses this interface.  Calls do not synchronise; they queue work on
- * the given HIP stream (NULL = the default stream).  A handle must be used from
- * one stream at a time.
+ * the given HIP stream (NULL = the default stream).  The host side of a handle is
+ * not thread-safe: call it from one thread at a time.  On the device, calls with one
+ * handle on one stream are ordered; across streams the caller orders them as okv_write
+ * states.
  */
 #ifndef OKV_H
 #define OKV_H
@@ -150,7 +152,11 @@ typedef struct okv_layout_info {
 /* Validate cfg (host only, no GPU touched on failure), copy the rotation
  * parameters to the current device, allocate the split-K workspace there and
  * return a handle with sequence length 0.  The current HIP device at this call is
- * the device of the handle. */
+ * the device of the handle.  The handle fixes U once for every head and token, as
+ * the idea card's Implementation notes draw the signs or SO(4) blocks once and keep
+ * them (and the OIQ report, Section 3.2, generates D once per model); the cache it
+ * describes starts empty, as the append-only key and value caches of those notes do.
+ * *out is NULL on error. */
 int okv_create(const okv_config* cfg, okv_handle** out);
 
 /* Append n_new tokens to every sequence: rotate each new key and value vector by
@@ -158,10 +164,15 @@ int okv_create(const okv_config* cfg, okv_handle** out);
  * len .. len+n_new-1 (the write path of the idea card's Implementation notes).
  * k, v: device, [batch][n_new][kv][d] in the input type, 16-byte aligned.
  * Asynchronous on hip_stream; len advances by n_new at once (host side).
- * It writes positions len .. len+n_new-1 only (and rewrites the earlier codes of the
- * current 32-token value tile unchanged), while okv_decode_attn reads positions below
- * its own len: so a write may run on another stream concurrently with a decode
- * enqueued before it; the next decode must be ordered after the write. */
+ * Ordering: it writes positions len .. len+n_new-1 and rewrites the earlier codes of
+ * the current 32-token value tile unchanged (a read-modify-write of that tile), while
+ * okv_decode_attn reads positions below its own len.  So
+ *   - write after write: every okv_write must be ordered after the handle's previous
+ *     okv_write (same stream, or an event wait): two writes into one value tile are a
+ *     read-modify-write race;
+ *   - write after decode: a write may run on another stream concurrently with a decode
+ *     enqueued before it (the decode never reads the new positions);
+ *   - decode after write: the next decode must be ordered after the write. */
 int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* hip_stream);
 
 /* One decode step: for every (sequence, query head) attend over all len cached
@@ -213,7 +224,12 @@ int okv_so4_eval(const float* x, int32_t n, int32_t head_dim, int32_t block, int
                  const float* rot, const float* cand, int32_t n_cand, int32_t group, double* err,
                  void* hip_stream);
 
-/* Free the handle's device memory (not the caller's buffers).  NULL is OK. */
+/* Release a handle: free its device copy of U and its split-K workspace (not the
+ * caller's cache buffers, which keep the codes written so far).  The end of the
+ * append-only cache's life in the idea card's Implementation notes; nothing of the
+ * method runs here.  Work already queued with the handle must have finished (the call
+ * does not wait for it).  NULL is OK; OKV_E_HIP if a device free fails (the handle is
+ * released anyway). */
 int okv_destroy(okv_handle* h);
 
 /* ---- auxiliary calls (not part of the method) ---- */
@@ -258,6 +274,14 @@ typedef enum okv_decode_kernel {
 } okv_decode_kernel;
 int okv_set_decode_kernel(okv_handle* h, int32_t kind);
 int okv_get_decode_kernel(const okv_handle* h, int32_t* kind);
+
+/* Streaming-read probe: one pass over `bytes` bytes of the device buffer buf with
+ * 16-byte loads (grid-stride over 16 workgroups of 256 threads per compute unit), the
+ * HBM read rate a plain kernel reaches, for comparison with the decode kernels.  buf:
+ * device, 16-byte aligned, bytes >= 16 (the last bytes % 16 are not read); sink:
+ * device uint32, written only when the loads' checksum hits a fixed value (it keeps
+ * the loads from being removed).  Asynchronous on hip_stream; no handle needed. */
+int okv_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* hip_stream);
 
 #ifdef __cplusplus
 }
