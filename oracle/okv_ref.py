@@ -21,7 +21,8 @@ __all__ = [
     "rne_codes", "quantize_f32", "dequantize", "bits_of", "group_bytes",
     "G32_BIT_POSITIONS", "group_bit_positions", "pack_g32", "unpack_g32", "pack_rows", "unpack_rows",
     "pack_vtiles", "unpack_vtiles",
-    "write_unit", "meta_values", "attend_unit", "attend_exact", "attend_prefill_unit",
+    "write_unit", "meta_values", "attend_unit", "attend_unit_lengths", "attend_exact",
+    "attend_prefill_unit",
     "gini", "channel_gini", "block_max_stats", "attention_rel_rmse",
 ]
 
@@ -497,6 +498,26 @@ def attend_unit(q, k_codes, k_meta, v_codes, v_meta, t: int, spec, u_mat) -> np.
     q1 = np.asarray(q, dtype=np.float64) @ u_mat.T          # rows of U q
     y1 = attend_exact(q1, k_hat, v_hat)
     return y1 @ u_mat                                       # rows of U^T y1
+
+
+def attend_unit_lengths(queries, k_codes, k_meta, v_codes, v_meta, spec, u_mat) -> list:
+    """Decode attention of one KV head at several cache lengths: queries is a list of
+    (t, q) with q (G, d) the query heads of a decode step that saw t cached tokens.
+    Each entry is attend_unit(q, ..., t, ...): the read path of the idea card's
+    Implementation notes over tokens 0 .. t-1 (the cache is append-only, so a step at
+    length t reads the first t tokens of the final cache).  The cache is decoded once.
+    Returns a list of (G, d) float64 arrays."""
+    if not queries:
+        return []
+    d, b = spec.d, bits_of(spec)
+    t_max = max(int(t) for t, _ in queries)
+    k_hat = dequantize(unpack_rows(np.asarray(k_codes)[:t_max], d, b), np.asarray(k_meta)[:t_max], spec)
+    v_hat = dequantize(unpack_vtiles(v_codes, t_max, b), np.asarray(v_meta)[:t_max], spec)
+    outs = []
+    for t, q in queries:
+        q1 = np.asarray(q, dtype=np.float64) @ u_mat.T
+        outs.append(attend_exact(q1, k_hat[:int(t)], v_hat[:int(t)]) @ u_mat)
+    return outs
 
 
 def attend_prefill_unit(q, positions, k_codes, k_meta, v_codes, v_meta, spec, u_mat) -> np.ndarray:

@@ -65,22 +65,9 @@ def compare_unit(cache, wl, b, h, t, ref):
 
 
 def exact_ties(ref, wl):
-    """Number of rotated values that lie exactly on a rounding threshold of their
-    stored scale (the oracle's own count; reported, expected ~0)."""
-    n = 0
-    for key, mkey in (("k_rot", "k_meta"), ("v_rot", "v_meta")):
-        y = ref[key].astype(np.float64)
-        s, off = oracle.meta_values(ref[mkey], wl)
-        t, d = y.shape
-        yb = y.reshape(t, d // wl.block, wl.block)
-        if wl.quant == "sym":
-            q = yb / s[..., None]
-        else:
-            q = (yb.astype(np.float32) - off[..., None].astype(np.float32)).astype(np.float64) / s[..., None]
-        with np.errstate(invalid="ignore", divide="ignore"):
-            frac = q - np.floor(q)
-        n += int(np.count_nonzero(frac == 0.5))
-    return n
+    """Number of rotated values on an exact rounding threshold (oracle_pool.exact_ties)."""
+    from oracle_pool import exact_ties as _ties
+    return _ties(ref, wl)
 
 
 def decode_ref_unit(wl, q_host, b, hk, ref, t, u):

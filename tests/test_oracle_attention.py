@@ -126,3 +126,28 @@ def test_attend_prefill_first_position_is_its_own_value():
     y = oracle.attend_prefill_unit(q, [0, 0, 0], c["k_codes"], c["k_meta"], c["v_codes"], c["v_meta"], wl, u)
     v0 = oracle.dequantize(c["v_u"][:1], c["v_meta"][:1], wl)[0] @ u
     assert np.abs(y[:, 0] - v0).max() <= 1e-13 * np.abs(v0).max()
+
+
+def test_attend_unit_lengths_equals_attend_unit_per_length():
+    # several cache lengths from one decoded cache: each equals the one-length read
+    # path over the first t tokens, and the shortest equals torch SDPA on the
+    # un-rotated dequantised prefix
+    import torch
+    rng = np.random.default_rng(41)
+    sp = SimpleNamespace(d=128, block=32, quant="sym", scale_dtype="f16", eps=1e-6, rotation="sign")
+    p32 = np.where(rng.random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    u = oracle.rotation_matrix("sign", p32.astype(np.float64), 128)
+    k = rng.standard_normal((77, 128)).astype(np.float32)
+    v = rng.standard_normal((77, 128)).astype(np.float32)
+    ref = oracle.write_unit(k, v, sp, p32)
+    qs = [(t, rng.standard_normal((3, 128)).astype(np.float32)) for t in (1, 31, 32, 33, 77)]
+    got = oracle.attend_unit_lengths(qs, ref["k_codes"], ref["k_meta"], ref["v_codes"], ref["v_meta"], sp, u)
+    for (t, q), y in zip(qs, got):
+        want = oracle.attend_unit(q, ref["k_codes"], ref["k_meta"], ref["v_codes"], ref["v_meta"], t, sp, u)
+        assert np.array_equal(y, want)
+    t, q = qs[2]
+    kx = oracle.dequantize(ref["k_u"][:t], ref["k_meta"][:t], sp) @ u          # U^T k_hat, as rows
+    vx = oracle.dequantize(ref["v_u"][:t], ref["v_meta"][:t], sp) @ u
+    sd = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None], torch.from_numpy(kx)[None], torch.from_numpy(vx)[None])[0]
+    assert np.allclose(got[2], sd.numpy(), atol=1e-10)
