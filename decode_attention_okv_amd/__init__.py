@@ -21,7 +21,7 @@ __all__ = [
     "okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_strerror", "okv_layout",
     "okv_get_len", "okv_set_len", "okv_set_splits", "okv_get_splits", "okv_max_splits",
     "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel", "okv_get_decode_kernel",
-    "okv_prefill_attn", "okv_read_probe", "read_probe",
+    "okv_prefill_attn", "okv_read_probe", "read_probe", "okv_decode_attn_noalloc",
     "DECODE_KERNEL", "make_config", "OkvCache",
 ]
 
@@ -38,7 +38,7 @@ EXPORTS = ("okv_create", "okv_write", "okv_decode_attn", "okv_destroy", "okv_str
            "okv_layout", "okv_get_len", "okv_set_len", "okv_set_splits", "okv_max_splits",
            "okv_get_splits", "okv_timing_enable", "okv_timing_read", "okv_set_decode_kernel",
            "okv_get_decode_kernel", "okv_last_hip_error", "okv_prefill_attn", "okv_so4_calibrate",
-           "okv_so4_eval", "okv_read_probe")
+           "okv_so4_eval", "okv_read_probe", "okv_decode_attn_noalloc")
 
 
 class OkvConfig(ctypes.Structure):
@@ -88,6 +88,7 @@ def _load():
         "okv_create": (i32, [P(OkvConfig), P(vp)]),
         "okv_write": (i32, [vp, vp, vp, i32, vp]),
         "okv_decode_attn": (i32, [vp, vp, vp, vp]),
+        "okv_decode_attn_noalloc": (i32, [vp, vp, vp, vp]),
         "okv_prefill_attn": (i32, [vp, vp, i32, vp, vp]),
         "okv_destroy": (i32, [vp]),
         "okv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -161,6 +162,10 @@ def okv_write(h, k_ptr: int, v_ptr: int, n_new: int, stream=None) -> int:
 
 def okv_decode_attn(h, q_ptr: int, out_ptr: int, stream=None) -> int:
     return lib.okv_decode_attn(h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(out_ptr), _stream_ptr(stream))
+
+
+def okv_decode_attn_noalloc(h, q_ptr: int, out_ptr: int, stream=None) -> int:
+    return lib.okv_decode_attn_noalloc(h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(out_ptr), _stream_ptr(stream))
 
 
 def okv_prefill_attn(h, q_ptr: int, n_q: int, out_ptr: int, stream=None) -> int:

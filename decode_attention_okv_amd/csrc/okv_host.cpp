@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -94,6 +95,40 @@ struct TimingSlot {
 
 }  // namespace
 
+// ---- static split-K scratch of okv_decode_attn_noalloc
+//
+// A file-scope device array: each GPU the library runs on holds its own copy (from the
+// code object's load until the process ends).  In host code `g_scratch` is only a
+// host-side stand-in for the symbol, never a device address: the device address of a
+// GPU's copy is looked up once per device (scratch_setup, from okv_create with that
+// device current) and kept in g_scratch_ptr; kernels receive that pointer.
+namespace {
+constexpr size_t kScratchBytes = size_t{16} << 20;   // 16 MiB per GPU
+constexpr size_t kScratchFloats = kScratchBytes / sizeof(float);
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) float g_scratch[kScratchFloats];
+
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+
+// Look up the device address of the scratch on `device` (the current device), once.
+void scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::call_once(g_scratch_once[device], [device] {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_scratch));
+    g_scratch_err[device] = e;
+    if (e == hipSuccess) g_scratch_ptr[device] = static_cast<float*>(p);
+  });
+}
+
+}  // namespace
+
 struct okv_handle {
   okv_config cfg;
   int device = 0;
@@ -151,6 +186,53 @@ void free_timing(okv_handle* h) {
   }
   h->slots.clear();
   h->recorded = 0;
+}
+
+// One decode call (attention kernel + split merge) with the split partials in `ws`
+// (B x Hq x nsplit x (d + 2) floats); arguments already checked.
+int decode_launch(okv_handle* h, const void* q, float* out, hipStream_t s, float* ws) {
+  const okv_config& c = h->cfg;
+  const int nsplit = choose_splits(h, h->len);
+  okv::DecodeParams p{};
+  p.k_codes = static_cast<const uint8_t*>(c.k_codes);
+  p.v_codes = static_cast<const uint8_t*>(c.v_codes);
+  p.k_meta = c.k_meta;
+  p.v_meta = c.v_meta;
+  p.q = q;
+  p.rot = h->d_rot;
+  p.ws = ws;
+  p.hq = c.num_q_heads;
+  p.hkv = c.num_kv_heads;
+  p.tcap = c.max_tokens;
+  p.ntile_cap = c.max_tokens / okv::kTile;
+  p.T = h->len;
+  p.nsplit = nsplit;
+  p.block = c.block;
+  p.quant = c.quant;
+  p.scale_dtype = c.scale_dtype;
+  p.rotation = c.rotation;
+  p.in_bf16 = c.in_dtype == OKV_DT_BF16;
+  p.bits = c.bits;
+  okv::ReduceParams r{};
+  r.ws = ws;
+  r.rot = h->d_rot;
+  r.out = out;
+  r.hq = c.num_q_heads;
+  r.nsplit = nsplit;
+  r.rotation = c.rotation;
+  if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
+  TimingSlot* ts = nullptr;
+  if (h->timing && h->recorded < static_cast<int>(h->slots.size())) ts = &h->slots[h->recorded++];
+  const hipError_t le = decode_kernel_of(h) == OKV_DECODE_GROUPED
+                           ? okv::launch_decode_grouped(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
+                                                        ts ? ts->e1 : nullptr)
+                           : okv::launch_decode_head(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
+                                                     ts ? ts->e1 : nullptr);
+  if (!hip_ok(le)) return OKV_E_HIP;
+  if (!hip_ok(okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr))) {
+    return OKV_E_HIP;
+  }
+  return OKV_OK;
 }
 
 }  // namespace
@@ -219,6 +301,9 @@ int okv_create(const okv_config* cfg, okv_handle** out) {
     delete h;
     return OKV_E_HIP;
   }
+  // set-up of okv_decode_attn_noalloc: the scratch's address on this device, once per
+  // device (a failure is reported by that call, not here)
+  scratch_setup(h->device);
   const size_t ws_floats = static_cast<size_t>(cfg->batch) * cfg->num_q_heads * kMaxSplits * (d + 2);
   if (!hip_ok(hipMalloc(&h->d_rot, nrot * sizeof(float))) ||
       !hip_ok(hipMemcpy(h->d_rot, rp, nrot * sizeof(float), hipMemcpyHostToDevice)) ||
@@ -287,49 +372,24 @@ int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream) 
   if (h == nullptr || q == nullptr || out == nullptr) return OKV_E_INVALID;
   if (!aligned16(q) || !aligned16(out)) return OKV_E_ALIGN;
   if (h->len < 1) return OKV_E_INVALID;
+  return decode_launch(h, q, out, static_cast<hipStream_t>(hip_stream), h->d_ws);
+}
+
+int okv_decode_attn_noalloc(okv_handle* h, const void* q, float* out, void* hip_stream) {
+  if (h == nullptr || q == nullptr || out == nullptr) return OKV_E_INVALID;
+  if (!aligned16(q) || !aligned16(out)) return OKV_E_ALIGN;
+  if (h->len < 1) return OKV_E_INVALID;
   const okv_config& c = h->cfg;
-  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const int nsplit = choose_splits(h, h->len);
-  okv::DecodeParams p{};
-  p.k_codes = static_cast<const uint8_t*>(c.k_codes);
-  p.v_codes = static_cast<const uint8_t*>(c.v_codes);
-  p.k_meta = c.k_meta;
-  p.v_meta = c.v_meta;
-  p.q = q;
-  p.rot = h->d_rot;
-  p.ws = h->d_ws;
-  p.hq = c.num_q_heads;
-  p.hkv = c.num_kv_heads;
-  p.tcap = c.max_tokens;
-  p.ntile_cap = c.max_tokens / okv::kTile;
-  p.T = h->len;
-  p.nsplit = nsplit;
-  p.block = c.block;
-  p.quant = c.quant;
-  p.scale_dtype = c.scale_dtype;
-  p.rotation = c.rotation;
-  p.in_bf16 = c.in_dtype == OKV_DT_BF16;
-  p.bits = c.bits;
-  okv::ReduceParams r{};
-  r.ws = h->d_ws;
-  r.rot = h->d_rot;
-  r.out = out;
-  r.hq = c.num_q_heads;
-  r.nsplit = nsplit;
-  r.rotation = c.rotation;
-  if (!hip_ok(hipSetDevice(h->device))) return OKV_E_HIP;
-  TimingSlot* ts = nullptr;
-  if (h->timing && h->recorded < static_cast<int>(h->slots.size())) ts = &h->slots[h->recorded++];
-  const hipError_t le = decode_kernel_of(h) == OKV_DECODE_GROUPED
-                           ? okv::launch_decode_grouped(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
-                                                        ts ? ts->e1 : nullptr)
-                       : okv::launch_decode_head(p, c.batch, c.head_dim, s, ts ? ts->e0 : nullptr,
-                                                 ts ? ts->e1 : nullptr);
-  if (!hip_ok(le)) return OKV_E_HIP;
-  if (!hip_ok(okv::launch_reduce(r, c.batch, c.head_dim, s, ts ? ts->e2 : nullptr, ts ? ts->e3 : nullptr))) {
+  const size_t need = static_cast<size_t>(c.batch) * c.num_q_heads * choose_splits(h, h->len) *
+                      (static_cast<size_t>(c.head_dim) + 2);
+  if (need > kScratchFloats) return OKV_E_CAPACITY;
+  if (h->device < 0 || h->device >= kMaxDevices) return OKV_E_UNSUPPORTED;
+  float* ws = g_scratch_ptr[h->device];
+  if (ws == nullptr) {
+    g_last_hip = g_scratch_err[h->device] != hipSuccess ? g_scratch_err[h->device] : hipErrorInvalidSymbol;
     return OKV_E_HIP;
   }
-  return OKV_OK;
+  return decode_launch(h, q, out, static_cast<hipStream_t>(hip_stream), ws);
 }
 
 int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void* hip_stream) {

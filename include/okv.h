@@ -182,6 +182,20 @@ int okv_write(okv_handle* h, const void* k, const void* v, int32_t n_new, void* 
  * cache is empty.  Asynchronous on hip_stream. */
 int okv_decode_attn(okv_handle* h, const void* q, float* out, void* hip_stream);
 
+/* okv_decode_attn without any device allocation, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and split count, the same output bit for bit, but the split-K
+ * partials go to a static device scratch of 16 MiB (4,194,304 floats) that the library
+ * holds on each GPU it runs on until the process ends, instead of the handle's
+ * workspace.  It needs batch * num_q_heads * splits * (head_dim + 2) floats (splits:
+ * okv_get_splits); beyond 16 MiB it returns OKV_E_CAPACITY and launches nothing.  The
+ * scratch's address on a device is looked up by okv_create on that device; OKV_E_HIP if
+ * that failed.  Every call on one GPU shares that GPU's scratch and leaves the last
+ * call's partials in it: calls of this function that overlap on one GPU (other streams,
+ * other handles, other threads) race and must be ordered by the caller.  Arguments and
+ * the other errors as okv_decode_attn. */
+int okv_decode_attn_noalloc(okv_handle* h, const void* q, float* out, void* hip_stream);
+
 /* Prefill attention: the last n_q cached positions of every sequence (len - n_q ..
  * len - 1, already appended by okv_write) attend causally over the cache: the row at
  * position p sees tokens 0 .. p, its own included.  Each row is the read path of
