@@ -289,19 +289,24 @@ def write_record(wl, ms):
 
 
 def decode_calls(cache, wl, q, out, calls):
-    """`calls` okv_decode_attn calls back to back at the current length: torch events
-    around the loop (whole call: attention + merge + gaps) and the library's HIP events
-    on each kernel's own dispatch.  Returns (call_us, attn_kernel_us, reduce_kernel_us)."""
+    """`calls` okv_decode_attn calls back to back at the current length, twice: bare,
+    with torch events around the loop (whole call: attention + merge + gaps), then with
+    the library's HIP events on each kernel's own dispatch (kernel durations; those
+    events add launch gaps, so they stay out of the first loop).  Returns (call_us,
+    attn_kernel_us, reduce_kernel_us)."""
     import torch
     for _ in range(2):
         cache.decode_attn(q, out)
     torch.cuda.synchronize()
-    cache.timing(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(calls):
         cache.decode_attn(q, out)
     e1.record()
+    torch.cuda.synchronize()
+    cache.timing(True)
+    for _ in range(calls):
+        cache.decode_attn(q, out)
     torch.cuda.synchronize()
     n, attn_ms, red_ms = cache.timing_read()
     cache.timing(False)
@@ -493,7 +498,7 @@ def main():
     wl = okv_synth.workload(args.workload)
     W, K = args.warmup, args.steps
     T0 = wl.tokens
-    cap = -(-(T0 + W + K + 1) // 32) * 32
+    cap = -(-(T0 + W + 2 * K + 1) // 32) * 32
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     cache = new_cache(wl, cap, dev)
@@ -505,10 +510,12 @@ def main():
     print(f"# prefill {T0} tokens x {wl.batch} seq: {prefill_ms:.3f} ms", file=sys.stderr, flush=True)
 
     # ---- decode steps: inputs resident before timing.  A step appends one token to
-    # every sequence, then decodes; one stream, in that order.  The library's HIP
-    # events on the attention kernel's own dispatch run during the timed steps, so the
-    # kernel duration behind `roofline` is taken over the same region.
-    steps = W + K
+    # every sequence, then decodes; one stream, in that order.  Two timed regions of K
+    # steps each: the first, bare, gives `value`; the second runs the same steps with the
+    # library's HIP events attached to each kernel's own dispatch, which give the
+    # attention kernel's duration behind `roofline` (those events add launch gaps of
+    # several microseconds around the kernels, so they stay out of the first region).
+    steps = W + 2 * K
     news = [okv_synth.kv_tokens(wl, T0 + i, 1, device=dev, step=i) for i in range(steps)]
     qs = [okv_synth.queries(wl, i, device=dev) for i in range(steps)]
     out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
@@ -522,22 +529,30 @@ def main():
     torch.cuda.synchronize()
     splits = cache.splits()
     kernel = cache.decode_kernel()
-    cache.timing(True)
     ts, te = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ts.record()
-    for i in range(W, steps):
+    for i in range(W, W + K):
         step(i)
     te.record()
     torch.cuda.synchronize()
     step_ms_total = ts.elapsed_time(te)
+    assert torch.isfinite(out).all()
+    cache.timing(True)
+    t2s, t2e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t2s.record()
+    for i in range(W + K, steps):
+        step(i)
+    t2e.record()
+    torch.cuda.synchronize()
     ncalls, attn_ms, red_ms = cache.timing_read()
     cache.timing(False)
     assert ncalls == K, (ncalls, K)
     assert torch.isfinite(out).all()
-    lens = [T0 + i + 1 for i in range(W, steps)]
+    lens = [T0 + i + 1 for i in range(W, W + K)]
     tot_bytes = sum(sum(algorithmic_decode_bytes(wl, t)) for t in lens)
     value = tot_bytes / (step_ms_total * 1e-3) / 1e9
-    kern_bytes = sum(sum(algorithmic_decode_bytes(wl, t)[:2]) for t in lens)
+    lens2 = [T0 + i + 1 for i in range(W + K, steps)]
+    kern_bytes = sum(sum(algorithmic_decode_bytes(wl, t)[:2]) for t in lens2)
     achieved = kern_bytes / (attn_ms * 1e-3) / 1e9
     # the decode call alone, K calls back to back at the final length
     t_fin = cache.length
@@ -564,6 +579,7 @@ def main():
         "decode_kernel": kernel,
         "decode_kernel_us": round(1e3 * attn_ms / K, 2),
         "reduce_kernel_us": round(1e3 * red_ms / K, 2),
+        "ms_per_step_with_kernel_events": round(t2s.elapsed_time(t2e) / K, 4),
         **write_record(wl, prefill_ms),
         "decode_call": decode_record(wl, t_fin, call_us, c_attn_us, c_red_us, kernel, cache.splits()),
         "roofline": {

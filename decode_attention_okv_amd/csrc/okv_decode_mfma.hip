@@ -6,16 +6,18 @@
 //  * Q.K as C = Q K^T: A = 16 rows (head h, block b) holding one int8 digit of q_h
 //    restricted to block b (zero elsewhere), B = key codes of 16 tokens (columns) x 64
 //    dims.  A lane decodes one whole 32-code key group and feeds two instructions; the
-//    (head, block) rows keep the per-block scales separable.  Three instruction
+//    (head, block) rows keep the per-block scales separable.  A query group with more
+//    than 16 (head, block) pairs per 128-dim quad takes several 16-row sets (G = 8 with
+//    blocks of 32: two sets); a smaller one leaves rows zero.  Three instruction
 //    chains take the three balanced digits of the 24-bit fixed-point query and
 //    combine exactly in int32.  Each lane ends with whole logits (every block of its
 //    heads) of four consecutive tokens, so the softmax runs once per (token, head).
-//  * P.V: A = the step's weights p s as 21-bit integers in three balanced int8 digits, rows
-//    (head, block); B = value codes of 64 tokens x 16 dims, decoded once per step
-//    into LDS; C = int32 [rows x dims].  Only rows whose block holds the 16 dims are
-//    kept, scaled back to float once per step.  The C rows a lane keeps are the
-//    (head, block) rows whose weights it made, so the per-row scale and the softmax
-//    rescaling stay in registers.
+//  * P.V: the step's weights p s of each (head, block) row become 21-bit integers in
+//    three balanced int8 digit planes in LDS.  A = rows (head, digit) of one block:
+//    instruction i takes heads 4 i .. 4 i + 3, row 4 hh + d holding digit d of head
+//    4 i + hh; B = value codes of 64 tokens x 16 dims of that block, decoded once per
+//    step into LDS; C = int32, so lane (dim j, lq) holds the three digit sums of head
+//    4 i + lq and combines them exactly, then scales back to float once per step.
 //
 // Block metadata is decoded once per (token, block) into LDS as floats.  With the
 // asymmetric quantiser the zero-point enters directly (s u + z); with the symmetric
@@ -81,9 +83,14 @@ __device__ __forceinline__ void digits_q(int q, int& hi, int& mi, int& lo) {
   hi = (q2 - mi) >> 8;
 }
 
-template <int MDW>
+// A token's metadata row of MDB bytes (2, 4, 8 or a multiple of 16) into dwords (a
+// 2-byte row goes to the low half of w[0]).
+template <int MDB>
 __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
-  if constexpr (MDW == 1) {
+  constexpr int MDW = MDB / 4;
+  if constexpr (MDB == 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else if constexpr (MDW == 1) {
     w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   } else if constexpr (MDW == 2) {
     const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
@@ -124,62 +131,92 @@ struct StepRaw {
   uint32_t vm[MDW];       // value metadata row of token `lane`
 };
 
-// Resident waves per SIMD the register allocation aims for: four where the LDS
-// footprint (<= 40 KB) lets four workgroups share a CU (d = 128, b <= 3, except the
-// float32 and E4M3 metadata rows of 32-blocks), else no constraint.  The kernel streams
-// one step ahead per wave, so resident waves set the bytes in flight.
-template <int D, int FMT, int BLOCK, int BITS>
-constexpr int kWavesPerEu = (D == 128 && BITS <= 3 && !(BLOCK == 32 && FMT != kFmtSymF16)) ? 4 : 1;
+// Static shape of the grouped kernel for head dim D, quantisation block BLOCK and query
+// group G.  Q.K runs per 128-dim quad on 16-row sets of (head, block) pairs; P.V runs on
+// (head, digit) rows, four heads per instruction.
+template <int D, int FMT, int BLOCK, int G, int BITS>
+struct GroupShape {
+  static constexpr int NQ = D / 128;              // 128-dim quads
+  static constexpr int BPQ = 128 / BLOCK;         // quantisation blocks per quad (4, 2, 1)
+  static constexpr int NBLK = D / BLOCK;
+  static constexpr int ROWS = G * BPQ;            // (head, block) rows per quad
+  static constexpr int S = (ROWS + 15) / 16;      // 16-row sets
+  static constexpr int HPL = 4 / BPQ;             // heads per lane and set (C rows 4 lq .. 4 lq + 3)
+  static constexpr int NI = (G + 3) / 4;          // P.V instructions per 16 dims (4 heads x 3 digits)
+  static constexpr int NBPB = 8 / BPQ;            // 16-dim output blocks per quantisation block
+  static constexpr bool ASYM = FMT == kFmtAsym;
+  static constexpr int NS = ASYM ? 2 : 1;         // decoded metadata floats per entry: s (, z)
+  static constexpr int MST = ASYM ? 72 : 80;      // padded LDS row of one block's metadata
+  static constexpr int MSZ = FMT == kFmtSymF32 ? 4 : 2;   // bytes per decoded metadata value
+  static constexpr int UB0 = 4 * 64 * 64;         // per-wave value rows of half a quad
+  static constexpr int UB1 = 4 * G * D * 4;       // wave partials in the final combine
+  static constexpr int UB2 = G * D * 7;           // prologue: q1 floats and digits
+  static constexpr int UB = UB0 > UB1 ? (UB0 > UB2 ? UB0 : UB2) : (UB1 > UB2 ? UB1 : UB2);
+  // LDS of one workgroup (bytes): value rows / prologue / partials, weight digits, block
+  // metadata, Q operands, small per-head arrays
+  static constexpr int LDS = UB + 4 * NQ * S * 3 * 16 * 64 + 4 * 2 * NBLK * NS * MST * MSZ +
+                             NQ * S * 2 * 3 * 64 * 16 + 4 * NQ * S * 16 * 4 + 52 * G + 32 * G * NBLK;
+};
+
+// Resident waves per SIMD the register allocation aims for at d = 128 and b <= 3: as
+// many workgroups as the LDS footprint lets share a CU, up to four with blocks of 32
+// dims and three with wider blocks (whose lanes keep two or four heads' rows live: at
+// four waves, 128 registers, they spill loop-invariant values and run slower).  At
+// d = 256 and b = 4, no constraint.  The kernel streams one step ahead per wave, so
+// resident waves set the bytes in flight.
+template <int D, int FMT, int BLOCK, int G, int BITS>
+constexpr int waves_per_eu() {
+  using SH = GroupShape<D, FMT, BLOCK, G, BITS>;
+  if (D != 128 || BITS > 3) return 1;
+  const int wg = (160 * 1024) / SH::LDS;
+  const int cap = BLOCK == 32 ? 4 : 3;
+  return wg >= cap ? cap : (wg >= 1 ? wg : 1);
+}
 
 // One workgroup = one (split, KV head, sequence) and all G query heads of that KV
 // head; its four waves take the split's 64-token steps in turn.
 template <int D, int FMT, int BLOCK, int G, int BITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<D, FMT, BLOCK, BITS>)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, FMT, BLOCK, G, BITS>())))
 void decode_grouped_kernel(const DecodeParams p) {
-  constexpr int NQ = D / 128;          // quads of four 32-dim groups (128 dims each)
-  constexpr int BPQ = 128 / BLOCK;     // quantisation blocks per quad
-  constexpr int NBLK = D / BLOCK;
-  static_assert(G * BPQ == 16, "one 16-row (head, block) set per quad");
-  constexpr int ROWB = BITS * D / 8;    // bytes per key row
+  using SH = GroupShape<D, FMT, BLOCK, G, BITS>;
+  constexpr int NQ = SH::NQ, BPQ = SH::BPQ, NBLK = SH::NBLK, ROWS = SH::ROWS, S = SH::S, HPL = SH::HPL;
+  constexpr int NI = SH::NI, NBPB = SH::NBPB, NS = SH::NS, MST = SH::MST, UB = SH::UB;
+  constexpr bool ASYM = SH::ASYM;
+  static_assert(BPQ >= 1 && BPQ <= 4 && G >= 2, "blocks of 32 .. 128 dims, query groups of two or more");
+  constexpr int ROWB = BITS * D / 8;   // bytes per key row
   constexpr int GB = 4 * BITS;         // bytes per 32-code group
   constexpr int EXC = 1 << (BITS - 1); // excess of symmetric codes
   constexpr int MB = FMT == kFmtSymF32 ? 4 : 2;      // bytes per metadata entry
-  constexpr int MDW = NBLK * MB / 4;                 // metadata dwords per token
+  constexpr int MDB = NBLK * MB;                     // metadata bytes per token (2 .. 64)
+  constexpr int MDW = (MDB + 3) / 4;                 // metadata dwords per token
   constexpr int NBQ = 8;               // 16-dim output blocks per quad
   constexpr int DPL = D / 64;          // value groups per lane and tile
-  constexpr int HPL = 4 / BPQ;         // heads per lane (C rows 4 lq .. 4 lq + 3)
   constexpr int NU = G * D / 256;      // query elements per thread in the prologue
+  constexpr int SPAN = BLOCK < 64 ? BLOCK : 64;      // lanes of one block inside a wave
   // fixed-point limit that keeps every int32 block sum exact (see q_limit)
-  constexpr int QMAX = q_limit(BLOCK, code_max(FMT == kFmtAsym, BITS));
-  constexpr int WMAX = w_limit(code_max(FMT == kFmtAsym, BITS), kW7);
-  constexpr int UB0 = 4 * 64 * 64;     // per-wave value rows of half a quad
-  constexpr int UB1 = 4 * G * D * 4;   // wave partials in the final combine
-  constexpr int UB = UB0 > UB1 ? UB0 : UB1;
-  static_assert(G * D * 7 <= UB, "prologue buffers fit the shared region");
-  constexpr bool ASYM = FMT == kFmtAsym;
-  constexpr int NS = ASYM ? 2 : 1;     // decoded metadata floats per entry: s (, z)
-  // padded LDS row of one block's metadata floats: consecutive blocks start 16 banks
-  // apart, so the four-token reads of a quad's blocks never share a bank
-  constexpr int MST = ASYM ? 72 : 80;
-  // E4M3 and fp16 scales are exact in float16: half-size metadata rows (the smaller
-  // LDS footprint lets three workgroups share a CU)
+  constexpr int QMAX = q_limit(BLOCK, code_max(ASYM, BITS));
+  constexpr int WMAX = w_limit(code_max(ASYM, BITS), kW7);
+  static_assert(NU >= 1 && G * D % 256 == 0, "prologue: whole waves per head");
+  // E4M3 and fp16 scales are exact in float16: half-size metadata rows
   using MT = typename std::conditional<FMT == kFmtSymF32, float, _Float16>::type;
   using Raw = StepRaw<NQ, DPL, MDW, BITS>;
 
   // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
   __shared__ __align__(16) uint8_t u_s[UB];
-  // weight digits per row; row r is stored at wrow(r), which moves the four rows r with
-  // the same r % 4 (written by one instruction from the four lane rows) to different banks
-  __shared__ __align__(16) uint8_t wq_s[4][NQ][3][16][kStep];
+  // weight digit planes per (quad, row set, digit): 16 (head, block) rows of 64 tokens;
+  // row r is stored at wrow(r), which moves the four rows r with the same r % 4 (written
+  // by one instruction from the four lane rows) to different banks
+  __shared__ __align__(16) uint8_t wq_s[4][NQ][S][3][16][kStep];
   __shared__ __align__(16) MT mf_s[4][2][NBLK][NS][MST];        // [key/value][block][s, z][token]
+  // Q operands (the same for every wave, indexed by lane; in registers they would cost
+  // resident waves)
+  __shared__ __align__(16) v4i qbs_s[NQ][S][2][3][64];
+  __shared__ __align__(16) float wsg_s[4][NQ][16 * S];          // weight scale per (head, block) row
+  __shared__ float alpha_s[4][G];                                // softmax rescaling per head
   __shared__ float cm_s[4][G], cl_s[4][G];
   __shared__ float cob_s[4][G][NBLK];
   __shared__ int32_t qds_s[G][NBLK][4];              // per (head, block): sum q, hi, mid, lo
   __shared__ uint32_t qam_s[G];                      // per head: max |q1| (float bits)
-  // The Q operands wait in LDS (in registers they would cost a resident wave per SIMD);
-  // the same for every wave, indexed by lane
-  constexpr bool QB_LDS = true;
-  __shared__ __align__(16) v4i qbs_s[QB_LDS ? NQ : 1][2][3][64];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y;
@@ -201,6 +238,7 @@ void decode_grouped_kernel(const DecodeParams p) {
     q_s[e / D][jd] = x;
   }
   if (tid < G) qam_s[tid] = 0u;
+  for (int e = tid; e < G * NBLK * 4; e += 256) (&qds_s[0][0][0])[e] = 0;
   __syncthreads();
   for (int hs = 1; hs < D && p.rotation != kRotNone; hs <<= 1) {   // U = I: no transform
     for (int e = tid; e < G * D / 2; e += 256) {
@@ -243,101 +281,117 @@ void decode_grouped_kernel(const DecodeParams p) {
     qd_s[0][h][jd] = static_cast<uint8_t>(hi);
     qd_s[1][h][jd] = static_cast<uint8_t>(mi);
     qd_s[2][h][jd] = static_cast<uint8_t>(lo);
-    // block sums over the BLOCK consecutive lanes of the block
+    // block sums: over the SPAN consecutive lanes of the block in this wave, then
+    // across waves (blocks of 128 dims span two waves) in LDS
     int s0 = qi, s1 = hi, s2 = mi, s3 = lo;
 #pragma unroll
-    for (int m = 1; m < BLOCK; m <<= 1) {
+    for (int m = 1; m < SPAN; m <<= 1) {
       s0 += __shfl_xor(s0, m, 64);
       s1 += __shfl_xor(s1, m, 64);
       s2 += __shfl_xor(s2, m, 64);
       s3 += __shfl_xor(s3, m, 64);
     }
-    if (jd % BLOCK == 0) {
-      qds_s[h][jd / BLOCK][0] = s0;
-      qds_s[h][jd / BLOCK][1] = s1;
-      qds_s[h][jd / BLOCK][2] = s2;
-      qds_s[h][jd / BLOCK][3] = s3;
+    if (jd % SPAN == 0) {
+      atomicAdd(&qds_s[h][jd / BLOCK][0], s0);
+      atomicAdd(&qds_s[h][jd / BLOCK][1], s1);
+      atomicAdd(&qds_s[h][jd / BLOCK][2], s2);
+      atomicAdd(&qds_s[h][jd / BLOCK][3], s3);
     }
   }
   __syncthreads();
 
-  // ---- lane roles.  Q.K runs as C = Q K^T: C rows are the (head, block) pairs, C
-  // columns 16 tokens.  Column j of 16-token group hf is token 4 j + hf of the step, so
-  // lane (j, lq) ends with the logits of four consecutive tokens for C rows 4 lq .. 4 lq
-  // + 3: heads lq HPL .. lq HPL + HPL - 1, every block of the quad.  A head's logit is
-  // then summed over its blocks inside the lane, and the P.V rows the lane accumulates
-  // (C rows 4 lq + u of the same instruction shape) are the same (head, block) pairs.
-  const int j = lane & 15;             // Q row (head, block) / token column / P.V row or dim
-  const int lq = lane >> 4;            // k-chunk of the MFMA operands
-  const int hA = j / BPQ;              // head of Q operand row j
-  const int bA = j % BPQ;              // block (within a quad) of Q operand row j
-  // base-2 logit per integer unit of head lq HPL + hl (kept positive: a zero query has
-  // all-zero logits)
-  float c_logit[HPL];
+  // ---- lane roles.  Q.K runs as C = Q K^T per row set s: C rows are the (head, block)
+  // pairs r = 16 s + row (head r / BPQ, block r % BPQ of the quad), C columns 16 tokens.
+  // Column j of 16-token group hf is token 4 j + hf of the step, so lane (j, lq) ends with
+  // the logits of four consecutive tokens for C rows 4 lq .. 4 lq + 3 of each set: heads
+  // (16 s + 4 lq) / BPQ .. + HPL - 1, every block of the quad.  A head's logit is summed
+  // over its blocks inside the lane; the weights the lane forms are those rows.  P.V
+  // runs on (head, digit) rows: instruction i takes heads 4 i .. 4 i + 3, row 4 hh + d
+  // = digit d of head 4 i + hh (d = 3: zero), so lane (dim j, lq) ends with the three
+  // digit sums of head 4 i + lq.
+  const int j = lane & 15;             // Q row / token column / dim within 16
+  const int lq = lane >> 4;            // k-chunk of the operands; lane row group of the results
+  // head of set s, head slot hl of this lane (valid when < G)
+  auto head_of = [&](int s, int hl) { return (16 * s + 4 * lq) / BPQ + hl; };
+  // base-2 logit per integer unit of each head this lane holds (kept positive: a zero
+  // query has all-zero logits)
+  float c_logit[S][HPL];
 #pragma unroll
-  for (int hl = 0; hl < HPL; ++hl) {
-    const float am = __uint_as_float(qam_s[lq * HPL + hl]);
-    c_logit[hl] = fmaxf((am / static_cast<float>(QMAX)) * kLog2e * cn, 1.0e-30f);
-  }
-  // Q operand rows: digit d of q_hA at dims 32 (4 qd + lq) + 16 c + e (e < 16), zero
-  // outside the row's block
-  v4i qb[QB_LDS ? 1 : NQ][2][3];
-  v4i cinit[NQ];       // initial value of the low-digit chain per C row
-  float qsum_f[NQ][4];
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int hl = 0; hl < HPL; ++hl) {
+      const int h = head_of(s, hl) < G ? head_of(s, hl) : G - 1;
+      const float am = __uint_as_float(qam_s[h]);
+      c_logit[s][hl] = fmaxf((am / static_cast<float>(QMAX)) * kLog2e * cn, 1.0e-30f);
+    }
+  int cinit[NQ][S][4];   // initial value of the low-digit chain per C row
+  float qsum_f[NQ][S][4];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    const int blk = qd * BPQ + bA;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int dim0 = 32 * (4 * qd + lq) + 16 * c;
-      const bool in_blk = dim0 / BLOCK == blk;       // 16 dims never straddle a block
+    for (int s = 0; s < S; ++s) {
+      // Q operand row j of set s: digit d of q_h at dims 32 (4 qd + lq) + 16 c + e (e < 16),
+      // zero outside the row's block and for rows past the group
+      const int rA = 16 * s + j;
+      const int hA = rA / BPQ < G ? rA / BPQ : G - 1;
+      const int blkA = qd * BPQ + rA % BPQ;
 #pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&qd_s[d][hA][dim0]);
-        const v4i x = in_blk ? v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
-                                   static_cast<int>(w.w)}
-                             : v4i{0, 0, 0, 0};
-        if constexpr (QB_LDS) {
-          if (wave == 0) qbs_s[qd][c][d][lane] = x;
-        } else {
-          qb[qd][c][d] = x;
+      for (int c = 0; c < 2; ++c) {
+        const int dim0 = 32 * (4 * qd + lq) + 16 * c;
+        const bool in_blk = rA < ROWS && dim0 / BLOCK == blkA;   // 16 dims never straddle a block
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          const uint4 w = *reinterpret_cast<const uint4*>(&qd_s[d][hA][dim0]);
+          const v4i x = in_blk ? v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                                     static_cast<int>(w.w)}
+                               : v4i{0, 0, 0, 0};
+          if (wave == 0) qbs_s[qd][s][c][d][lane] = x;
         }
       }
-    }
-    // C row 4 lq + rr = (head lq HPL + rr / BPQ, block qd BPQ + rr % BPQ); symmetric codes
-    // are centred (u - 2^(b-1)) by the low-digit chain's initial value -2^(b-1) sum(q)
-    // (the digit combination wraps in int32; only the centred total must fit)
+      // C row 4 lq + rr of set s; symmetric codes are centred (u - 2^(b-1)) by the
+      // low-digit chain's initial value -2^(b-1) sum(q) (the digit combination wraps in
+      // int32; only the centred total must fit)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int hr = lq * HPL + rr / BPQ, br = qd * BPQ + rr % BPQ;
-      cinit[qd][rr] = ASYM ? 0 : static_cast<int>(static_cast<uint32_t>(-EXC) * static_cast<uint32_t>(qds_s[hr][br][0]));
-      qsum_f[qd][rr] = static_cast<float>(qds_s[hr][br][0]);
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * s + 4 * lq + rr;
+        const bool ok = r < ROWS;
+        const int hr = ok ? r / BPQ : 0, br = qd * BPQ + r % BPQ;
+        cinit[qd][s][rr] = (ASYM || !ok) ? 0 : static_cast<int>(static_cast<uint32_t>(-EXC) * static_cast<uint32_t>(qds_s[hr][br][0]));
+        qsum_f[qd][s][rr] = ok ? static_cast<float>(qds_s[hr][br][0]) : 0.0f;
+      }
     }
   }
   __syncthreads();   // u_s is reused for value rows below
 
-  float m_run[HPL], l_run[HPL];
+  float m_run[S][HPL], l_run[S][HPL];
 #pragma unroll
-  for (int hl = 0; hl < HPL; ++hl) {
-    m_run[hl] = -INFINITY;
-    l_run[hl] = 0.0f;
-  }
-  float ob[NQ][4];
+  for (int s = 0; s < S; ++s)
 #pragma unroll
-  for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ob[qd][rr] = 0.0f;
-  float acc[NQ][NBQ][HPL];
+    for (int hl = 0; hl < HPL; ++hl) {
+      m_run[s][hl] = -INFINITY;
+      l_run[s][hl] = 0.0f;
+    }
+  float ob[NQ][S][4];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-    for (int nb = 0; nb < NBQ; ++nb)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int u = 0; u < HPL; ++u) acc[qd][nb][u] = 0.0f;
+      for (int rr = 0; rr < 4; ++rr) ob[qd][s][rr] = 0.0f;
+  float acc[NQ][NI][NBQ];   // head 4 i + lq, dim 128 qd + 16 nb + j
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NBQ; ++nb) acc[qd][i][nb] = 0.0f;
   // P.V centring of symmetric codes: the byte -2^(b-1) in every lane of a B operand
   // (a product with it gives -2^(b-1) times each weight row's sum)
   const int exc_b = static_cast<int>(0x01010101u * static_cast<uint32_t>((256 - EXC) & 255));
   const v4i excv = {exc_b, exc_b, exc_b, exc_b};
+  // P.V A operand of this lane: row j = 4 hh + d; the (head, block) row it reads is
+  // fixed per (instruction i, block) and the digit plane is d
+  const int pv_hh = j >> 2, pv_d = j & 3;
 
   const int T = p.T;
   const int ntiles = (T + kTile - 1) / kTile;
@@ -384,8 +438,8 @@ void decode_grouped_kernel(const DecodeParams p) {
   };
   auto load_m = [&](Raw& r, int st) {
     const uint32_t tok0 = static_cast<uint32_t>(st) * kStep;
-    load_row<MDW>(rkm, (tok0 + lane) * (NBLK * MB), r.km);
-    load_row<MDW>(rvm, (tok0 + lane) * (NBLK * MB), r.vm);
+    load_row<MDB>(rkm, (tok0 + lane) * MDB, r.km);
+    load_row<MDB>(rvm, (tok0 + lane) * MDB, r.vm);
   };
 
   // one step from the raw data in `r`; each part of `r` is refilled with step `nx`
@@ -410,22 +464,25 @@ void decode_grouped_kernel(const DecodeParams p) {
     load_v(r, nx, 0, 0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
-    // ---- logits (integer units of c_logit[hl]): head lq HPL + hl, token 4 j + hf
-    float L[HPL][4];
+    // ---- logits (integer units of c_logit): head slot hl of set s, token 4 j + hf
+    float L[S][HPL][4];
 #pragma unroll
-    for (int hl = 0; hl < HPL; ++hl)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int hf = 0; hf < 4; ++hf) L[hl][hf] = 0.0f;
+      for (int hl = 0; hl < HPL; ++hl)
+#pragma unroll
+        for (int hf = 0; hf < 4; ++hf) L[s][hl][hf] = 0.0f;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      v4i qq[2][3];
+      // Q operands of a single row set stay in registers over the quad's four token
+      // groups; with two or more sets they are read from LDS where they are used
+      v4i qq1[2][3];
+      if constexpr (S == 1) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          if constexpr (QB_LDS) qq[c][d] = qbs_s[qd][c][d][lane];
-          else qq[c][d] = qb[qd][c][d];
-        }
+          for (int d = 0; d < 3; ++d) qq1[c][d] = qbs_s[qd][0][c][d][lane];
+      }
       // key scales (and zero-points) of the lane's four tokens, every block of the quad
       float sk[BPQ][4], zk[BPQ][4];
 #pragma unroll
@@ -442,20 +499,25 @@ void decode_grouped_kernel(const DecodeParams p) {
                         static_cast<int>(dk[3])};
         const v4i a1 = {static_cast<int>(dk[4]), static_cast<int>(dk[5]), static_cast<int>(dk[6]),
                         static_cast<int>(dk[7])};
-        v4i c[3];
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          c[d] = mfma64(qq[0][d], a0, d == 2 ? cinit[qd] : v4i{0, 0, 0, 0});
-          c[d] = mfma64(qq[1][d], a1, c[d]);
-        }
+        for (int s = 0; s < S; ++s) {
+          v4i c[3];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int hl = rr / BPQ, bq = rr % BPQ;
-          // sum over the block of q (u - 2^(b-1)) (symmetric) or q u (asymmetric), exact
-          const int comb = combine3<16, 8>(c[0][rr], c[1][rr], c[2][rr]);
-          float v = __builtin_fmaf(sk[bq][hf], static_cast<float>(comb), L[hl][hf]);
-          if constexpr (ASYM) v = __builtin_fmaf(zk[bq][hf], qsum_f[qd][rr], v);
-          L[hl][hf] = v;
+          for (int d = 0; d < 3; ++d) {
+            const v4i ci = d == 2 ? v4i{cinit[qd][s][0], cinit[qd][s][1], cinit[qd][s][2], cinit[qd][s][3]}
+                                  : v4i{0, 0, 0, 0};
+            c[d] = mfma64(S == 1 ? qq1[0][d] : qbs_s[qd][s][0][d][lane], a0, ci);
+            c[d] = mfma64(S == 1 ? qq1[1][d] : qbs_s[qd][s][1][d][lane], a1, c[d]);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int hl = rr / BPQ, bq = rr % BPQ;
+            // sum over the block of q (u - 2^(b-1)) (symmetric) or q u (asymmetric), exact
+            const int comb = combine3<16, 8>(c[0][rr], c[1][rr], c[2][rr]);
+            float v = __builtin_fmaf(sk[bq][hf], static_cast<float>(comb), L[s][hl][hf]);
+            if constexpr (ASYM) v = __builtin_fmaf(zk[bq][hf], qsum_f[qd][s][rr], v);
+            L[s][hl][hf] = v;
+          }
         }
       }
     }
@@ -464,93 +526,116 @@ void decode_grouped_kernel(const DecodeParams p) {
       // masking into selects executed on every step
       asm volatile("");
 #pragma unroll
-      for (int hl = 0; hl < HPL; ++hl)
+      for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int hf = 0; hf < 4; ++hf)
-          if (base + 4 * j + hf >= T) L[hl][hf] = -INFINITY;
+        for (int hl = 0; hl < HPL; ++hl)
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf)
+            if (base + 4 * j + hf >= T) L[s][hl][hf] = -INFINITY;
     }
     // ---- online softmax per head (base 2), lazy maximum: the running maximum moves
     // only when a logit exceeds it by more than 8, which each lane can test on its own
     // tokens; the step maximum over the 16 token columns is needed only then
-    float tl[HPL];
+    float tl[S][HPL];
     bool up = false;
 #pragma unroll
-    for (int hl = 0; hl < HPL; ++hl) {
-      const float t = fmaxf(fmaxf(L[hl][0], L[hl][1]), fmaxf(L[hl][2], L[hl][3])) * c_logit[hl];
-      tl[hl] = t;
-      up = up || t > m_run[hl] + 8.0f;
-    }
-    if (__any(up)) {
+    for (int s = 0; s < S; ++s)
 #pragma unroll
       for (int hl = 0; hl < HPL; ++hl) {
-        // finite: every step holds a valid token
-        const float m_new = fmaxf(m_run[hl], row16_max(tl[hl]));
-        const float alpha = __builtin_amdgcn_exp2f(m_run[hl] - m_new);
-        l_run[hl] *= alpha;
+        const float t = fmaxf(fmaxf(L[s][hl][0], L[s][hl][1]), fmaxf(L[s][hl][2], L[s][hl][3])) * c_logit[s][hl];
+        tl[s][hl] = t;
+        up = up || t > m_run[s][hl] + 8.0f;
+      }
+    if (__any(up)) {
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
+      for (int s = 0; s < S; ++s)
 #pragma unroll
-          for (int bq = 0; bq < BPQ; ++bq) ob[qd][hl * BPQ + bq] *= alpha;
+        for (int hl = 0; hl < HPL; ++hl) {
+          // finite: every step holds a valid token
+          const float m_new = fmaxf(m_run[s][hl], row16_max(tl[s][hl]));
+          const float alpha = __builtin_amdgcn_exp2f(m_run[s][hl] - m_new);
+          l_run[s][hl] *= alpha;
 #pragma unroll
-          for (int nb = 0; nb < NBQ; ++nb) acc[qd][nb][hl] *= alpha;
+          for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+            for (int bq = 0; bq < BPQ; ++bq) ob[qd][s][hl * BPQ + bq] *= alpha;
+          m_run[s][hl] = m_new;
+          const int h = head_of(s, hl);
+          if (j == 0 && h < G) alpha_s[wave][h] = alpha;
         }
-        m_run[hl] = m_new;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
+      // the P.V accumulators of head 4 i + lq follow their head's rescaling
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int h = 4 * i + lq < G ? 4 * i + lq : G - 1;
+        const float a = alpha_s[wave][h];
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+          for (int nb = 0; nb < NBQ; ++nb) acc[qd][i][nb] *= a;
       }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
     }
-    float pr[HPL][4];
+    float pr[S][HPL][4];
 #pragma unroll
-    for (int hl = 0; hl < HPL; ++hl)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int hf = 0; hf < 4; ++hf) {
-        pr[hl][hf] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[hl][hf], c_logit[hl], -m_run[hl]));
-        l_run[hl] += pr[hl][hf];
-      }
+      for (int hl = 0; hl < HPL; ++hl)
+#pragma unroll
+        for (int hf = 0; hf < 4; ++hf) {
+          pr[s][hl][hf] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[s][hl][hf], c_logit[s][hl], -m_run[s][hl]));
+          l_run[s][hl] += pr[s][hl][hf];
+        }
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      // ---- weights w = p s_v of C row (head, block) as 21-bit integers, byte digits
+      // ---- weights w = p s_v of row (head, block) as 21-bit integers, byte digits
       float sv[BPQ][4], zv[BPQ][4];
 #pragma unroll
       for (int bq = 0; bq < BPQ; ++bq) {
         meta4(&mf[1][qd * BPQ + bq][0][4 * j], sv[bq]);
         if constexpr (ASYM) meta4(&mf[1][qd * BPQ + bq][NS - 1][4 * j], zv[bq]);
       }
-      float wsg[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int hl = rr / BPQ, bq = rr % BPQ;
-        float w[4];
+      for (int s = 0; s < S; ++s) {
 #pragma unroll
-        for (int hf = 0; hf < 4; ++hf) {
-          // zero past T (scale reads as zero); an fma, so that the float16 scale enters
-          // v_fma_mix_f32 without a separate conversion
-          w[hf] = __builtin_fmaf(pr[hl][hf], sv[bq][hf], 0.0f);
-          if constexpr (ASYM) ob[qd][rr] = __builtin_fmaf(pr[hl][hf], zv[bq][hf], ob[qd][rr]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const int hl = rr / BPQ, bq = rr % BPQ;
+          float w[4];
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf) {
+            // zero past T (scale reads as zero); an fma, so that the float16 scale enters
+            // v_fma_mix_f32 without a separate conversion
+            w[hf] = __builtin_fmaf(pr[s][hl][hf], sv[bq][hf], 0.0f);
+            if constexpr (ASYM) ob[qd][s][rr] = __builtin_fmaf(pr[s][hl][hf], zv[bq][hf], ob[qd][s][rr]);
+          }
+          // row maximum over the step's 64 tokens; w >= 0, so the float bits order as
+          // unsigned integers (an integer maximum needs no NaN quieting)
+          const float wm = __uint_as_float(row16_max_u32(
+              umax(umax(__float_as_uint(w[0]), __float_as_uint(w[1])), umax(__float_as_uint(w[2]), __float_as_uint(w[3])))));
+          // w winv <= WMAX - 1 up to an ulp of rcp; integer wi and its three digits from
+          // one float addition (kDigitBias)
+          const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
+          if (j == 0) wsg_s[wave][qd][16 * s + 4 * lq + rr] = wm * (1.0f / static_cast<float>(WMAX - 1));
+          uint32_t f[4];
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf) f[hf] = __float_as_uint(__builtin_fmaf(w[hf], winv, kDigitBias));
+          // byte transpose: digit plane k gets byte k of the four tokens' words; planes 0
+          // and 1 then flip bit 7 of every byte (the xor 0x80 of the digit rule)
+          const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
+          const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
+          const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
+          const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
+          const int prow = 4 * lq + rr;
+          const int off = 16 * slot16(j >> 2, prow) + 4 * (j & 3);
+          *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][0][wrow(prow)][off]) =
+              __builtin_amdgcn_perm(y23, y01, 0x05040100u);                                      // d2
+          *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][1][wrow(prow)][off]) =
+              __builtin_amdgcn_perm(x23, x01, 0x07060302u) ^ 0x80808080u;                        // d1
+          *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][2][wrow(prow)][off]) =
+              __builtin_amdgcn_perm(x23, x01, 0x05040100u) ^ 0x80808080u;                        // d0
         }
-        // row maximum over the step's 64 tokens; w >= 0, so the float bits order as
-        // unsigned integers (an integer maximum needs no NaN quieting)
-        const float wm = __uint_as_float(row16_max_u32(
-            umax(umax(__float_as_uint(w[0]), __float_as_uint(w[1])), umax(__float_as_uint(w[2]), __float_as_uint(w[3])))));
-        // w winv <= WMAX - 1 up to an ulp of rcp; integer wi and its three digits from
-        // one float addition (kDigitBias)
-        const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
-        wsg[rr] = wm * (1.0f / static_cast<float>(WMAX - 1));
-        uint32_t f[4];
-#pragma unroll
-        for (int hf = 0; hf < 4; ++hf) f[hf] = __float_as_uint(__builtin_fmaf(w[hf], winv, kDigitBias));
-        // byte transpose: digit plane k gets byte k of the four tokens' words; planes 0
-        // and 1 then flip bit 7 of every byte (the xor 0x80 of the digit rule)
-        const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
-        const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
-        const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
-        const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
-        const int prow = 4 * lq + rr;
-        uint8_t* row = &wq_s[wave][qd][0][wrow(prow)][0];
-        const int off = 16 * slot16(j >> 2, prow) + 4 * (j & 3);
-        *reinterpret_cast<uint32_t*>(row + off) = __builtin_amdgcn_perm(y23, y01, 0x05040100u);   // d2
-        *reinterpret_cast<uint32_t*>(row + 16 * kStep + off) =
-            __builtin_amdgcn_perm(x23, x01, 0x07060302u) ^ 0x80808080u;                            // d1
-        *reinterpret_cast<uint32_t*>(row + 32 * kStep + off) =
-            __builtin_amdgcn_perm(x23, x01, 0x05040100u) ^ 0x80808080u;                            // d0
       }
       if (qd > 0) {
         // the previous quad's P.V is done with the value rows
@@ -559,15 +644,10 @@ void decode_grouped_kernel(const DecodeParams p) {
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_wave_barrier();
-      // ---- P.V: rows (head, block), K = the step's 64 tokens, 16 dims per instruction
-      v4i a[3], c0[3];
-#pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        const uint4 x = *reinterpret_cast<const uint4*>(&wq_s[wave][qd][d][wrow(j)][16 * slot16(lq, j)]);
-        a[d] = v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
-        // symmetric: start each chain at -2^(b-1) times the row's digit sum
-        c0[d] = ASYM ? v4i{0, 0, 0, 0} : mfma64(a[d], excv, v4i{0, 0, 0, 0});
-      }
+      // ---- P.V: rows (head, digit) of one quantisation block, K = the step's 64
+      // tokens, 16 dims per instruction
+      v4i pa[NI], pc[NI];
+      float pw[NI];
 #pragma unroll
       for (int nb = 0; nb < NBQ; ++nb) {
         if (nb == NBQ / 2) {
@@ -579,18 +659,33 @@ void decode_grouped_kernel(const DecodeParams p) {
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           __builtin_amdgcn_wave_barrier();
         }
-        const int bqn = (16 * nb) / BLOCK;          // block (within the quad) of these dims
+        if (nb % NBPB == 0) {
+          // first 16 dims of block bq: A operands, centring and scales of its rows
+          const int bq = nb / NBPB;
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int h = 4 * i + pv_hh;
+            const bool ok = pv_d < 3 && h < G;
+            const int r = (ok ? h : 0) * BPQ + bq;     // (head, block) row of the weights
+            const uint4 x = *reinterpret_cast<const uint4*>(
+                &wq_s[wave][qd][r >> 4][ok ? pv_d : 0][wrow(r & 15)][16 * slot16(lq, r & 15)]);
+            pa[i] = ok ? v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)}
+                       : v4i{0, 0, 0, 0};
+            // symmetric: start each product at -2^(b-1) times the rows' digit sums
+            pc[i] = ASYM ? v4i{0, 0, 0, 0} : mfma64(pa[i], excv, v4i{0, 0, 0, 0});
+            const int hw = 4 * i + lq < G ? 4 * i + lq : 0;
+            pw[i] = wsg_s[wave][qd][hw * BPQ + bq];
+          }
+        }
         const int rrow = 16 * (nb % (NBQ / 2)) + j;
         const uint4 x = *reinterpret_cast<const uint4*>(vrow + rrow * 64 + 16 * slot16(lq, rrow));
         const v4i bv = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
-        const v4i e0 = mfma64(a[0], bv, c0[0]);
-        const v4i e1 = mfma64(a[1], bv, c0[1]);
-        const v4i e2 = mfma64(a[2], bv, c0[2]);
 #pragma unroll
-        for (int u = 0; u < HPL; ++u) {
-          const int rr = u * BPQ + bqn;             // C row 4 lq + rr = (head lq HPL + u, block bqn)
-          const int ai = combine3<16, 8>(e0[rr], e1[rr], e2[rr]);
-          acc[qd][nb][u] = __builtin_fmaf(wsg[rr], static_cast<float>(ai), acc[qd][nb][u]);
+        for (int i = 0; i < NI; ++i) {
+          const v4i e = mfma64(pa[i], bv, pc[i]);
+          // rows 4 lq + d: the three digit sums of head 4 i + lq
+          const int ai = combine3<16, 8>(e[0], e[1], e[2]);
+          acc[qd][i][nb] = __builtin_fmaf(pw[i], static_cast<float>(ai), acc[qd][i][nb]);
         }
       }
       // the next quad or step overwrites this wave's LDS rows
@@ -623,32 +718,50 @@ void decode_grouped_kernel(const DecodeParams p) {
   // ---- combine the four waves; partials per query head (sums over the 16 token
   // columns of each lane row)
 #pragma unroll
-  for (int hl = 0; hl < HPL; ++hl) l_run[hl] = row16_sum(l_run[hl]);
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int hl = 0; hl < HPL; ++hl) l_run[s][hl] = row16_sum(l_run[s][hl]);
   if constexpr (ASYM) {
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) ob[qd][rr] = row16_sum(ob[qd][rr]);
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ob[qd][s][rr] = row16_sum(ob[qd][s][rr]);
   }
   __syncthreads();   // every wave is done with its value rows
   float* cacc = reinterpret_cast<float*>(u_s);      // [4][G][D]
   if (j == 0) {
 #pragma unroll
-    for (int hl = 0; hl < HPL; ++hl) {
-      cm_s[wave][lq * HPL + hl] = m_run[hl];
-      cl_s[wave][lq * HPL + hl] = l_run[hl];
-    }
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int hl = 0; hl < HPL; ++hl) {
+        const int h = head_of(s, hl);
+        if (h < G) {
+          cm_s[wave][h] = m_run[s][hl];
+          cl_s[wave][h] = l_run[s][hl];
+        }
+      }
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) cob_s[wave][lq * HPL + rr / BPQ][qd * BPQ + rr % BPQ] = ob[qd][rr];
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * s + 4 * lq + rr;
+          if (r < ROWS) cob_s[wave][r / BPQ][qd * BPQ + r % BPQ] = ob[qd][s][rr];
+        }
   }
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-    for (int nb = 0; nb < NBQ; ++nb)
+    for (int i = 0; i < NI; ++i) {
+      const int h = 4 * i + lq;
+      if (h < G) {
 #pragma unroll
-      for (int u = 0; u < HPL; ++u) cacc[(wave * G + lq * HPL + u) * D + 128 * qd + 16 * nb + j] = acc[qd][nb][u];
+        for (int nb = 0; nb < NBQ; ++nb) cacc[(wave * G + h) * D + 128 * qd + 16 * nb + j] = acc[qd][i][nb];
+      }
+    }
   __syncthreads();
   for (int e = tid; e < G * D; e += 256) {
     const int hh = e / D, dim = e % D;
@@ -686,23 +799,31 @@ void launch_fmt(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, 
   else launch_t<D, kFmtSymF16, BLOCK, G>(p, grid, s, e0, e1);
 }
 
+template <int D, int G>
+bool launch_g(const DecodeParams& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (p.block) {
+    case 32: launch_fmt<D, 32, G>(p, grid, s, e0, e1); return true;
+    case 64: launch_fmt<D, 64, G>(p, grid, s, e0, e1); return true;
+    case 128: launch_fmt<D, 128, G>(p, grid, s, e0, e1); return true;
+    default: return false;
+  }
+}
+
 template <int D>
 bool launch_d(const DecodeParams& p, int group, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (p.block == 32 && group == 4) {
-    launch_fmt<D, 32, 4>(p, grid, s, e0, e1);
-    return true;
+  switch (group) {
+    case 2: return launch_g<D, 2>(p, grid, s, e0, e1);
+    case 4: return launch_g<D, 4>(p, grid, s, e0, e1);
+    case 8: return launch_g<D, 8>(p, grid, s, e0, e1);
+    default: return false;
   }
-  if (p.block == 64 && group == 8) {
-    launch_fmt<D, 64, 8>(p, grid, s, e0, e1);
-    return true;
-  }
-  return false;
 }
 
 }  // namespace
 
 bool grouped_decode_supported(int d, int block, int group) {
-  return (d == 128 || d == 256) && ((block == 32 && group == 4) || (block == 64 && group == 8));
+  return (d == 128 || d == 256) && (block == 32 || block == 64 || block == 128) &&
+         (group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_decode_grouped(const DecodeParams& p, int batch, int d, hipStream_t s, hipEvent_t e0,

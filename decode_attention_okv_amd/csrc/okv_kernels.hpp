@@ -73,7 +73,7 @@ hipError_t launch_decode_head(const DecodeParams& p, int batch, int d, hipStream
                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Grouped decode (one workgroup per KV head serves its whole query group on MFMA):
-// built for head_dim 128/256 with (group 4, block 32) or (group 8, block 64).  Grid
+// built for head_dim 128/256, query groups 2, 4 and 8, blocks of 32, 64 and 128.  Grid
 // (nsplit, hkv, batch); writes the same workspace as launch_decode_head.
 bool grouped_decode_supported(int d, int block, int group);
 hipError_t launch_decode_grouped(const DecodeParams& p, int batch, int d, hipStream_t s,

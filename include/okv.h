@@ -276,7 +276,7 @@ int okv_timing_read(okv_handle* h, int32_t* calls, double* attn_ms, double* redu
  * (split, sequence, query head) reads the packed cache of its KV head.
  * OKV_DECODE_GROUPED: one workgroup per (split, sequence, KV head) reads the packed
  * cache once for the whole query group and computes Q.K and P.V on int8 matrix
- * cores; built for query group 4 with block 32 and query group 8 with block 64.
+ * cores; built for query groups of 2, 4 and 8 with blocks of 32, 64 and 128 dims.
  * OKV_DECODE_AUTO (default) takes the grouped kernel where it is built, else the
  * per-head one.  okv_set_decode_kernel returns OKV_E_UNSUPPORTED for
  * OKV_DECODE_GROUPED on other configurations; okv_get_decode_kernel reports the

@@ -35,7 +35,7 @@ def _need_gpu():
 def expected_kernel(wl, kernel):
     if kernel != "auto":
         return kernel
-    grouped = wl.d in (128, 256) and (wl.group, wl.block) in ((4, 32), (8, 64))
+    grouped = wl.d in (128, 256) and wl.group in (2, 4, 8) and wl.block in (32, 64, 128)
     return "grouped" if grouped else "per_head"
 
 
@@ -359,3 +359,19 @@ def test_asym_zero_point_block_by_hand():
     assert v_u.tolist() == want_u[0].tolist()
     assert cache.v_meta[0, 0, 0].cpu().numpy().view(np.uint8).reshape(2, 2).tolist() == want_meta[0].tolist()
     cache.close()
+
+
+# grouped decode over every query group it is built for (2, 4, 8) and blocks of 32, 64
+# and 128 dims: (head, block) rows in one or two 16-row sets, P.V rows of four heads
+@pytest.mark.parametrize("d,block,quant,group,meta", [
+    (128, 32, "sym", 8, "f16"), (128, 32, "asym", 8, "e4m3"), (128, 32, "sym", 2, "f32"),
+    (128, 64, "sym", 2, "f16"), (128, 64, "asym", 4, "e4m3"), (128, 128, "sym", 8, "f16"),
+    (128, 128, "asym", 2, "e4m3"), (256, 32, "sym", 8, "f16"), (256, 64, "asym", 2, "e4m3"),
+    (256, 128, "sym", 4, "f32"),
+])
+def test_grouped_shapes(d, block, quant, group, meta):
+    rot = "so4" if d == 256 else "sign"
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(
+        batch=2, hq=2 * group, hkv=2, d=d, block=block, quant=quant, scale_dtype=meta, rotation=rot)
+    run_case(wl, 700, [300, 400], steps=1, kernel="grouped")
+    run_case(wl, 97, [97], splits=3, kernel="grouped")
