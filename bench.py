@@ -288,6 +288,71 @@ def write_record(wl, ms):
             "write_GBs": round(write_bytes_per_position(wl) * wl.tokens / (ms * 1e-3) / 1e9, 1)}
 
 
+def settle(cache, q, out, ms):
+    """Untimed decode calls back to back for about `ms` milliseconds of GPU time: under
+    sustained load the GPU's power management lowers and then restores its clocks over
+    the first tens of calls (a transient of ~10 ms), and timed regions start after it, at
+    the steady state a decoder serving continuously runs in.  Returns the call count."""
+    import torch
+    n, el = 0, 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while el < ms and n < 1000:
+        e0.record()
+        for _ in range(10):
+            cache.decode_attn(q, out)
+        e1.record()
+        torch.cuda.synchronize()
+        el += e0.elapsed_time(e1)
+        n += 10
+    return n
+
+
+def series_leg(name, dev, n=150):
+    """Sustained load: the streaming-read probe, then `n` decode calls of the workload
+    back to back, each timed with its own events; GB/s over windows of call indices
+    (the clock transient of the first tens of calls shows here)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_okv_amd as okv
+    import okv_synth
+    wl = okv_synth.workload(name)
+    cache = new_cache(wl, -(-(wl.tokens + 32) // 32) * 32, dev)
+    timed_prefill(cache, wl, dev)
+    q = okv_synth.queries(wl, 0, device=dev)
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    nb = 2 << 30
+    buf = torch.ones(nb // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def run(fn, k):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+        ev[0].record()
+        for i in range(k):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(k)])
+
+    okv.read_probe(buf, sink)
+    cache.decode_attn(q, out)
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    tp = run(lambda: okv.read_probe(buf, sink), 100)
+    time.sleep(2.0)
+    td = run(lambda: cache.decode_attn(q, out), n)
+    byt = sum(algorithmic_decode_bytes(wl, wl.tokens))
+    wins = [(1, 6), (10, 20), (20, 40), (40, 60), (n - 20, n)]
+    rec = {"workload": name, "calls": n,
+           "probe_GBs": round(nb / (float(np.mean(tp)) * 1e-3) / 1e9, 1),
+           "decode_GBs_by_call": {f"{a}-{b}": round(byt / (float(np.mean(td[a:b])) * 1e-3) / 1e9, 1) for a, b in wins},
+           "decode_us_by_call": {f"{a}-{b}": round(1e3 * float(np.mean(td[a:b])), 1) for a, b in wins}}
+    cache.close()
+    del buf, cache
+    torch.cuda.empty_cache()
+    return rec
+
+
 def decode_calls(cache, wl, q, out, calls):
     """`calls` okv_decode_attn calls back to back at the current length, twice: bare,
     with torch events around the loop (whole call: attention + merge + gaps), then with
@@ -326,7 +391,7 @@ def decode_record(wl, t, call_us, attn_us, red_us, kernel, splits):
             "call_frac_hbm_peak": round((kern_b + ob) / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def decode_workload_leg(name, dev, calls=20):
+def decode_workload_leg(name, dev, calls=20, settle_ms=0.0):
     """A decode workload at its full size: prefill write (timed), then `calls` decode
     calls back to back.  Reports write rates, decode call / kernel times, GB/s and the
     fraction of the HBM peak, and the recorded HBM traffic of the decode kernel."""
@@ -340,6 +405,8 @@ def decode_workload_leg(name, dev, calls=20):
     q = okv_synth.queries(wl, 0, device=dev)
     out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
     print(f"# leg {name}: decode x {calls}", file=sys.stderr, flush=True)
+    if settle_ms > 0:
+        settle(cache, q, out, settle_ms)
     call_us, attn_us, red_us = decode_calls(cache, wl, q, out, calls)
     kern = cache.decode_kernel()
     rec = {"workload": name, "batch": wl.batch, "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.d,
@@ -462,6 +529,12 @@ def main():
     ap.add_argument("--legs", default="gqa_b16h64kv8_t128k_asym,gqa_h32kv8_t32k,so4_d256_b32_t8k,tiny_d128_t256",
                     help="other workloads to run at full size ('' to skip)")
     ap.add_argument("--read-probe", type=int, default=1, help="run the streaming-read probe (0 to skip)")
+    ap.add_argument("--series", type=int, default=0,
+                    help="also time this many back-to-back decode calls one by one after the probe "
+                         "(the clock transient under sustained load; 0 to skip)")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed decode calls (GPU milliseconds) before the warm-up steps, past the "
+                         "clock transient of the first tens of calls (0 to skip)")
     ap.add_argument("--prefill-workload", default="gqa_h32kv8_t32k",
                     help="workload of the chunked-prefill attention leg ('' to skip)")
     ap.add_argument("--prefill-rows", type=int, default=2048)
@@ -524,6 +597,7 @@ def main():
         cache.write(*news[i])
         cache.decode_attn(qs[i], out)
 
+    settle_calls = settle(cache, qs[0], out, args.settle_ms) if args.settle_ms > 0 else 0
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
@@ -576,6 +650,7 @@ def main():
                    "scale_dtype": wl.scale_dtype, "rotation": wl.rotation, "splits": splits},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_schedule": "serial: append 1 token, then decode, one stream",
+        "settle": {"ms": args.settle_ms, "decode_calls": settle_calls},
         "decode_kernel": kernel,
         "decode_kernel_us": round(1e3 * attn_ms / K, 2),
         "reduce_kernel_us": round(1e3 * red_ms / K, 2),
@@ -603,9 +678,11 @@ def main():
             elif name == "tiny_d128_t256":
                 res["workloads"].append(tiny_leg(dev))
             else:
-                res["workloads"].append(decode_workload_leg(name, dev))
+                res["workloads"].append(decode_workload_leg(name, dev, settle_ms=args.settle_ms))
     if args.read_probe:
         res["hbm_read_probe"] = read_probe_leg(dev)
+    if args.series:
+        res["sustained_series"] = series_leg(wl.name, dev, args.series)
     if args.widths:
         res["code_widths"] = [variant_leg(wl, bits=int(b)) for b in args.widths.split(",")]
     if args.rotations:
