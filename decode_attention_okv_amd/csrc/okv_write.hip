@@ -83,20 +83,21 @@ __device__ __forceinline__ void keep_mask(int n, uint32_t* m) {
   }
 }
 
-// One workgroup owns one 32-token tile of one (sequence, KV head).  Its 64
-// four-lane groups take the 32 key and 32 value vectors of the tile's slots; lane r
-// of a group holds elements EPL r .. EPL r + EPL - 1 of the vector.  New slots are
-// quantised; key rows are stored straight from the lanes; value codes go through LDS
-// to be regrouped per dimension (old codes of earlier tokens are kept, slots after
-// the new tokens stay zero).
+// One workgroup owns one 32-token tile of one (sequence, KV head).  Each of the tile's
+// 32 key and 32 value vectors is held by LPV = D / 64 lanes; lane r of a vector holds
+// elements 64 r .. 64 r + 63.  New slots are quantised; key rows are stored straight
+// from the lanes; value codes go through LDS to be regrouped per dimension (old codes
+// of earlier tokens are kept, slots after the new tokens stay zero).
 //
 // SIGN_BF16: the sign-flip rotation with bfloat16 inputs, fixed at compile time, so that
 // the other rotations' and float32 inputs' code leaves this variant.
 template <int D, int BLOCK, bool ASYM, int BITS, bool SIGN_BF16>
-__global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
+__global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
   const int rotation = SIGN_BF16 ? static_cast<int>(kRotSign) : p.rotation;
   const bool in_bf16 = SIGN_BF16 || p.in_bf16 != 0;
-  constexpr int EPL = D / 4;                          // elements per lane
+  constexpr int EPL = 64;                             // elements per lane
+  constexpr int LPV = D / EPL;                        // lanes per vector (2 or 4)
+  constexpr int NT = 64 * LPV;                        // threads: 64 vectors of the tile
   constexpr int GPL = EPL / 32;                       // 32-code groups per lane
   constexpr int BPL = EPL >= BLOCK ? EPL / BLOCK : 1; // quantisation blocks per lane
   constexpr int LPB = BLOCK > EPL ? BLOCK / EPL : 1;  // lanes per block
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   constexpr int EXC = 1 << (BITS - 1);                // excess of symmetric codes
   constexpr int LEV = EXC - 1;                        // symmetric levels: codes -LEV .. LEV
   constexpr int TOP = (1 << BITS) - 1;                // largest code
+  static_assert(NT == D && (LPV == 2 || LPV == 4), "one thread per dim of the tile stage");
   __shared__ __align__(16) uint8_t vt[kTile][D];      // value codes u of the tile, [slot][dim]
 
   const int tile = p.tile0 + static_cast<int>(blockIdx.x);
@@ -117,16 +119,23 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   const int s_hi = min(p.len + p.n_new - tile_base, kTile);
   const size_t unit = static_cast<size_t>(b) * p.hkv + h;
 
-  const int vi = tid >> 2, r = tid & 3;
+  const int vi = tid / LPV, r = tid % LPV;
   const int tensor = vi >> 5, slot = vi & 31;
-  const bool active = slot >= s_lo && slot < s_hi;    // uniform over the four lanes
+  const bool active = slot >= s_lo && slot < s_hi;    // uniform over the vector's lanes
   uint32_t* vdst = reinterpret_cast<uint32_t*>(&vt[slot][EPL * r]);
 
-  // SO(4) matrices of B: staged in LDS once per workgroup (every lane reads those of
-  // its dims for each vector)
-  __shared__ __align__(16) float rot_s[4 * D];
-  if (rotation == kRotSo4) {                          // uniform over the workgroup
-    for (int e = tid; e < 4 * D; e += 256) rot_s[e] = p.rot[e];
+  // SO(4) matrices of B (every lane reads those of its dims for each vector), or the
+  // sign flips of D as bit masks over pairs of bfloat16 inputs: staged in LDS once per
+  // workgroup
+  __shared__ __align__(16) float rot_s[SIGN_BF16 ? 1 : 4 * D];
+  __shared__ __align__(16) uint32_t sgn_s[SIGN_BF16 ? D / 2 : 1];
+  if constexpr (SIGN_BF16) {
+    if (tid < D / 2) {
+      sgn_s[tid] = (p.rot[2 * tid] < 0.0f ? 0x8000u : 0u) | (p.rot[2 * tid + 1] < 0.0f ? 0x80000000u : 0u);
+    }
+    __syncthreads();
+  } else if (rotation == kRotSo4) {                   // uniform over the workgroup
+    for (int e = tid; e < 4 * D; e += NT) rot_s[e] = p.rot[e];
     __syncthreads();
   }
 
@@ -139,7 +148,12 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
 #pragma unroll
       for (int i = 0; i < EPL / 8; ++i) {
         const uint4 w = s4[i];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        if constexpr (SIGN_BF16) {
+          // the sign flip of two elements at once: x D is exact, a sign bit each
+          const uint4 g = reinterpret_cast<const uint4*>(sgn_s + EPL / 2 * r)[i];
+          ws[0] ^= g.x; ws[1] ^= g.y; ws[2] ^= g.z; ws[3] ^= g.w;
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           x[8 * i + 2 * k] = bf16_bits_to_f32(ws[k] & 0xFFFFu);
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
         x[4 * i] = w.x; x[4 * i + 1] = w.y; x[4 * i + 2] = w.z; x[4 * i + 3] = w.w;
       }
     }
-    if (rotation == kRotSign) {
+    if (!SIGN_BF16 && rotation == kRotSign) {
       const float4* sg = reinterpret_cast<const float4*>(p.rot + EPL * r);
 #pragma unroll
       for (int i = 0; i < EPL / 4; ++i) {
@@ -164,33 +178,37 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
     }
     const bool rotated = rotation != kRotNone;     // U = I: y = x (uniform)
     if (rotated) {
-    // butterfly stages of stride 1 .. EPL/2 inside the lane
+      // butterfly stages of stride 1 .. EPL/2 inside the lane
 #pragma unroll
-    for (int hs = 1; hs < EPL; hs <<= 1) {
+      for (int hs = 1; hs < EPL; hs <<= 1) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        if (!(e & hs)) {
-          const float a = x[e], c = x[e + hs];
-          x[e] = a + c;
-          x[e + hs] = a - c;
+        for (int e = 0; e < EPL; ++e) {
+          if (!(e & hs)) {
+            const float a = x[e], c = x[e + hs];
+            x[e] = a + c;
+            x[e + hs] = a - c;
+          }
         }
       }
-    }
-    // strides EPL and 2 EPL: partner lane r ^ 1, then r ^ 2.  Each stage is one
-    // fma(sg, partner, own) = RN(own +- partner): the lower lane gets a + b, the upper
-    // one b - a = -(a - b).  After both stages lanes 1 and 2 hold their values negated
-    // (RN is odd, so the magnitudes are exactly the specified ones); sigma undoes it.
-    {
-      const float sg1 = (r & 1) ? -1.0f : 1.0f;
+      // strides EPL (partner lane r ^ 1) and, with four lanes, 2 EPL (r ^ 2).  Each
+      // stage is one fma(sg, partner, own) = RN(own +- partner): the lower lane gets
+      // a + b, the upper one b - a = -(a - b).  Lanes whose index has odd parity end
+      // up holding their values negated (RN is odd, so the magnitudes are exactly the
+      // specified ones); sigma undoes it.
+      {
+        const float sg1 = (r & 1) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg1, dpp<kXor1>(x[e]), x[e]);
-      const float sg2 = (r & 2) ? -1.0f : 1.0f;
+        for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg1, dpp<kXor1>(x[e]), x[e]);
+      }
+      if constexpr (LPV == 4) {
+        const float sg2 = (r & 2) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg2, dpp<kXor2>(x[e]), x[e]);
-    }
+        for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg2, dpp<kXor2>(x[e]), x[e]);
+      }
     }
     const float cnorm = (D == 128) ? __uint_as_float(0x3DB504F3u) : 0.0625f;  // RN32(1/sqrt(D))
-    const float sc = ((r ^ (r >> 1)) & 1) ? -cnorm : cnorm;   // sigma * c
+    const bool neg = LPV == 4 ? ((r ^ (r >> 1)) & 1) != 0 : (r & 1) != 0;
+    const float sc = neg ? -cnorm : cnorm;           // sigma * c
     // Symmetric codes with the sign-flip rotation use the unnormalised values: the
     // block maximum of |RN(x c)| is RN(max|x| c) (rounding is monotone), and the
     // code quotient folds c in.  Otherwise y = RN(x c) is formed here.
@@ -270,69 +288,73 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
       mblk[bb] = xs * rsblk[bb];      // quotient multiplier: y / s ~ x mblk
     }
 
-    // ---- codes u (0 .. 2^b - 1) as integer-valued floats, written over x.  Fast
-    // rounding: rint of the approximate quotient (within ~3e-6 of the exact one,
-    // |q| <= 16); the excess 2^(b-1) added before rint is even, so ties keep their
-    // parity.
-    // If any value of the wave lies within kNear of a rounding boundary, the wave
-    // takes the exact rounding of the exact quotient instead.
-    constexpr bool KEEP = EPL <= 32;            // keep the rounded quotients in registers
-    float kq[KEEP ? EPL : 1];
+    // ---- codes u (0 .. 2^b - 1) of each 32-code group as bytes of eight words (byte j
+    // of word k = code 4 k + j).  Fast rounding: rint of the approximate quotient
+    // (within ~3e-6 of the exact one, |q| <= 16); the excess 2^(b-1) added before rint
+    // is even, so ties keep their parity.  If any value of the wave lies within kNear
+    // of a rounding boundary, the wave takes the exact rounding of the exact quotient
+    // instead.
     auto quotient = [&](int e) {
       const int bb = e / BE;
       if constexpr (!ASYM) return __builtin_fmaf(x[e], mblk[bb], static_cast<float>(EXC));   // 2^(b-1) + y / s
       else return (x[e] - zblk[bb]) * rsblk[bb];                          // RN32(y - z) / s
     };
+    uint32_t pk[GPL][8];
     float dist = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float t = quotient(e);
-      const float k = __builtin_rintf(t);
-      if constexpr (KEEP) kq[e] = k;
-      dist = fmaxf(dist, fabsf(t - k));
-    }
+    for (int g = 0; g < GPL; ++g)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = quotient(32 * g + 4 * k + i);
+          const float kk = __builtin_rintf(t);
+          dist = fmaxf(dist, fabsf(t - kk));
+          u[i] = ASYM ? __builtin_amdgcn_fmed3f(kk, 0.0f, static_cast<float>(TOP))
+                      : __builtin_amdgcn_fmed3f(kk, 1.0f, static_cast<float>(TOP));
+        }
+        pk[g][k] = bytes_of(u);
+      }
     if (__any(dist > kNear)) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int bb = e / BE;
-        const float y = x[e] * xs;
-        x[e] = ASYM ? static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, TOP))
-                    : static_cast<float>(rne_code(y, sblk[bb], rsblk[bb], -LEV, LEV) + EXC);
-      }
+      for (int g = 0; g < GPL; ++g)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 32 * g + 4 * k + i, bb = e / BE;
+            const float y = x[e] * xs;
+            u[i] = ASYM ? static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, TOP))
+                        : static_cast<float>(rne_code(y, sblk[bb], rsblk[bb], -LEV, LEV) + EXC);
+          }
+          pk[g][k] = bytes_of(u);
+        }
     } else {
+      // zero scale: code 0 (the exact path's rule)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float k;
-        if constexpr (KEEP) k = kq[e];
-        else k = __builtin_rintf(quotient(e));
-        x[e] = ASYM ? __builtin_amdgcn_fmed3f(k, 0.0f, static_cast<float>(TOP))
-                    : __builtin_amdgcn_fmed3f(k, 1.0f, static_cast<float>(TOP));
-      }
-#pragma unroll
-      for (int bb = 0; bb < BPL; ++bb) {
+      for (int g = 0; g < GPL; ++g) {
+        const int bb = (32 * g) / BE;
         if (!(sblk[bb] > 0.0f)) {
 #pragma unroll
-          for (int e = 0; e < BE; ++e) x[bb * BE + e] = ASYM ? 0.0f : static_cast<float>(EXC);   // zero scale: code 0
+          for (int k = 0; k < 8; ++k) pk[g][k] = ASYM ? 0u : 0x01010101u * static_cast<uint32_t>(EXC);
         }
       }
     }
-    const float* u = x;
 
     // ---- pack
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
-      uint32_t d[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) d[k] = bytes_of(&u[32 * g + 4 * k]);
       if (tensor == 0) {
         uint32_t w[BITS];
-        pack_group<BITS>(d, w);
+        pack_group<BITS>(pk[g], w);
         uint32_t* dst = reinterpret_cast<uint32_t*>(p.k_codes + row * (BITS * D / 8) + GB * (GPL * r + g));
 #pragma unroll
         for (int k = 0; k < BITS; ++k) dst[k] = w[k];
       } else {
-        reinterpret_cast<uint4*>(vdst)[2 * g] = make_uint4(d[0], d[1], d[2], d[3]);
-        reinterpret_cast<uint4*>(vdst)[2 * g + 1] = make_uint4(d[4], d[5], d[6], d[7]);
+        reinterpret_cast<uint4*>(vdst)[2 * g] = make_uint4(pk[g][0], pk[g][1], pk[g][2], pk[g][3]);
+        reinterpret_cast<uint4*>(vdst)[2 * g + 1] = make_uint4(pk[g][4], pk[g][5], pk[g][6], pk[g][7]);
       }
     }
   } else if (tensor == 1) {
@@ -342,9 +364,10 @@ __global__ __launch_bounds__(256) void write_kernel(const WriteParams p) {
   }
   __syncthreads();
 
-  // ---- value tile: dim j is one group over the tile's 32 tokens
+  // ---- value tile: dim j is one group over the tile's 32 tokens (one thread per dim)
   uint8_t* vtile = p.v_codes + (unit * p.ntile_cap + tile) * static_cast<size_t>(D) * GB;
-  for (int j = tid; j < D; j += 256) {
+  {
+    const int j = tid;
     uint32_t d[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -370,11 +393,11 @@ template <int D, int BLOCK, int BITS>
 void launch_b(const WriteParams& p, dim3 grid, hipStream_t s) {
   const bool sb = p.rotation == kRotSign && p.in_bf16;
   if (p.quant == kQuantAsym) {
-    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, false>), grid, dim3(256), 0, s, p);
+    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, true>), grid, dim3(D), 0, s, p);
+    else hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, false>), grid, dim3(D), 0, s, p);
   } else {
-    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, false>), grid, dim3(256), 0, s, p);
+    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, true>), grid, dim3(D), 0, s, p);
+    else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, false>), grid, dim3(D), 0, s, p);
   }
 }
 
