@@ -27,6 +27,37 @@ __device__ __forceinline__ float dpp(float v) {
 constexpr int kXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;   // quad_perm [2,3,0,1]
 
+// x[e] = RN(x[e] + sg * (x[e] of the partner lane)) for 16 elements, one v_fmac_f32 with
+// a DPP source each (quad_perm [1,0,3,2]: partner lane ^ 1; [2,3,0,1]: lane ^ 2).  The
+// compiler does not fold a DPP move into v_fmac_f32 (a move and an fma per element).
+// The hazard check does not see inside inline asm: the leading s_nop gives the wait
+// states a DPP read needs after a VALU or EXEC write of its sources, the trailing one
+// covers a DPP read of the results right after the block.
+#define OKV_FMAC_DPP(i, perm) "v_fmac_f32_dpp %" #i ", %" #i ", %16 " perm " row_mask:0xf bank_mask:0xf\n"
+#define OKV_FMAC_DPP16(perm)                                                                 \
+  "s_nop 4\n" OKV_FMAC_DPP(0, perm) OKV_FMAC_DPP(1, perm) OKV_FMAC_DPP(2, perm)               \
+      OKV_FMAC_DPP(3, perm) OKV_FMAC_DPP(4, perm) OKV_FMAC_DPP(5, perm) OKV_FMAC_DPP(6, perm)  \
+      OKV_FMAC_DPP(7, perm) OKV_FMAC_DPP(8, perm) OKV_FMAC_DPP(9, perm) OKV_FMAC_DPP(10, perm) \
+      OKV_FMAC_DPP(11, perm) OKV_FMAC_DPP(12, perm) OKV_FMAC_DPP(13, perm)                    \
+      OKV_FMAC_DPP(14, perm) OKV_FMAC_DPP(15, perm) "s_nop 1"
+template <int CTRL>
+__device__ __forceinline__ void fmac_dpp16(float* x, float sg) {
+  static_assert(CTRL == kXor1 || CTRL == kXor2, "lane partner");
+  if constexpr (CTRL == kXor1) {
+    asm(OKV_FMAC_DPP16("quad_perm:[1,0,3,2]")
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+          "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
+        : "v"(sg));
+  } else {
+    asm(OKV_FMAC_DPP16("quad_perm:[2,3,0,1]")
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+          "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
+        : "v"(sg));
+  }
+}
+#undef OKV_FMAC_DPP16
+#undef OKV_FMAC_DPP
+
 // Distance from a half-integer below which the fast code rounding defers to the exact
 // one: the approximate quotient is within ~2e-6 of the exact one for |q| <= 8.
 constexpr float kNear = 0.5f - 0x1.0p-17f;
@@ -83,20 +114,27 @@ __device__ __forceinline__ void keep_mask(int n, uint32_t* m) {
   }
 }
 
+// Elements of a vector per lane: 32 at d = 128 (four lanes per vector, two cross-lane
+// butterfly stages, about 76 registers: six waves per SIMD) and 64 at d = 256.  Holding
+// 64 elements at d = 128 saves one butterfly stage but takes about 143 registers (three
+// waves per SIMD), which left the loads less overlap with the arithmetic.
+constexpr int write_epl(int d) { return d == 128 ? 32 : 64; }
+constexpr int write_threads(int d) { return 64 * (d / write_epl(d)); }
+
 // One workgroup owns one 32-token tile of one (sequence, KV head).  Each of the tile's
-// 32 key and 32 value vectors is held by LPV = D / 64 lanes; lane r of a vector holds
-// elements 64 r .. 64 r + 63.  New slots are quantised; key rows are stored straight
-// from the lanes; value codes go through LDS to be regrouped per dimension (old codes
-// of earlier tokens are kept, slots after the new tokens stay zero).
+// 32 key and 32 value vectors is held by LPV = D / EPL lanes; lane r of a vector holds
+// elements EPL r .. EPL r + EPL - 1.  New slots are quantised; key rows are stored
+// straight from the lanes; value codes go through LDS to be regrouped per dimension
+// (old codes of earlier tokens are kept, slots after the new tokens stay zero).
 //
 // SIGN_BF16: the sign-flip rotation with bfloat16 inputs, fixed at compile time, so that
 // the other rotations' and float32 inputs' code leaves this variant.
 template <int D, int BLOCK, bool ASYM, int BITS, bool SIGN_BF16>
-__global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
+__global__ __launch_bounds__(write_threads(D)) void write_kernel(const WriteParams p) {
   const int rotation = SIGN_BF16 ? static_cast<int>(kRotSign) : p.rotation;
   const bool in_bf16 = SIGN_BF16 || p.in_bf16 != 0;
-  constexpr int EPL = 64;                             // elements per lane
-  constexpr int LPV = D / EPL;                        // lanes per vector (2 or 4)
+  constexpr int EPL = write_epl(D);                   // elements per lane
+  constexpr int LPV = D / EPL;                        // lanes per vector (4)
   constexpr int NT = 64 * LPV;                        // threads: 64 vectors of the tile
   constexpr int GPL = EPL / 32;                       // 32-code groups per lane
   constexpr int BPL = EPL >= BLOCK ? EPL / BLOCK : 1; // quantisation blocks per lane
@@ -107,7 +145,7 @@ __global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
   constexpr int EXC = 1 << (BITS - 1);                // excess of symmetric codes
   constexpr int LEV = EXC - 1;                        // symmetric levels: codes -LEV .. LEV
   constexpr int TOP = (1 << BITS) - 1;                // largest code
-  static_assert(NT == D && (LPV == 2 || LPV == 4), "one thread per dim of the tile stage");
+  static_assert(NT >= D && (LPV == 2 || LPV == 4), "one thread per dim of the tile stage");
   __shared__ __align__(16) uint8_t vt[kTile][D];      // value codes u of the tile, [slot][dim]
 
   const int tile = p.tile0 + static_cast<int>(blockIdx.x);
@@ -198,12 +236,12 @@ __global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
       {
         const float sg1 = (r & 1) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg1, dpp<kXor1>(x[e]), x[e]);
+        for (int e = 0; e < EPL; e += 16) fmac_dpp16<kXor1>(x + e, sg1);
       }
       if constexpr (LPV == 4) {
         const float sg2 = (r & 2) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = __builtin_fmaf(sg2, dpp<kXor2>(x[e]), x[e]);
+        for (int e = 0; e < EPL; e += 16) fmac_dpp16<kXor2>(x + e, sg2);
       }
     }
     const float cnorm = (D == 128) ? __uint_as_float(0x3DB504F3u) : 0.0625f;  // RN32(1/sqrt(D))
@@ -299,6 +337,17 @@ __global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
       if constexpr (!ASYM) return __builtin_fmaf(x[e], mblk[bb], static_cast<float>(EXC));   // 2^(b-1) + y / s
       else return (x[e] - zblk[bb]) * rsblk[bb];                          // RN32(y - z) / s
     };
+    // Symmetric codes skip the clipping in the fast rounding: |y| <= max|y| + eps, so
+    // |y / s| exceeds 2^(b-1) - 1 by at most the scale's rounding (2^-11 relative for a
+    // normal float16, 2^-24 for a normal float32), and rint stays within the code range.
+    // A block whose scale is zero or subnormal in its storage type (less relative
+    // precision) sends the wave to the exact rounding, which clips.
+    bool exact = false;
+    if constexpr (!ASYM) {
+      const float smin = p.scale_dtype == kScaleF16 ? 0x1.0p-14f : 0x1.0p-125f;
+#pragma unroll
+      for (int bb = 0; bb < BPL; ++bb) exact = exact || !(sblk[bb] >= smin);
+    }
     uint32_t pk[GPL][8];
     float dist = 0.0f;
 #pragma unroll
@@ -311,12 +360,11 @@ __global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
           const float t = quotient(32 * g + 4 * k + i);
           const float kk = __builtin_rintf(t);
           dist = fmaxf(dist, fabsf(t - kk));
-          u[i] = ASYM ? __builtin_amdgcn_fmed3f(kk, 0.0f, static_cast<float>(TOP))
-                      : __builtin_amdgcn_fmed3f(kk, 1.0f, static_cast<float>(TOP));
+          u[i] = ASYM ? __builtin_amdgcn_fmed3f(kk, 0.0f, static_cast<float>(TOP)) : kk;
         }
         pk[g][k] = bytes_of(u);
       }
-    if (__any(dist > kNear)) {
+    if (__any(exact || dist > kNear)) {
 #pragma unroll
       for (int g = 0; g < GPL; ++g)
 #pragma unroll
@@ -326,12 +374,20 @@ __global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
           for (int i = 0; i < 4; ++i) {
             const int e = 32 * g + 4 * k + i, bb = e / BE;
             const float y = x[e] * xs;
-            u[i] = ASYM ? static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, TOP))
-                        : static_cast<float>(rne_code(y, sblk[bb], rsblk[bb], -LEV, LEV) + EXC);
+            if constexpr (ASYM) {
+              u[i] = static_cast<float>(rne_code(y - zblk[bb], sblk[bb], rsblk[bb], 0, TOP));
+            } else {
+              // a float32 scale below 2^-64 (it can be subnormal; its reciprocal can
+              // overflow) is taken together with y times 2^64, which is exact
+              const bool tiny = sblk[bb] < 0x1.0p-64f;
+              const float f = tiny ? 0x1.0p64f : 1.0f;
+              const float s2 = sblk[bb] * f;
+              u[i] = static_cast<float>(rne_code(y * f, s2, tiny ? __builtin_amdgcn_rcpf(s2) : rsblk[bb], -LEV, LEV) + EXC);
+            }
           }
           pk[g][k] = bytes_of(u);
         }
-    } else {
+    } else if constexpr (ASYM) {
       // zero scale: code 0 (the exact path's rule)
 #pragma unroll
       for (int g = 0; g < GPL; ++g) {
@@ -364,9 +420,9 @@ __global__ __launch_bounds__(D) void write_kernel(const WriteParams p) {
   }
   __syncthreads();
 
-  // ---- value tile: dim j is one group over the tile's 32 tokens (one thread per dim)
+  // ---- value tile: dim j is one group over the tile's 32 tokens (threads j < D)
   uint8_t* vtile = p.v_codes + (unit * p.ntile_cap + tile) * static_cast<size_t>(D) * GB;
-  {
+  if (tid < D) {
     const int j = tid;
     uint32_t d[8];
 #pragma unroll
@@ -393,11 +449,11 @@ template <int D, int BLOCK, int BITS>
 void launch_b(const WriteParams& p, dim3 grid, hipStream_t s) {
   const bool sb = p.rotation == kRotSign && p.in_bf16;
   if (p.quant == kQuantAsym) {
-    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, true>), grid, dim3(D), 0, s, p);
-    else hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, false>), grid, dim3(D), 0, s, p);
+    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, true>), grid, dim3(write_threads(D)), 0, s, p);
+    else hipLaunchKernelGGL((write_kernel<D, BLOCK, true, BITS, false>), grid, dim3(write_threads(D)), 0, s, p);
   } else {
-    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, true>), grid, dim3(D), 0, s, p);
-    else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, false>), grid, dim3(D), 0, s, p);
+    if (sb) hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, true>), grid, dim3(write_threads(D)), 0, s, p);
+    else hipLaunchKernelGGL((write_kernel<D, BLOCK, false, BITS, false>), grid, dim3(write_threads(D)), 0, s, p);
   }
 }
 

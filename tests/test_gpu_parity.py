@@ -262,6 +262,41 @@ def test_fixed_point_headroom_aligned(d, block, quant, hq, kernel, bits):
     cache.close()
 
 
+@pytest.mark.parametrize("scale_dtype,eps,block,in_dtype", [
+    ("f16", 1e-6, 32, "f32"), ("f16", 0.0, 32, "bf16"), ("f16", 0.0, 128, "f32"),
+    ("f32", 0.0, 32, "f32"), ("f32", 0.0, 64, "bf16"),
+])
+def test_tiny_magnitudes_write(scale_dtype, eps, block, in_dtype):
+    # vectors from 1e-40 to 1e3 in size (one all-zero token): symmetric scales that are
+    # zero or subnormal in their storage type lose relative precision, so |y / s| may
+    # pass 3 and the codes must be clipped; scales near the float16 range's top
+    # overflow.  Codes and scales byte-exact against the oracle.
+    _need_gpu()
+    import oracle
+    wl = okv_synth.workload("tiny_d128_t256").with_(
+        batch=1, hq=2, hkv=1, block=block, quant="sym", scale_dtype=scale_dtype, eps=eps,
+        rotation="sign", in_dtype=in_dtype)
+    p32, _ = params_of(wl)
+    t = 96
+    rng = np.random.default_rng(11)
+    mag = np.logspace(-40, 3, t)
+    kx = (rng.standard_normal((t, wl.d)) * mag[:, None]).astype(np.float32)
+    vx = (rng.standard_normal((t, wl.d)) * mag[::-1, None]).astype(np.float32)
+    kx[7] = 0.0
+    # one outlier element per vector: the other elements of its block sit far below it
+    kx[::5, 3] *= 1e4
+    k = torch.from_numpy(kx).reshape(1, t, 1, wl.d).to(wl.torch_dtype).cuda()
+    v = torch.from_numpy(vx).reshape(1, t, 1, wl.d).to(wl.torch_dtype).cuda()
+    cache = make_cache(wl, 128, p32)
+    say("tiny magnitudes okv_write", scale_dtype, eps, block, in_dtype)
+    cache.write(k, v)
+    kh, vh = unit_inputs(k, v, 0, 0)
+    ref = oracle.write_unit(kh, vh, wl, p32)
+    mism = compare_unit(cache, wl, 0, 0, t, ref)
+    assert all(x == 0 for x in mism.values()), mism
+    cache.close()
+
+
 def test_error_paths():
     _need_gpu()
     import decode_attention_okv_amd as okv
