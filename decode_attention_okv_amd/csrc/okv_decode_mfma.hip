@@ -155,7 +155,7 @@ struct GroupShape {
   // LDS of one workgroup (bytes): value rows / prologue / partials, weight digits, block
   // metadata, Q operands, small per-head arrays
   static constexpr int LDS = UB + 4 * NQ * S * 3 * 16 * 64 + 4 * 2 * NBLK * NS * MST * MSZ +
-                             NQ * S * 2 * 3 * 64 * 16 + 4 * NQ * S * 16 * 4 + 52 * G + 32 * G * NBLK;
+                             NQ * S * 2 * 3 * 64 * 16 + 4 * NQ * S * 16 * 4 + 52 * G + 20 * G * NBLK;
 };
 
 // Resident waves per SIMD the register allocation aims for at d = 128 and b <= 3: as
@@ -215,7 +215,7 @@ void decode_grouped_kernel(const DecodeParams p) {
   __shared__ float alpha_s[4][G];                                // softmax rescaling per head
   __shared__ float cm_s[4][G], cl_s[4][G];
   __shared__ float cob_s[4][G][NBLK];
-  __shared__ int32_t qds_s[G][NBLK][4];              // per (head, block): sum q, hi, mid, lo
+  __shared__ int32_t qds_s[G][NBLK];                 // per (head, block): sum of q
   __shared__ uint32_t qam_s[G];                      // per head: max |q1| (float bits)
 
   const int split = blockIdx.x;
@@ -238,7 +238,7 @@ void decode_grouped_kernel(const DecodeParams p) {
     q_s[e / D][jd] = x;
   }
   if (tid < G) qam_s[tid] = 0u;
-  for (int e = tid; e < G * NBLK * 4; e += 256) (&qds_s[0][0][0])[e] = 0;
+  for (int e = tid; e < G * NBLK; e += 256) (&qds_s[0][0])[e] = 0;
   __syncthreads();
   for (int hs = 1; hs < D && p.rotation != kRotNone; hs <<= 1) {   // U = I: no transform
     for (int e = tid; e < G * D / 2; e += 256) {
@@ -283,20 +283,10 @@ void decode_grouped_kernel(const DecodeParams p) {
     qd_s[2][h][jd] = static_cast<uint8_t>(lo);
     // block sums: over the SPAN consecutive lanes of the block in this wave, then
     // across waves (blocks of 128 dims span two waves) in LDS
-    int s0 = qi, s1 = hi, s2 = mi, s3 = lo;
+    int s0 = qi;
 #pragma unroll
-    for (int m = 1; m < SPAN; m <<= 1) {
-      s0 += __shfl_xor(s0, m, 64);
-      s1 += __shfl_xor(s1, m, 64);
-      s2 += __shfl_xor(s2, m, 64);
-      s3 += __shfl_xor(s3, m, 64);
-    }
-    if (jd % SPAN == 0) {
-      atomicAdd(&qds_s[h][jd / BLOCK][0], s0);
-      atomicAdd(&qds_s[h][jd / BLOCK][1], s1);
-      atomicAdd(&qds_s[h][jd / BLOCK][2], s2);
-      atomicAdd(&qds_s[h][jd / BLOCK][3], s3);
-    }
+    for (int m = 1; m < SPAN; m <<= 1) s0 += __shfl_xor(s0, m, 64);
+    if (jd % SPAN == 0) atomicAdd(&qds_s[h][jd / BLOCK], s0);
   }
   __syncthreads();
 
@@ -356,8 +346,8 @@ void decode_grouped_kernel(const DecodeParams p) {
         const int r = 16 * s + 4 * lq + rr;
         const bool ok = r < ROWS;
         const int hr = ok ? r / BPQ : 0, br = qd * BPQ + r % BPQ;
-        cinit[qd][s][rr] = (ASYM || !ok) ? 0 : static_cast<int>(static_cast<uint32_t>(-EXC) * static_cast<uint32_t>(qds_s[hr][br][0]));
-        qsum_f[qd][s][rr] = ok ? static_cast<float>(qds_s[hr][br][0]) : 0.0f;
+        cinit[qd][s][rr] = (ASYM || !ok) ? 0 : static_cast<int>(static_cast<uint32_t>(-EXC) * static_cast<uint32_t>(qds_s[hr][br]));
+        qsum_f[qd][s][rr] = ok ? static_cast<float>(qds_s[hr][br]) : 0.0f;
       }
     }
   }
@@ -664,13 +654,13 @@ void decode_grouped_kernel(const DecodeParams p) {
           const int bq = nb / NBPB;
 #pragma unroll
           for (int i = 0; i < NI; ++i) {
-            const int h = 4 * i + pv_hh;
-            const bool ok = pv_d < 3 && h < G;
-            const int r = (ok ? h : 0) * BPQ + bq;     // (head, block) row of the weights
+            // rows 4 hh + 3 and rows of heads past the group only feed result rows that
+            // are never read, so they take any valid row's digits (no masking)
+            const int h = 4 * i + pv_hh < G ? 4 * i + pv_hh : G - 1;
+            const int r = h * BPQ + bq;                // (head, block) row of the weights
             const uint4 x = *reinterpret_cast<const uint4*>(
-                &wq_s[wave][qd][r >> 4][ok ? pv_d : 0][wrow(r & 15)][16 * slot16(lq, r & 15)]);
-            pa[i] = ok ? v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)}
-                       : v4i{0, 0, 0, 0};
+                &wq_s[wave][qd][r >> 4][pv_d < 3 ? pv_d : 2][wrow(r & 15)][16 * slot16(lq, r & 15)]);
+            pa[i] = v4i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
             // symmetric: start each product at -2^(b-1) times the rows' digit sums
             pc[i] = ASYM ? v4i{0, 0, 0, 0} : mfma64(pa[i], excv, v4i{0, 0, 0, 0});
             const int hw = 4 * i + lq < G ? 4 * i + lq : 0;
