@@ -147,7 +147,8 @@ struct GroupShape {
   static constexpr bool ASYM = FMT == kFmtAsym;
   static constexpr int NS = ASYM ? 2 : 1;         // decoded metadata floats per entry: s (, z)
   static constexpr int MST = ASYM ? 72 : 80;      // padded LDS row of one block's metadata
-  static constexpr int MSZ = FMT == kFmtSymF32 ? 4 : 2;   // bytes per decoded metadata value
+  // bytes per decoded metadata value in LDS
+  static constexpr int MSZ = FMT == kFmtSymF32 || (ASYM && NBLK <= 2) ? 4 : 2;
   static constexpr int UB0 = 4 * 64 * 64;         // per-wave value rows of half a quad
   static constexpr int UB1 = 4 * G * D * 4;       // wave partials in the final combine
   static constexpr int UB2 = G * D * 7;           // prologue: q1 floats and digits
@@ -197,8 +198,10 @@ void decode_grouped_kernel(const DecodeParams p) {
   constexpr int QMAX = q_limit(BLOCK, code_max(ASYM, BITS));
   constexpr int WMAX = w_limit(code_max(ASYM, BITS), kW7);
   static_assert(NU >= 1 && G * D % 256 == 0, "prologue: whole waves per head");
-  // E4M3 and fp16 scales are exact in float16: half-size metadata rows
-  using MT = typename std::conditional<FMT == kFmtSymF32, float, _Float16>::type;
+  // fp16 scales stay float16 in LDS (half-size rows, no conversion); E4M3 pairs decode
+  // to float32 (v_cvt_pk_f32_fp8) and are kept as float32 when there are at most two
+  // blocks (no conversion back), else as float16 (exact) to keep the LDS footprint
+  using MT = typename std::conditional<SH::MSZ == 4, float, _Float16>::type;
   using Raw = StepRaw<NQ, DPL, MDW, BITS>;
 
   // u_s: q1 and its digits (prologue), decoded value rows (steps), wave partials (end)
