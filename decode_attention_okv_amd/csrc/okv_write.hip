@@ -247,10 +247,10 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
     const float cnorm = (D == 128) ? __uint_as_float(0x3DB504F3u) : 0.0625f;  // RN32(1/sqrt(D))
     const bool neg = LPV == 4 ? ((r ^ (r >> 1)) & 1) != 0 : (r & 1) != 0;
     const float sc = neg ? -cnorm : cnorm;           // sigma * c
-    // Symmetric codes with the sign-flip rotation use the unnormalised values: the
-    // block maximum of |RN(x c)| is RN(max|x| c) (rounding is monotone), and the
-    // code quotient folds c in.  Otherwise y = RN(x c) is formed here.
-    const bool normalized = ASYM || rotation == kRotSo4;
+    // With the sign-flip rotation the values stay unnormalised: the block statistics of
+    // RN(x c) follow from those of x (rounding is monotone), and the code quotient folds
+    // c in.  SO(4) needs y = RN(x c) as the input of its 4 x 4 products.
+    const bool normalized = rotation == kRotSo4;
     if (normalized && rotated) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = x[e] * sc;
@@ -278,7 +278,8 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
     const size_t row = unit * p.tcap + pos;
     void* meta = tensor ? p.v_meta : p.k_meta;
     const bool meta_lane = (r % LPB) == 0;
-    float sblk[BPL], rsblk[BPL], zblk[BPL], mblk[BPL];
+    float sblk[BPL], rsblk[BPL], zblk[BPL], mblk[BPL], nzblk[BPL], ymax[BPL];
+    bool exact = false;   // this lane's blocks need the exact rounding (see below)
 #pragma unroll
     for (int bb = 0; bb < BPL; ++bb) {
       const int blk = (EPL * r) / BLOCK + bb;
@@ -308,6 +309,12 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
           mn = fminf(mn, x[bb * BE + e]);
           mx = fmaxf(mx, x[bb * BE + e]);
         }
+        {
+          // the extremes of y = RN(x xs): RN is monotone, decreasing in x when xs < 0
+          const float a = mn * xs, c = mx * xs;
+          mn = fminf(a, c);
+          mx = fmaxf(a, c);
+        }
         if constexpr (LPB >= 2) {
           mn = fminf(mn, dpp<kXor1>(mn));
           mx = fmaxf(mx, dpp<kXor1>(mx));
@@ -316,6 +323,7 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
           mn = fminf(mn, dpp<kXor2>(mn));
           mx = fmaxf(mx, dpp<kXor2>(mx));
         }
+        ymax[bb] = fmaxf(fabsf(mn), fabsf(mx));
         const float s32 = (mx - mn) / static_cast<float>(TOP);
         const uint32_t sb = e4m3_encode(s32), zb = e4m3_encode(mn);
         if (meta_lane) reinterpret_cast<uint16_t*>(meta)[row * NBLK + blk] = static_cast<uint16_t>(sb | (zb << 8));
@@ -324,6 +332,17 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
       }
       rsblk[bb] = __builtin_amdgcn_rcpf(sblk[bb]);
       mblk[bb] = xs * rsblk[bb];      // quotient multiplier: y / s ~ x mblk
+      if constexpr (ASYM) {
+        // (y - z) / s ~ x mblk - z / s in one fma.  Its error is at most
+        // (|y| + |z|) / s 1.5 2^-23 + 2^-21 (reciprocal, two products, the fma), and the
+        // exact quotient of RN(y - z) differs from (y - z) / s by at most
+        // (|y| / s + 8) 2^-24; with (max|y| + |z|) / s <= 16 (blocks that hold values of
+        // both signs stay below 15) both stay under 4.8e-6, inside the near-tie margin.
+        // Other blocks, and zero scales, take the exact rounding.
+        nzblk[bb] = -zblk[bb] * rsblk[bb];
+        const float big = (ymax[bb] + fabsf(zblk[bb])) * rsblk[bb];
+        exact = exact || !(big <= 16.0f);
+      }
     }
 
     // ---- codes u (0 .. 2^b - 1) of each 32-code group as bytes of eight words (byte j
@@ -335,14 +354,13 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
     auto quotient = [&](int e) {
       const int bb = e / BE;
       if constexpr (!ASYM) return __builtin_fmaf(x[e], mblk[bb], static_cast<float>(EXC));   // 2^(b-1) + y / s
-      else return (x[e] - zblk[bb]) * rsblk[bb];                          // RN32(y - z) / s
+      else return __builtin_fmaf(x[e], mblk[bb], nzblk[bb]);                  // (y - z) / s
     };
     // Symmetric codes skip the clipping in the fast rounding: |y| <= max|y| + eps, so
     // |y / s| exceeds 2^(b-1) - 1 by at most the scale's rounding (2^-11 relative for a
     // normal float16, 2^-24 for a normal float32), and rint stays within the code range.
     // A block whose scale is zero or subnormal in its storage type (less relative
     // precision) sends the wave to the exact rounding, which clips.
-    bool exact = false;
     if constexpr (!ASYM) {
       const float smin = p.scale_dtype == kScaleF16 ? 0x1.0p-14f : 0x1.0p-125f;
 #pragma unroll
@@ -387,16 +405,6 @@ __global__ __launch_bounds__(write_threads(D)) void write_kernel(const WritePara
           }
           pk[g][k] = bytes_of(u);
         }
-    } else if constexpr (ASYM) {
-      // zero scale: code 0 (the exact path's rule)
-#pragma unroll
-      for (int g = 0; g < GPL; ++g) {
-        const int bb = (32 * g) / BE;
-        if (!(sblk[bb] > 0.0f)) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) pk[g][k] = ASYM ? 0u : 0x01010101u * static_cast<uint32_t>(EXC);
-        }
-      }
     }
 
     // ---- pack
