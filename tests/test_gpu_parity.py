@@ -297,6 +297,34 @@ def test_tiny_magnitudes_write(scale_dtype, eps, block, in_dtype):
     cache.close()
 
 
+@pytest.mark.parametrize("rotation", ["none", "sign"])
+def test_asym_off_centre_blocks_write(rotation):
+    # asymmetric blocks whose values sit far from zero relative to their spread (the
+    # fast quotient's error bound fails there and the exact rounding takes over), mixed
+    # with centred ones; U = I keeps the offsets in every block, the sign flip keeps
+    # them only in tokens that are constant plus small noise; byte-exact
+    _need_gpu()
+    import oracle
+    wl = okv_synth.workload("gqa_b16h64kv8_t128k_asym").with_(
+        batch=1, hq=8, hkv=1, rotation=rotation, in_dtype="f32")
+    p32, _ = params_of(wl)
+    t = 96
+    rng = np.random.default_rng(23)
+    off = rng.uniform(-60.0, 60.0, size=(t, 1))
+    spread = np.where(np.arange(t)[:, None] % 3 == 0, 1.0, 0.01)
+    kx = (off + spread * rng.standard_normal((t, wl.d))).astype(np.float32)
+    vx = (off[::-1] + spread * rng.standard_normal((t, wl.d))).astype(np.float32)
+    k = torch.from_numpy(kx).reshape(1, t, 1, wl.d).cuda()
+    v = torch.from_numpy(vx).reshape(1, t, 1, wl.d).cuda()
+    cache = make_cache(wl, 128, p32)
+    say("asym off-centre okv_write", rotation)
+    cache.write(k, v)
+    ref = oracle.write_unit(kx, vx, wl, p32)
+    mism = compare_unit(cache, wl, 0, 0, t, ref)
+    assert all(x == 0 for x in mism.values()), mism
+    cache.close()
+
+
 def test_error_paths():
     _need_gpu()
     import decode_attention_okv_amd as okv
