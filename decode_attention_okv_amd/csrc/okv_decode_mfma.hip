@@ -12,8 +12,9 @@
 //    chains take the three balanced digits of the 24-bit fixed-point query and
 //    combine exactly in int32.  Each lane ends with whole logits (every block of its
 //    heads) of four consecutive tokens, so the softmax runs once per (token, head).
-//  * P.V: the step's weights p s of each (head, block) row become 21-bit integers in
-//    three balanced int8 digit planes in LDS.  A = rows (head, digit) of one block:
+//  * P.V: the step's weights p s of each (head, block) row become 21-bit integers
+//    (relative to one scale per head, or per row, and step) in three balanced int8
+//    digit planes in LDS.  A = rows (head, digit) of one block:
 //    instruction i takes heads 4 i .. 4 i + 3, row 4 hh + d holding digit d of head
 //    4 i + hh; B = value codes of 64 tokens x 16 dims of that block, decoded once per
 //    step into LDS; C = int32, so lane (dim j, lq) holds the three digit sums of head
@@ -174,6 +175,17 @@ constexpr int waves_per_eu() {
   return wg >= cap ? cap : (wg >= 1 ? wg : 1);
 }
 
+// P.V weight scales: one per (head, step), shared by the head's blocks of a quad (the
+// blocks' value scales are of one magnitude, so sharing costs a row at most a few of its
+// 21 bits, and a head's row maximum is taken once instead of once per block), except
+// where the kernel runs at four waves per SIMD or with 4-bit codes: there the extra
+// live values spill or cost a resident wave, and one scale per (head, block) row is
+// faster.
+template <int D, int FMT, int BLOCK, int G, int BITS>
+constexpr bool shared_weight_scale() {
+  return BITS <= 3 && waves_per_eu<D, FMT, BLOCK, G, BITS>() < 4;
+}
+
 // One workgroup = one (split, KV head, sequence) and all G query heads of that KV
 // head; its four waves take the split's 64-token steps in turn.
 template <int D, int FMT, int BLOCK, int G, int BITS>
@@ -183,6 +195,8 @@ void decode_grouped_kernel(const DecodeParams p) {
   constexpr int NQ = SH::NQ, BPQ = SH::BPQ, NBLK = SH::NBLK, ROWS = SH::ROWS, S = SH::S, HPL = SH::HPL;
   constexpr int NI = SH::NI, NBPB = SH::NBPB, NS = SH::NS, MST = SH::MST, UB = SH::UB;
   constexpr bool ASYM = SH::ASYM;
+  constexpr bool SHW = shared_weight_scale<D, FMT, BLOCK, G, BITS>();
+  constexpr int NSC = SHW ? 1 : BPQ;   // weight scales per (lane head, quad)
   static_assert(BPQ >= 1 && BPQ <= 4 && G >= 2, "blocks of 32 .. 128 dims, query groups of two or more");
   constexpr int ROWB = BITS * D / 8;   // bytes per key row
   constexpr int GB = 4 * BITS;         // bytes per 32-code group
@@ -214,7 +228,8 @@ void decode_grouped_kernel(const DecodeParams p) {
   // Q operands (the same for every wave, indexed by lane; in registers they would cost
   // resident waves)
   __shared__ __align__(16) v4i qbs_s[NQ][S][2][3][64];
-  __shared__ __align__(16) float wsg_s[4][NQ][16 * S];          // weight scale per (head, block) row
+  // P.V weight scales per quad: per head (first G entries) or per (head, block) row
+  __shared__ __align__(16) float wsg_s[4][NQ][16 * S];
   __shared__ float alpha_s[4][G];                                // softmax rescaling per head
   __shared__ float cm_s[4][G], cl_s[4][G];
   __shared__ float cob_s[4][G][NBLK];
@@ -590,44 +605,67 @@ void decode_grouped_kernel(const DecodeParams p) {
         meta4(&mf[1][qd * BPQ + bq][0][4 * j], sv[bq]);
         if constexpr (ASYM) meta4(&mf[1][qd * BPQ + bq][NS - 1][4 * j], zv[bq]);
       }
+      // shared scales: per token, the largest value scale over the quad's blocks
+      // (scales are >= 0)
+      float svm[4];
+#pragma unroll
+      for (int hf = 0; hf < 4; ++hf) {
+        uint32_t m = __float_as_uint(sv[0][hf]);
+        if constexpr (SHW) {
+#pragma unroll
+          for (int bq = 1; bq < BPQ; ++bq) m = umax(m, __float_as_uint(sv[bq][hf]));
+        }
+        svm[hf] = __uint_as_float(m);
+      }
 #pragma unroll
       for (int s = 0; s < S; ++s) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int hl = rr / BPQ, bq = rr % BPQ;
-          float w[4];
+        for (int hl = 0; hl < HPL; ++hl) {
+          // the largest weight of the scale's rows over the step's 64 tokens: p >= 0 and
+          // rounding is monotonic, so with a shared scale it is p svm of the largest
+          // product per token; w >= 0, so float bits order as unsigned integers (no NaN
+          // quieting).  w winv <= WMAX - 1 up to an ulp of rcp
+          const int hw = head_of(s, hl);
+          float winv[NSC];
 #pragma unroll
-          for (int hf = 0; hf < 4; ++hf) {
-            // zero past T (scale reads as zero); an fma, so that the float16 scale enters
-            // v_fma_mix_f32 without a separate conversion
-            w[hf] = __builtin_fmaf(pr[s][hl][hf], sv[bq][hf], 0.0f);
-            if constexpr (ASYM) ob[qd][s][rr] = __builtin_fmaf(pr[s][hl][hf], zv[bq][hf], ob[qd][s][rr]);
+          for (int k = 0; k < NSC; ++k) {
+            uint32_t mx = 0u;
+#pragma unroll
+            for (int hf = 0; hf < 4; ++hf)
+              mx = umax(mx, __float_as_uint(__builtin_fmaf(pr[s][hl][hf], SHW ? svm[hf] : sv[k][hf], 0.0f)));
+            const float wm = __uint_as_float(row16_max_u32(mx));
+            winv[k] = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
+            if (j == 0 && hw < G)
+              wsg_s[wave][qd][SHW ? hw : 16 * s + 4 * lq + hl * BPQ + k] = wm * (1.0f / static_cast<float>(WMAX - 1));
           }
-          // row maximum over the step's 64 tokens; w >= 0, so the float bits order as
-          // unsigned integers (an integer maximum needs no NaN quieting)
-          const float wm = __uint_as_float(row16_max_u32(
-              umax(umax(__float_as_uint(w[0]), __float_as_uint(w[1])), umax(__float_as_uint(w[2]), __float_as_uint(w[3])))));
-          // w winv <= WMAX - 1 up to an ulp of rcp; integer wi and its three digits from
-          // one float addition (kDigitBias)
-          const float winv = wm > 1.0e-30f ? static_cast<float>(WMAX - 1) * __builtin_amdgcn_rcpf(wm) : 0.0f;
-          if (j == 0) wsg_s[wave][qd][16 * s + 4 * lq + rr] = wm * (1.0f / static_cast<float>(WMAX - 1));
-          uint32_t f[4];
 #pragma unroll
-          for (int hf = 0; hf < 4; ++hf) f[hf] = __float_as_uint(__builtin_fmaf(w[hf], winv, kDigitBias));
-          // byte transpose: digit plane k gets byte k of the four tokens' words; planes 0
-          // and 1 then flip bit 7 of every byte (the xor 0x80 of the digit rule)
-          const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
-          const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
-          const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
-          const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
-          const int prow = 4 * lq + rr;
-          const int off = 16 * slot16(j >> 2, prow) + 4 * (j & 3);
-          *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][0][wrow(prow)][off]) =
-              __builtin_amdgcn_perm(y23, y01, 0x05040100u);                                      // d2
-          *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][1][wrow(prow)][off]) =
-              __builtin_amdgcn_perm(x23, x01, 0x07060302u) ^ 0x80808080u;                        // d1
-          *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][2][wrow(prow)][off]) =
-              __builtin_amdgcn_perm(x23, x01, 0x05040100u) ^ 0x80808080u;                        // d0
+          for (int bq = 0; bq < BPQ; ++bq) {
+            const int rr = hl * BPQ + bq;
+            // weights w = p s_v, zero past T (the scale reads as zero); fmas, so that a
+            // float16 scale enters v_fma_mix_f32 without a separate conversion.  Integer
+            // wi and its three digits from one float addition (kDigitBias)
+            uint32_t f[4];
+#pragma unroll
+            for (int hf = 0; hf < 4; ++hf) {
+              const float w = __builtin_fmaf(pr[s][hl][hf], sv[bq][hf], 0.0f);
+              if constexpr (ASYM) ob[qd][s][rr] = __builtin_fmaf(pr[s][hl][hf], zv[bq][hf], ob[qd][s][rr]);
+              f[hf] = __float_as_uint(__builtin_fmaf(w, winv[SHW ? 0 : bq], kDigitBias));
+            }
+            // byte transpose: digit plane k gets byte k of the four tokens' words; planes 0
+            // and 1 then flip bit 7 of every byte (the xor 0x80 of the digit rule)
+            const uint32_t x01 = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);   // f0.b0 f1.b0 f0.b1 f1.b1
+            const uint32_t x23 = __builtin_amdgcn_perm(f[3], f[2], 0x05010400u);
+            const uint32_t y01 = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);   // f0.b2 f1.b2 f0.b3 f1.b3
+            const uint32_t y23 = __builtin_amdgcn_perm(f[3], f[2], 0x07030602u);
+            const int prow = 4 * lq + rr;
+            const int off = 16 * slot16(j >> 2, prow) + 4 * (j & 3);
+            *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][0][wrow(prow)][off]) =
+                __builtin_amdgcn_perm(y23, y01, 0x05040100u);                                      // d2
+            *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][1][wrow(prow)][off]) =
+                __builtin_amdgcn_perm(x23, x01, 0x07060302u) ^ 0x80808080u;                        // d1
+            *reinterpret_cast<uint32_t*>(&wq_s[wave][qd][s][2][wrow(prow)][off]) =
+                __builtin_amdgcn_perm(x23, x01, 0x05040100u) ^ 0x80808080u;                        // d0
+          }
         }
       }
       if (qd > 0) {
@@ -640,7 +678,7 @@ void decode_grouped_kernel(const DecodeParams p) {
       // ---- P.V: rows (head, digit) of one quantisation block, K = the step's 64
       // tokens, 16 dims per instruction
       v4i pa[NI], pc[NI];
-      float pw[NI];
+      float pw[NI];   // weight scale of head 4 i + lq and the block
 #pragma unroll
       for (int nb = 0; nb < NBQ; ++nb) {
         if (nb == NBQ / 2) {
@@ -667,7 +705,7 @@ void decode_grouped_kernel(const DecodeParams p) {
             // symmetric: start each product at -2^(b-1) times the rows' digit sums
             pc[i] = ASYM ? v4i{0, 0, 0, 0} : mfma64(pa[i], excv, v4i{0, 0, 0, 0});
             const int hw = 4 * i + lq < G ? 4 * i + lq : 0;
-            pw[i] = wsg_s[wave][qd][hw * BPQ + bq];
+            pw[i] = wsg_s[wave][qd][SHW ? hw : hw * BPQ + bq];
           }
         }
         const int rrow = 16 * (nb % (NBQ / 2)) + j;
