@@ -1,7 +1,9 @@
 // Streaming-read probe (auxiliary, not part of the method): one pass over a device
-// buffer with 16-byte loads, grid-stride, the way the decode kernels stream the cache.
-// It gives the HBM read bandwidth a plain kernel reaches on the current GPU, the
+// buffer with 16-byte non-temporal loads, eight in flight per lane, grid-stride.  It
+// gives the HBM read bandwidth a plain streaming kernel reaches on the current GPU, the
 // practical ceiling beside the 8 TB/s peak against which the decode kernels are read.
+// (One load per lane per iteration without the non-temporal hint reads about 15 %
+// slower on MI355X; eight in flight with the hint is the fastest pattern measured.)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -10,14 +12,24 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, uint64_t n,
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+constexpr int kUnroll = 8;   // 16-byte loads in flight per lane
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const v4u* __restrict__ p, uint64_t n,
                                                           uint32_t* __restrict__ sink) {
   uint32_t a = 0;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * 256u;
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256u + threadIdx.x; i < n; i += stride) {
-    const uint4 x = p[i];
-    a ^= x.x + x.y + x.z + x.w;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * 256u * kUnroll;
+  // chunks of 256 kUnroll elements per workgroup; element i + 256 u of a chunk per lane
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256u * kUnroll + threadIdx.x;
+  for (; i + 256u * (kUnroll - 1) < n; i += stride) {
+    v4u x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = __builtin_nontemporal_load(p + i + 256u * u);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) a ^= x[u][0] + x[u][1] + x[u][2] + x[u][3];
   }
+  // the lane's elements of the last, partial chunk
+  for (; i < n; i += 256u) a ^= p[i][0];
   // a data-dependent store that (almost) never happens keeps the loads alive
   if (a == 0x9E3779B9u) sink[0] = a;
 }
@@ -34,8 +46,8 @@ extern "C" int okv_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, v
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
     return OKV_E_HIP;
   }
-  const dim3 grid(static_cast<unsigned>(cus > 0 ? 16 * cus : 4096));
+  const dim3 grid(static_cast<unsigned>(cus > 0 ? 64 * cus : 16384));
   hipLaunchKernelGGL(read_probe_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(hip_stream),
-                     static_cast<const uint4*>(buf), bytes / 16, sink);
+                     static_cast<const v4u*>(buf), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? OKV_OK : OKV_E_HIP;
 }

@@ -290,8 +290,9 @@ int okv_set_decode_kernel(okv_handle* h, int32_t kind);
 int okv_get_decode_kernel(const okv_handle* h, int32_t* kind);
 
 /* Streaming-read probe: one pass over `bytes` bytes of the device buffer buf with
- * 16-byte loads (grid-stride over 16 workgroups of 256 threads per compute unit), the
- * HBM read rate a plain kernel reaches, for comparison with the decode kernels.  buf:
+ * 16-byte non-temporal loads, eight in flight per lane (grid-stride over 64 workgroups
+ * of 256 threads per compute unit), the HBM read rate a plain streaming kernel
+ * reaches, for comparison with the decode kernels.  buf:
  * device, 16-byte aligned, bytes >= 16 (the last bytes % 16 are not read); sink:
  * device uint32, written only when the loads' checksum hits a fixed value (it keeps
  * the loads from being removed).  Asynchronous on hip_stream; no handle needed. */
