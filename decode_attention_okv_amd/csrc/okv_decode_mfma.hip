@@ -175,10 +175,12 @@ constexpr int waves_per_eu() {
   return wg >= cap ? cap : (wg >= 1 ? wg : 1);
 }
 
-// P.V weight scales: one per (head, step), shared by the head's blocks of a quad (the
-// blocks' value scales are of one magnitude, so sharing costs a row at most a few of its
-// 21 bits, and a head's row maximum is taken once instead of once per block), except
-// where the kernel runs at four waves per SIMD or with 4-bit codes: there the extra
+// P.V weight scales: one per (head, step), shared by the head's blocks of a quad, so a
+// head's row maximum is taken once instead of once per block.  A block whose weights
+// reach only 2^-k of the head's largest keeps 21 - k bits, and its share of the output
+// is smaller in the same proportion, so the error relative to the output stays that of
+// 21-bit weights (on the workloads' caches the blocks' scales are of one magnitude).
+// Not where the kernel runs at four waves per SIMD or with 4-bit codes: there the extra
 // live values spill or cost a resident wave, and one scale per (head, block) row is
 // faster.
 template <int D, int FMT, int BLOCK, int G, int BITS>
