@@ -198,6 +198,9 @@ void decode_grouped_kernel(const DecodeParams p) {
   constexpr int NI = SH::NI, NBPB = SH::NBPB, NS = SH::NS, MST = SH::MST, UB = SH::UB;
   constexpr bool ASYM = SH::ASYM;
   constexpr bool SHW = shared_weight_scale<D, FMT, BLOCK, G, BITS>();
+  // P.V results combined one 16-dim block late (a few more live registers: the same
+  // shapes as the shared weight scale)
+  constexpr bool DEFER = SHW;
   constexpr int NSC = SHW ? 1 : BPQ;   // weight scales per (lane head, quad)
   static_assert(BPQ >= 1 && BPQ <= 4 && G >= 2, "blocks of 32 .. 128 dims, query groups of two or more");
   constexpr int ROWB = BITS * D / 8;   // bytes per key row
@@ -681,6 +684,18 @@ void decode_grouped_kernel(const DecodeParams p) {
       // tokens, 16 dims per instruction
       v4i pa[NI], pc[NI];
       float pw[NI];   // weight scale of head 4 i + lq and the block
+      // rows 4 lq + d of ev: the three digit sums of head 4 i + lq for dims 16 nbx + j
+      auto combine = [&](const v4i* ev, const float* pws, int nbx) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int ai = combine3<16, 8>(ev[i][0], ev[i][1], ev[i][2]);
+          acc[qd][i][nbx] = __builtin_fmaf(pws[i], static_cast<float>(ai), acc[qd][i][nbx]);
+        }
+      };
+      // with DEFER, the products of the previous 16 dims are combined after this
+      // block's products are issued, so their results are read an instruction later
+      v4i ep[NI];
+      float pwp[NI];
 #pragma unroll
       for (int nb = 0; nb < NBQ; ++nb) {
         if (nb == NBQ / 2) {
@@ -713,14 +728,21 @@ void decode_grouped_kernel(const DecodeParams p) {
         const int rrow = 16 * (nb % (NBQ / 2)) + j;
         const uint4 x = *reinterpret_cast<const uint4*>(vrow + rrow * 64 + 16 * slot16(lq, rrow));
         const v4i bv = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w)};
+        v4i e[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const v4i e = mfma64(pa[i], bv, pc[i]);
-          // rows 4 lq + d: the three digit sums of head 4 i + lq
-          const int ai = combine3<16, 8>(e[0], e[1], e[2]);
-          acc[qd][i][nb] = __builtin_fmaf(pw[i], static_cast<float>(ai), acc[qd][i][nb]);
+        for (int i = 0; i < NI; ++i) e[i] = mfma64(pa[i], bv, pc[i]);
+        if constexpr (DEFER) {
+          if (nb > 0) combine(ep, pwp, nb - 1);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            ep[i] = e[i];
+            pwp[i] = pw[i];
+          }
+        } else {
+          combine(e, pw, nb);
         }
       }
+      if constexpr (DEFER) combine(ep, pwp, NBQ - 1);
       // the next quad or step overwrites this wave's LDS rows
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_wave_barrier();
