@@ -353,6 +353,31 @@ def test_error_paths():
     assert okv.okv_destroy(ctypes.c_void_p()) == okv.OKV_OK
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, (1 << 24) + 16 * 77])
+def test_read_probe(nbytes):
+    # the streaming-read probe reads floor(nbytes / 16) 16-byte elements and writes its
+    # sink only when a lane's checksum (xor of element sums) equals 0x9E3779B9: on a zero
+    # buffer it stays silent, and planting that value in the first or the last element
+    # (the ragged tail) makes exactly one lane write it; argument checks fail before any
+    # launch
+    _need_gpu()
+    import decode_attention_okv_amd as okv
+    magic = 0x9E3779B9 - (1 << 32)           # as int32
+    n = nbytes // 16
+    for planted in (None, 0, n - 1):
+        say("okv_read_probe", nbytes, "planted element", planted)
+        buf = torch.zeros(4 * n + 4, dtype=torch.int32, device="cuda")
+        if planted is not None:
+            buf[4 * planted] = magic
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        assert okv.okv_read_probe(buf.data_ptr(), nbytes, sink.data_ptr()) == okv.OKV_OK
+        torch.cuda.synchronize()
+        assert sink.cpu().tolist() == ([0, 0, 0, 0] if planted is None else [magic, 0, 0, 0]), planted
+    assert okv.okv_read_probe(buf.data_ptr() + 4, nbytes, sink.data_ptr()) == okv.OKV_E_ALIGN
+    assert okv.okv_read_probe(buf.data_ptr(), 15, sink.data_ptr()) == okv.OKV_E_INVALID
+    assert okv.okv_read_probe(0, nbytes, sink.data_ptr()) == okv.OKV_E_INVALID
+
+
 def test_append_overlaps_previous_decode():
     """One-token appends on a second stream, running concurrently with the previous
     decode, give the same outputs bit for bit as the same steps on one stream: an
