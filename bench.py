@@ -17,8 +17,10 @@ asymmetric 128K decode, the 32K GQA append-and-decode steps, the SO(4) d = 256
 prefill write and decode, the tiny one-head case), "hbm_read_probe" (a plain
 streaming-read kernel on the same GPU), "prefill_attn" (chunked-prefill attention
 over the packed cache), "code_widths" and "rotations" (2-/4-bit codes, the
-unrotated and SO(4) variants on the headline workload), "so4_calibration" and
-"cpu_baseline" (the CPU oracle on a bounded sample).
+unrotated and SO(4) variants on the headline workload), "so4_calibration",
+"cpu_baseline" (the CPU oracle on a bounded sample) and "gpu_under_load" (the
+firmware's clock, power and temperature tables during 2.5 s of untimed decode calls on
+the headline and the asymmetric 128K workloads, after every timed leg).
 """
 from __future__ import annotations
 
@@ -288,15 +290,126 @@ def write_record(wl, ms):
             "write_GBs": round(write_bytes_per_position(wl) * wl.tokens / (ms * 1e-3) / 1e9, 1)}
 
 
+class GpuMonitor:
+    """Clock, power and temperature of the benchmarked GPU from the power-management
+    firmware's metrics table (amdsmi, read-only; no HIP call).  The firmware refreshes
+    that table about once a second, so a daemon thread polls it while sustained untimed
+    work runs (never inside a timed region) and keeps each fresh table (a new firmware
+    timestamp).  If amdsmi is missing, cannot see the GPU, or does not answer within two
+    seconds, the record says so and the benchmark goes on."""
+
+    def __init__(self, pci):
+        import threading
+        self.pci, self.err, self.h = tuple(pci), None, None
+        self.samples, self.last_ts, self.on = [], None, threading.Event()
+        self.ready, self.stop = threading.Event(), threading.Event()
+        threading.Thread(target=self._run, daemon=True).start()
+        if not self.ready.wait(2.0):
+            self.err = "amdsmi did not answer within 2 s"
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            for h in amdsmi.amdsmi_get_processor_handles():
+                # "domain:bus:device.function", hexadecimal
+                dom, bus, dev_fn = str(amdsmi.amdsmi_get_gpu_device_bdf(h)).split(":")
+                if (int(dom, 16), int(bus, 16), int(dev_fn.split(".")[0], 16)) == self.pci:
+                    self.h = h
+                    break
+            if self.h is None:
+                raise RuntimeError("no amdsmi device at PCI %04x:%02x:%02x" % self.pci)
+            self.get = amdsmi.amdsmi_get_gpu_metrics_info
+            self.idle = self._read()[1]
+        except Exception as e:   # noqa: BLE001 - any failure only disables the record
+            self.err = " ".join(f"{type(e).__name__}: {e}".split())[:200]
+        self.ready.set()
+        while self.h is not None and not self.stop.is_set():
+            if self.on.wait(0.5) and not self.stop.is_set():
+                try:
+                    ts, rec = self._read()
+                    if ts != self.last_ts:
+                        self.last_ts = ts
+                        self.samples.append(rec)
+                except Exception:   # noqa: BLE001
+                    pass
+                time.sleep(0.005)
+
+    def _read(self):
+        m = self.get(self.h)
+        clk = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 65535]
+
+        def num(k):
+            v = m.get(k)
+            return v if isinstance(v, int) and 0 <= v < 65535 else None
+        return m.get("firmware_timestamp"), {
+            "gfxclk_mhz_per_xcd": clk, "socket_power_w": num("current_socket_power"),
+            "hotspot_c": num("temperature_hotspot"), "mem_c": num("temperature_mem")}
+
+    def start(self):
+        self.samples = []
+        if self.h is not None:
+            self.last_ts = self._read()[0]     # the table current now predates the load
+        self.on.set()
+
+    def record(self):
+        """Stop polling; the fresh tables seen since start()."""
+        self.on.clear()
+        time.sleep(0.01)
+        if self.err or self.h is None:
+            return {"unavailable": self.err or "no device"}
+        return {"idle_before": self.idle, "tables_under_load": list(self.samples)}
+
+    def close(self):
+        self.stop.set()
+        self.on.set()
+
+
+def gpu_clock_leg(name, dev, seconds=2.5):
+    """The workload's cache (prefill untimed), then untimed decode calls back to back for
+    `seconds` of wall time while the monitor collects the firmware's tables: the clock
+    and power the GPU holds under this load.  Runs after every timed leg."""
+    import torch
+
+    import okv_synth
+    wl = okv_synth.workload(name)
+    print(f"# leg {name}: {seconds} s of decode calls, clock and power", file=sys.stderr, flush=True)
+    cache = new_cache(wl, -(-(wl.tokens + 32) // 32) * 32, dev)
+    k, v = okv_synth.kv_tokens(wl, 0, wl.tokens, device=dev)
+    cache.write(k, v)
+    del k, v
+    q = okv_synth.queries(wl, 0, device=dev)
+    out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    MONITOR.start()
+    t_end, n = time.perf_counter() + seconds, 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            cache.decode_attn(q, out)
+        torch.cuda.synchronize()
+        n += 10
+    rec = {"workload": name, "decode_kernel": cache.decode_kernel(), "decode_calls": n, **MONITOR.record()}
+    cache.close()
+    del cache, q, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+MONITOR = None
+
+
 def settle(cache, q, out, ms):
-    """Untimed decode calls back to back for about `ms` milliseconds of GPU time: under
-    sustained load the GPU's power management lowers and then restores its clocks over
-    the first tens of calls (a transient of ~10 ms), and timed regions start after it, at
-    the steady state a decoder serving continuously runs in.  Returns the call count."""
+    """Untimed decode calls back to back for about `ms` milliseconds of GPU time, so that
+    timed regions start at the steady state a decoder serving continuously runs in.
+    Under sustained load the GPU's power management changes its clocks twice: a dip a
+    few milliseconds in that recovers after about 10 ms, then a slower rise; on the 128K
+    MHA decode the call time settles after about half a second of continuous load (in
+    runs of thousands of calls, 297-299 us per call over the first 0.5 s against 287-289
+    us after it).  Returns the call count."""
     import torch
     n, el = 0, 0.0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    while el < ms and n < 1000:
+    while el < ms:
         e0.record()
         for _ in range(10):
             cache.decode_attn(q, out)
@@ -532,9 +645,13 @@ def main():
     ap.add_argument("--series", type=int, default=0,
                     help="also time this many back-to-back decode calls one by one after the probe "
                          "(the clock transient under sustained load; 0 to skip)")
-    ap.add_argument("--settle-ms", type=float, default=60.0,
-                    help="untimed decode calls (GPU milliseconds) before the warm-up steps, past the "
-                         "clock transient of the first tens of calls (0 to skip)")
+    ap.add_argument("--gpu-monitor", type=int, default=1,
+                    help="after the timed regions, 2.5 s of untimed decode calls while the "
+                         "firmware's clock / power / temperature tables are read (amdsmi, "
+                         "read-only; 0 to skip)")
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="untimed decode calls (GPU milliseconds) before the warm-up steps, until the "
+                         "GPU's clocks have settled under the load (0 to skip)")
     ap.add_argument("--prefill-workload", default="gqa_h32kv8_t32k",
                     help="workload of the chunked-prefill attention leg ('' to skip)")
     ap.add_argument("--prefill-rows", type=int, default=2048)
@@ -574,6 +691,10 @@ def main():
     cap = -(-(T0 + W + 2 * K + 1) // 32) * 32
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    global MONITOR
+    if args.gpu_monitor:
+        pr = torch.cuda.get_device_properties(0)
+        MONITOR = GpuMonitor((pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id))
     cache = new_cache(wl, cap, dev)
     if args.splits:
         cache.set_splits(args.splits)
@@ -695,6 +816,10 @@ def main():
         res["so4_calibration"] = calibration_leg()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
+    if MONITOR is not None:
+        res["gpu_under_load"] = [gpu_clock_leg(n, dev) for n in
+                                 [wl.name] + [x for x in legs if x == "gqa_b16h64kv8_t128k_asym"]]
+        MONITOR.close()
     print(json.dumps(res), flush=True)
 
 
