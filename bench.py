@@ -18,7 +18,9 @@ prefill write and decode, the tiny one-head case), "hbm_read_probe" (a plain
 streaming-read kernel on the same GPU), "prefill_attn" (chunked-prefill attention
 over the packed cache), "code_widths" and "rotations" (2-/4-bit codes, the
 unrotated and SO(4) variants on the headline workload), "so4_calibration",
-"cpu_baseline" (the CPU oracle on a bounded sample) and "gpu_under_load" (the
+"cpu_baseline" (the CPU oracle on a bounded sample), "oracle_spot_check" (the oracle's
+write and decode of one (sequence, KV head) of the timed cache, compared with the
+library's bytes and output) and "gpu_under_load" (the
 firmware's clock, power and temperature tables during 2.5 s of untimed decode calls on
 the headline and the asymmetric 128K workloads, after every timed leg).
 """
@@ -199,6 +201,65 @@ def calibration_leg(name="so4_d256_b32_t8k", n=16384, sweeps=4, n_cand=16):
             "error_before": round(float(trace[0]), 1), "error_after": round(float(trace[-1]), 1)}
 
 
+def capture_unit(cache, wl, unit_kv, news, q, out):
+    """Host copies, for the oracle spot check, of (sequence 0, KV head 0) of the timed
+    cache at its final length: the raw keys and values written (prefill and every
+    append, in order), the cache bytes, and the last decode call's query and output for
+    the KV head's query heads."""
+    import numpy as np
+
+    import okv_synth
+    t, g = cache.length, wl.group
+    ntile = -(-t // 32)
+    app_k = np.stack([okv_synth.host_f32(n[0][0, 0, 0]) for n in news])
+    app_v = np.stack([okv_synth.host_f32(n[1][0, 0, 0]) for n in news])
+    assert unit_kv["k"].shape[0] + app_k.shape[0] == t, (unit_kv["k"].shape, app_k.shape, t)
+    return {"t": t, "k": np.concatenate([unit_kv["k"], app_k]), "v": np.concatenate([unit_kv["v"], app_v]),
+            "k_codes": cache.k_codes[0, 0, :t].cpu().numpy(), "v_codes": cache.v_codes[0, 0, :ntile].cpu().numpy(),
+            "k_meta": cache.k_meta[0, 0, :t].cpu().numpy(), "v_meta": cache.v_meta[0, 0, :t].cpu().numpy(),
+            "q": okv_synth.host_f32(q)[0, :g], "y": out[0, :g].cpu().numpy()}
+
+
+def oracle_spot_check(wl, spot):
+    """The CPU oracle's write of the captured unit's raw keys and values, compared byte
+    for byte with the library's cache of that unit; the exact rounding ties among its
+    values (a rotated value on a threshold of its stored scale); and the oracle's decode
+    of the last query against the library's output (max |y - y_ref| / RMS(y_ref))."""
+    import numpy as np
+
+    import okv_synth
+    import oracle
+    unit = wl.with_(batch=1, hkv=1, hq=wl.group)
+    p32 = okv_synth.rotation_params(unit, dtype=np.float32)
+    u = oracle.rotation_matrix(unit.rotation, p32.astype(np.float64), unit.d)
+    t0 = time.perf_counter()
+    ref = oracle.write_unit(spot["k"], spot["v"], unit, p32)
+    mism = {}
+    for key in ("k_codes", "v_codes", "k_meta", "v_meta"):
+        a = np.ascontiguousarray(spot[key]).view(np.uint8)
+        b = np.ascontiguousarray(np.asarray(ref[key])).view(np.uint8)
+        mism[key] = int(np.count_nonzero(a != b)) if a.shape == b.shape else -1
+    ties = 0
+    for key, mkey in (("k_rot", "k_meta"), ("v_rot", "v_meta")):
+        y = ref[key].astype(np.float64)
+        sc, off = oracle.meta_values(ref[mkey], unit)
+        yb = y.reshape(y.shape[0], unit.d // unit.block, unit.block)
+        if unit.quant == "sym":
+            x = yb / sc[..., None]
+        else:
+            x = (yb.astype(np.float32) - off[..., None].astype(np.float32)).astype(np.float64) / sc[..., None]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            ties += int(np.count_nonzero(x - np.floor(x) == 0.5))
+    y_ref = oracle.attend_unit(spot["q"], ref["k_codes"], ref["k_meta"], ref["v_codes"], ref["v_meta"],
+                               spot["t"], unit, u)
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    err = float(np.abs(spot["y"].astype(np.float64) - y_ref).max() / rms)
+    return {"unit": "sequence 0, KV head 0 of the timed cache", "tokens": spot["t"],
+            "byte_mismatches": mism, "exact_ties": ties, "decode_max_err_over_rms": float("%.3g" % err),
+            "bound": 2e-3, "ok": all(v == 0 for v in mism.values()) and err <= 2e-3,
+            "oracle_s": round(time.perf_counter() - t0, 1)}
+
+
 def cpu_baseline(wl, target_s=12.0):
     """Time the CPU oracle's decode on (sequence, KV head) units of the workload at
     its full context length (same distributions; values drawn on the host)."""
@@ -262,17 +323,20 @@ def new_cache(wl, cap, dev, bits=None):
                         device=dev, bits=wl.bits if bits is None else bits)
 
 
-def timed_prefill(cache, wl, dev, warm=20, reps=10):
+def timed_prefill(cache, wl, dev, warm=20, reps=10, keep_unit=None):
     """okv_write of the workload's whole context in one call.  A first untimed call on
     the first 32 positions loads the kernel; the first whole write is timed on its own
     (the GPU comes from idle), then `warm` untimed and `reps` timed whole writes, each
     rewinding the cache to 0 first (the same work every time: the clocks pass through
     the same transient as for decode calls, and settle within about 20 writes).
-    Returns (median ms of the timed writes, ms of the first one)."""
+    Returns (median ms of the timed writes, ms of the first one).  `keep_unit`, a dict,
+    receives float32 host copies of the keys and values of (sequence 0, KV head 0)."""
     import torch
 
     import okv_synth
     k, v = okv_synth.kv_tokens(wl, 0, wl.tokens, device=dev)
+    if keep_unit is not None:
+        keep_unit["k"], keep_unit["v"] = okv_synth.host_f32(k[0, :, 0]), okv_synth.host_f32(v[0, :, 0])
     cache.write(k[:, :32].contiguous(), v[:, :32].contiguous())
     torch.cuda.synchronize()
 
@@ -718,7 +782,8 @@ def main():
         cache.set_splits(args.splits)
 
     # ---- prefill (timed separately: okv_write tokens/s)
-    prefill_ms = timed_prefill(cache, wl, dev)
+    unit_kv = None if args.no_cpu_baseline else {}
+    prefill_ms = timed_prefill(cache, wl, dev, keep_unit=unit_kv)
     print(f"# prefill {T0} tokens x {wl.batch} seq: {prefill_ms[0]:.3f} ms (first {prefill_ms[1]:.3f} ms)",
           file=sys.stderr, flush=True)
 
@@ -771,6 +836,7 @@ def main():
     cache.timing(False)
     assert ncalls == K, (ncalls, K)
     assert torch.isfinite(out).all()
+    spot = None if unit_kv is None else capture_unit(cache, wl, unit_kv, news, qs[steps - 1], out)
 
     res = {
         "metric": METRIC,
@@ -839,6 +905,7 @@ def main():
         res["so4_calibration"] = calibration_leg()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
+        res["oracle_spot_check"] = oracle_spot_check(wl, spot)
     if MONITOR is not None:
         res["gpu_under_load"] = [gpu_clock_leg(n, dev) for n in
                                  [wl.name] + [x for x in legs if x == "gqa_b16h64kv8_t128k_asym"]]
