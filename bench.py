@@ -78,11 +78,13 @@ def recorded_traffic(wl, kernel):
     return int(rec["read_bytes"]) + int(rec["write_bytes"])
 
 
-def prefill_attn_leg(name, rows, reps=5):
+def prefill_attn_leg(name, rows, reps=5, settle_s=1.5):
     """Chunked-prefill attention over the packed cache: the last `rows` positions of a
     full context attend causally (okv_prefill_attn).  Algorithmic work: 4 d flops per
-    (query head, causal query-key pair), QK^T and P.V; the kernel issues each product
-    twice (float16 hi + lo), which the f16 MFMA peak fraction does not count."""
+    (query head, causal query-key pair), QK^T and P.V; the kernel issues the products
+    two or three times (float16 hi + lo parts), which the f16 MFMA peak fraction does
+    not count.  `ms` is the median of 2 reps calls after `settle_s` seconds of untimed
+    calls; `ms_first_calls` the mean of the first `reps` calls after one untimed call."""
     import numpy as np
     import torch
 
@@ -103,19 +105,30 @@ def prefill_attn_leg(name, rows, reps=5):
     out = torch.empty((wl.batch, rows, wl.hq, wl.d), dtype=torch.float32, device="cuda")
     cache.prefill_attn(q, out=out)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        cache.prefill_attn(q, out=out)
-    e1.record()
-    torch.cuda.synchronize()
+
+    def timed(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record()
+        for i in range(n):
+            cache.prefill_attn(q, out=out)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+
+    first = timed(reps)
+    # then untimed calls for `settle_s` seconds, so that the timed calls run at the
+    # clocks the GPU holds under this load, as for the decode legs
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        timed(10)
+    ms = timed(2 * reps)[reps]
     assert torch.isfinite(out).all()
-    ms = e0.elapsed_time(e1) / reps
     pairs = rows * (t - rows) + rows * (rows + 1) // 2
     flops = 4.0 * wl.d * wl.hq * wl.batch * pairs
     cache.close()
     return {
-        "workload": wl.name, "context": t, "rows": rows, "calls": reps, "ms": round(ms, 3),
+        "workload": wl.name, "context": t, "rows": rows, "calls": 2 * reps, "ms": round(ms, 3),
+        "ms_first_calls": round(sum(first) / reps, 3), "settle_s": settle_s,
         "tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 1),
         "frac_f16_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS, 4),
     }
@@ -733,7 +746,8 @@ def main():
                          "read-only; 0 to skip)")
     ap.add_argument("--settle-ms", type=float, default=1500.0,
                     help="untimed decode calls (GPU milliseconds) before the warm-up steps, until the "
-                         "GPU's clocks have settled under the load (0 to skip)")
+                         "GPU's clocks have settled under the load; the prefill-attention leg runs "
+                         "untimed calls for as many wall-clock milliseconds (0 to skip)")
     ap.add_argument("--prefill-workload", default="gqa_h32kv8_t32k",
                     help="workload of the chunked-prefill attention leg ('' to skip)")
     ap.add_argument("--prefill-rows", type=int, default=2048)
@@ -900,7 +914,8 @@ def main():
         # sign rotation with D = I: same kernels and bytes as the headline)
         res["rotations"] = [variant_leg(wl, rotation="none", block=wl.d), variant_leg(wl, rotation="so4")]
     if args.prefill_workload:
-        res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows)
+        res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows,
+                                               settle_s=args.settle_ms / 1000.0)
     if args.calibration:
         res["so4_calibration"] = calibration_leg()
     if not args.no_cpu_baseline:
