@@ -134,10 +134,11 @@ def prefill_attn_leg(name, rows, reps=5, settle_s=1.5):
     }
 
 
-def variant_leg(wl, calls=10, **over):
+def variant_leg(wl, calls=10, settle_ms=0.0, **over):
     """One variant of the workload (another code width, rotation or block): write the
-    context (timed with events around all write calls), then time `calls` decode calls
-    at full length with HIP events on the attention kernel's own dispatch."""
+    context (timed with events around all write calls), then, after `settle_ms` of
+    untimed decode calls, time `calls` decode calls at full length with HIP events on
+    the attention kernel's own dispatch."""
     import numpy as np
     import torch
 
@@ -166,6 +167,8 @@ def variant_leg(wl, calls=10, **over):
     for _ in range(3):
         cache.decode_attn(q, out)
     torch.cuda.synchronize()
+    if settle_ms > 0:
+        settle(cache, q, out, settle_ms)
     cache.timing(True)
     for _ in range(calls):
         cache.decode_attn(q, out)
@@ -908,11 +911,12 @@ def main():
     if args.series:
         res["sustained_series"] = series_leg(wl.name, dev, args.series)
     if args.widths:
-        res["code_widths"] = [variant_leg(wl, bits=int(b)) for b in args.widths.split(",")]
+        res["code_widths"] = [variant_leg(wl, settle_ms=args.settle_ms, bits=int(b)) for b in args.widths.split(",")]
     if args.rotations:
         # the unrotated per-token baseline and U = B H (the Hadamard-only variant is the
         # sign rotation with D = I: same kernels and bytes as the headline)
-        res["rotations"] = [variant_leg(wl, rotation="none", block=wl.d), variant_leg(wl, rotation="so4")]
+        res["rotations"] = [variant_leg(wl, settle_ms=args.settle_ms, rotation="none", block=wl.d),
+                            variant_leg(wl, settle_ms=args.settle_ms, rotation="so4")]
     if args.prefill_workload:
         res["prefill_attn"] = prefill_attn_leg(args.prefill_workload, args.prefill_rows,
                                                settle_s=args.settle_ms / 1000.0)
