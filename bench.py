@@ -630,9 +630,10 @@ def decode_workload_leg(name, dev, calls=20, settle_ms=0.0):
     return rec
 
 
-def steps_leg(name, dev):
-    """The 32K GQA workload as its configuration runs it: prefill write (timed), then
-    wl.decode_steps serial steps of (append one token, decode), timed as a whole."""
+def steps_leg(name, dev, settle_ms=0.0):
+    """The 32K GQA workload as its configuration runs it: prefill write (timed), then,
+    after `settle_ms` of untimed decode calls, wl.decode_steps serial steps of (append
+    one token, decode), timed as a whole."""
     import torch
 
     import okv_synth
@@ -644,6 +645,8 @@ def steps_leg(name, dev):
     news = [okv_synth.kv_tokens(wl, wl.tokens + i, 1, device=dev, step=i) for i in range(n + 2)]
     qs = [okv_synth.queries(wl, i, device=dev) for i in range(n + 2)]
     out = torch.empty((wl.batch, wl.hq, wl.d), dtype=torch.float32, device=dev)
+    if settle_ms > 0:
+        settle(cache, qs[0], out, settle_ms)
     for i in range(2):                      # warm-up steps (appended tokens stay)
         cache.write(*news[i])
         cache.decode_attn(qs[i], out)
@@ -901,7 +904,7 @@ def main():
         res["workloads"] = []
         for name in legs:
             if name == "gqa_h32kv8_t32k":
-                res["workloads"].append(steps_leg(name, dev))
+                res["workloads"].append(steps_leg(name, dev, settle_ms=args.settle_ms))
             elif name == "tiny_d128_t256":
                 res["workloads"].append(tiny_leg(dev))
             else:
