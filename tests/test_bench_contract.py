@@ -57,3 +57,46 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _spot(name, t):
+    """A spot-check record built from the oracle's own write and decode of a small unit
+    (what the library would report if it matched the oracle exactly)."""
+    import numpy as np
+
+    import oracle
+    wl = okv_synth.workload(name)
+    unit = wl.with_(batch=1, hkv=1, hq=wl.group)
+    p32 = okv_synth.rotation_params(unit, dtype=np.float32)
+    u = oracle.rotation_matrix(unit.rotation, p32.astype(np.float64), unit.d)
+    k, v = okv_synth.kv_tokens(unit, 0, t)
+    kh, vh = okv_synth.host_f32(k)[0, :, 0], okv_synth.host_f32(v)[0, :, 0]
+    ref = oracle.write_unit(kh, vh, unit, p32)
+    q = okv_synth.host_f32(okv_synth.queries(unit, 0))[0]
+    y = oracle.attend_unit(q, ref["k_codes"], ref["k_meta"], ref["v_codes"], ref["v_meta"], t, unit, u)
+    return wl, {"t": t, "k": kh, "v": vh, "k_codes": ref["k_codes"].copy(), "v_codes": ref["v_codes"].copy(),
+                "k_meta": np.array(ref["k_meta"]), "v_meta": np.array(ref["v_meta"]), "q": q,
+                "y": y.astype(np.float32)}
+
+
+@pytest.mark.parametrize("name", ["tiny_d128_t256", "gqa_b16h64kv8_t128k_asym"])
+def test_oracle_spot_check_flags_mismatches(name):
+    """bench.py's spot check passes a faithful unit and flags a flipped code bit, a
+    changed scale byte and an output off by 1 % of its RMS."""
+    import numpy as np
+    wl, spot = _spot(name, 97)
+    rec = bench.oracle_spot_check(wl, spot)
+    assert rec["ok"] and rec["byte_mismatches"] == {"k_codes": 0, "v_codes": 0, "k_meta": 0, "v_meta": 0}
+    assert rec["decode_max_err_over_rms"] < 1e-6
+    bad = dict(spot, v_codes=spot["v_codes"].copy())
+    bad["v_codes"].reshape(-1)[7] ^= 4
+    rec = bench.oracle_spot_check(wl, bad)
+    assert not rec["ok"] and rec["byte_mismatches"]["v_codes"] == 1
+    bad = dict(spot, k_meta=spot["k_meta"].copy())
+    bad["k_meta"].view(np.uint8).reshape(-1)[3] ^= 1
+    rec = bench.oracle_spot_check(wl, bad)
+    assert not rec["ok"] and rec["byte_mismatches"]["k_meta"] == 1
+    y = spot["y"].astype(np.float64)
+    bad = dict(spot, y=(y + 0.01 * np.sqrt(np.mean(y ** 2))).astype(np.float32))
+    rec = bench.oracle_spot_check(wl, bad)
+    assert not rec["ok"] and 0.009 < rec["decode_max_err_over_rms"] < 0.011
