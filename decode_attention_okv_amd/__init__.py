@@ -131,10 +131,21 @@ def _check(status: int, where: str) -> None:
         raise OkvError(status, where)
 
 
-def _stream_ptr(stream):
+def _stream_ptr(stream, device=None):
+    """HIP stream handle for a call: `stream` (a torch stream or a raw handle), or by
+    default torch's current stream of `device` (a torch.device or index; the current
+    device when None).  torch's raw-handle query costs a fraction of a microsecond, where
+    building a Stream object costs about three, a noticeable part of a small call."""
     if stream is None:
         import torch
-        stream = torch.cuda.current_stream()
+        idx = torch.cuda.current_device() if device is None else (
+            device.index if isinstance(device, torch.device) else int(device))
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return ctypes.c_void_p(raw(idx))
+        stream = torch.cuda.current_stream(idx)
+    if isinstance(stream, ctypes.c_void_p):
+        return stream
     return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
 
 
@@ -361,19 +372,23 @@ class OkvCache:
             raise ValueError(f"expected contiguous {want} {tuple(shape)} on {self.device}, "
                              f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
+    def _stream(self, stream):
+        # the current stream of the cache's own device unless one is given
+        return _stream_ptr(stream, self.device) if stream is None else stream
+
     def write(self, k, v, stream=None):
         n_new = k.shape[1]
         shape = (self.batch, n_new, self.hkv, self.d)
         self._in_check(k, shape)
         self._in_check(v, shape)
-        _check(okv_write(self.handle, k.data_ptr(), v.data_ptr(), n_new, stream), "okv_write")
+        _check(okv_write(self.handle, k.data_ptr(), v.data_ptr(), n_new, self._stream(stream)), "okv_write")
 
     def decode_attn(self, q, out=None, stream=None):
         import torch
         self._in_check(q, (self.batch, self.hq, self.d))
         if out is None:
             out = torch.empty((self.batch, self.hq, self.d), dtype=torch.float32, device=self.device)
-        _check(okv_decode_attn(self.handle, q.data_ptr(), out.data_ptr(), stream), "okv_decode_attn")
+        _check(okv_decode_attn(self.handle, q.data_ptr(), out.data_ptr(), self._stream(stream)), "okv_decode_attn")
         return out
 
     def prefill_attn(self, q, out=None, stream=None):
@@ -383,7 +398,7 @@ class OkvCache:
         self._in_check(q, (self.batch, n, self.hq, self.d))
         if out is None:
             out = torch.empty((self.batch, n, self.hq, self.d), dtype=torch.float32, device=self.device)
-        _check(okv_prefill_attn(self.handle, q.data_ptr(), n, out.data_ptr(), stream), "okv_prefill_attn")
+        _check(okv_prefill_attn(self.handle, q.data_ptr(), n, out.data_ptr(), self._stream(stream)), "okv_prefill_attn")
         return out
 
     @property
