@@ -929,8 +929,11 @@ def main():
         res["cpu_baseline"] = cpu_baseline(wl)
         res["oracle_spot_check"] = oracle_spot_check(wl, spot)
     if MONITOR is not None:
-        res["gpu_under_load"] = [gpu_clock_leg(n, dev) for n in
-                                 [wl.name] + [x for x in legs if x == "gqa_b16h64kv8_t128k_asym"]]
+        if MONITOR.err or MONITOR.h is None:
+            res["gpu_under_load"] = {"unavailable": MONITOR.err or "no device"}
+        else:
+            res["gpu_under_load"] = [gpu_clock_leg(n, dev) for n in
+                                     [wl.name] + [x for x in legs if x == "gqa_b16h64kv8_t128k_asym"]]
         MONITOR.close()
     print(json.dumps(res), flush=True)
 
