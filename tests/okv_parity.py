@@ -92,3 +92,13 @@ def free_gpu():
     gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+def zero_token_attention(q1, k_hat, v_hat, n_zero):
+    """Softmax attention of the rows q1 (G, d) over the given keys / values plus n_zero
+    tokens whose key and value are zero vectors (float64): such a token has logit 0 and
+    adds exp(-m) to the denominator only (m = max(0, largest logit))."""
+    logits = q1 @ k_hat.T / np.sqrt(q1.shape[-1])
+    m = np.maximum(logits.max(axis=1, keepdims=True), 0.0)
+    p = np.exp(logits - m)
+    return (p @ v_hat) / (p.sum(axis=1, keepdims=True) + n_zero * np.exp(-m))

@@ -151,3 +151,26 @@ def test_attend_unit_lengths_equals_attend_unit_per_length():
     sd = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q.astype(np.float64))[None], torch.from_numpy(kx)[None], torch.from_numpy(vx)[None])[0]
     assert np.allclose(got[2], sd.numpy(), atol=1e-10)
+
+
+def test_zero_tokens_closed_form():
+    """Tokens whose key and value are zero vectors (zero codes with a zero scale) have
+    logit 0 and add only exp(-m) to the denominator: the closed form the largest-slice
+    GPU test uses equals the oracle's attention with those rows spelled out, also when
+    every real logit is negative (then m = 0 comes from the zero tokens)."""
+    from okv_parity import zero_token_attention
+    rng = np.random.default_rng(5)
+    for shift in (0.0, -40.0):
+        q = rng.standard_normal((3, 16))
+        k = rng.standard_normal((7, 16)) * 3
+        v = rng.standard_normal((7, 16))
+        n0 = 11
+        k_all = np.concatenate([k, np.zeros((n0, 16))])
+        v_all = np.concatenate([v, np.zeros((n0, 16))])
+        # a negative shift of every real logit: add a constant key component
+        qs = np.concatenate([q, np.ones((3, 1))], axis=1)
+        ks = np.concatenate([k_all, np.concatenate([np.full((7, 1), shift * np.sqrt(17)), np.zeros((n0, 1))])], axis=1)
+        vs = np.concatenate([v_all, np.zeros((7 + n0, 1))], axis=1)
+        want = oracle.attend_exact(qs, ks, vs)
+        got = zero_token_attention(qs, ks[:7], vs[:7], n0)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
