@@ -70,6 +70,8 @@ int validate_shape(const okv_config* c) {
   }
   // valid, but only these are built
   if (c->head_dim != 128 && c->head_dim != 256) return OKV_E_UNSUPPORTED;
+  // sequences and query heads are launch grid dimensions (y and z) of the kernels
+  if (c->batch > 65535 || c->num_q_heads > 65535) return OKV_E_UNSUPPORTED;
   if (c->block % 32 != 0) return OKV_E_UNSUPPORTED;
   // the kernels address one (sequence, KV head) slice of a cache buffer with 32-bit
   // byte offsets (buffer resources), up to 128 tokens past its end: the packed codes

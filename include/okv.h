@@ -113,13 +113,13 @@ typedef enum okv_rotation { OKV_ROT_SIGN = 0, OKV_ROT_SO4 = 1, OKV_ROT_NONE = 2 
 
 typedef struct okv_config {
   int32_t abi_version;   /* must be OKV_ABI_VERSION */
-  int32_t batch;         /* sequences, >= 1 */
-  int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads */
+  int32_t batch;         /* sequences, >= 1; this build: <= 65535 (a launch grid dimension) */
+  int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads; this build: <= 65535 */
   int32_t num_kv_heads;  /* >= 1 */
   int32_t head_dim;      /* d: power of two, 4 | d; this build: 128 or 256 */
   int32_t max_tokens;    /* cache capacity per sequence, multiple of 32; this build:
                           * (max_tokens + 128) * bits * head_dim / 8 < 2^32 */
-  int32_t block;         /* quantisation block m: m | d, 8 | m; this build: 32 or 64 */
+  int32_t block;         /* quantisation block m: m | d, 8 | m; this build: 32 | m */
   int32_t quant;         /* okv_quant */
   int32_t scale_dtype;   /* OKV_DT_F32 or OKV_DT_F16 (SYM); OKV_DT_E4M3 (ASYM) */
   int32_t in_dtype;      /* OKV_DT_F32 or OKV_DT_BF16: type of k, v and q */

@@ -130,6 +130,14 @@ int main() {
     rejects(big, OKV_E_UNSUPPORTED, __LINE__);
     big.max_tokens = 2147483616;   // the largest multiple of 32 in int32
     rejects(big, OKV_E_UNSUPPORTED, __LINE__);
+    big = base(s128);
+    big.batch = 65535;             // the largest grid dimension
+    EXPECT(okv_layout(&big, &info) == OKV_OK);
+    big.batch = 65536;
+    rejects(big, OKV_E_UNSUPPORTED, __LINE__);
+    big = base(s128);
+    big.num_q_heads = 65536;
+    rejects(big, OKV_E_UNSUPPORTED, __LINE__);
   }
   {
     // field by field rejections

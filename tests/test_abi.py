@@ -85,6 +85,8 @@ def test_layout_sizes():
     (dict(max_tokens=89478368), okv.OKV_E_UNSUPPORTED),   # 48 B rows: (89478368 + 128) x 48 > 2^32
     (dict(max_tokens=44739264, head_dim=256, rot_params=[1.0] * 256), okv.OKV_E_UNSUPPORTED),
     (dict(max_tokens=67108736, bits=4), okv.OKV_E_UNSUPPORTED),   # 64 B rows: (67108736 + 128) x 64 >= 2^32
+    (dict(batch=65536), okv.OKV_E_UNSUPPORTED),                    # launch grid dimensions
+    (dict(num_q_heads=65536, num_kv_heads=2), okv.OKV_E_UNSUPPORTED),
 ])
 def test_rejections(kw, status):
     cfg = base(**{k: v for k, v in kw.items() if k != "abi_version"})
