@@ -602,7 +602,7 @@ def decode_record(wl, t, call_us, attn_us, red_us, kernel, splits):
             "call_frac_hbm_peak": round((kern_b + ob) / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def decode_workload_leg(name, dev, calls=20, settle_ms=0.0):
+def decode_workload_leg(name, dev, calls=100, settle_ms=0.0):
     """A decode workload at its full size: prefill write (timed), then `calls` decode
     calls back to back.  Reports write rates, decode call / kernel times, GB/s and the
     fraction of the HBM peak, and the recorded HBM traffic of the decode kernel."""
