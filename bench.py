@@ -873,7 +873,8 @@ def main():
         "data": "synthetic",
         "seeds": "okv_synth: NumPy SeedSequence([workload id, stream, ...]) per draw (rotation, "
                  "channel scales, outliers); torch generators seeded from SeedSequence([workload id, "
-                 "stream, step + 1, first position]) for keys, values and queries",
+                 "stream, step + 1, first position]) for keys and values, ([workload id, stream, "
+                 "step]) for decode queries",
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.hq, "kv_heads": wl.hkv,
                    "head_dim": wl.d, "context": T0, "quant": wl.quant, "block": wl.block,
                    "scale_dtype": wl.scale_dtype, "rotation": wl.rotation, "splits": splits},
