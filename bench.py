@@ -447,7 +447,10 @@ class GpuMonitor:
     def start(self):
         self.samples = []
         if self.h is not None:
-            self.last_ts = self._read()[0]     # the table current now predates the load
+            try:
+                self.last_ts = self._read()[0]     # the table current now predates the load
+            except Exception:   # noqa: BLE001 - a failed read only loses this table
+                self.last_ts = None
         self.on.set()
 
     def record(self):
