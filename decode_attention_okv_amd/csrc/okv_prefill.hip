@@ -260,23 +260,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 
   const int n_kt = pos_last / kKT + 1;                // key tiles any row of the group sees
   // ---- raw tile data in registers, loaded one tile ahead: key code groups, the wave's
-  // value code groups, and the metadata of the wave's blocks (token = lane)
+  // value code groups, and the metadata of the wave's blocks (token = lane).  Byte
+  // offsets are unsigned 32-bit: a slice of packed codes reaches up to 4 GiB.
   constexpr int KGT = (kKT * NG + 255) / 256;         // key groups per thread
   uint32_t kw[KGT][BITS], vw[VGW][BITS], kmr[NBW], vmr[NBW];
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < KGT; ++i) {
       const int e = tid + 256 * i;
-      buf_group<BITS>(rk, static_cast<uint32_t>((t0 + e / NG) * ROWB + GB * (e % NG)), kw[i]);
+      buf_group<BITS>(rk, static_cast<uint32_t>(t0 + e / NG) * ROWB + GB * (e % NG), kw[i]);
     }
 #pragma unroll
     for (int i = 0; i < VGW; ++i) {
       const int grp = lane + 64 * i, dim = wave * WD + grp % WD, half = grp / WD;
-      buf_group<BITS>(rv, static_cast<uint32_t>((t0 / kTile + half) * D * GB + GB * dim), vw[i]);
+      buf_group<BITS>(rv, (static_cast<uint32_t>(t0 / kTile) + half) * (D * GB) + GB * dim, vw[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-      const uint32_t off = static_cast<uint32_t>(((t0 + lane) * NBLK + blk0 + i) * MB);
+      const uint32_t off = (static_cast<uint32_t>(t0 + lane) * NBLK + blk0 + i) * MB;
       kmr[i] = buf_meta<FMT>(rkm, off, 0);
       vmr[i] = buf_meta<FMT>(rvm, off, 0);
     }
