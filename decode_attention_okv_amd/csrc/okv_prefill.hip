@@ -236,7 +236,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   // per lane: softmax state of query j (replicated over lq, partial sums per lane);
   // accumulators of queries 4 lq + r, dims 16 nt + j
   const int my_pos = pos_first + 16 * wave + j;      // position of this lane's query
-  float m_run = -INFINITY, l_run = 0.0f;
+  // l_run: the row's running softmax sum, added to once per tile with a compensated
+  // (Kahan) sum, l_cmp holding the part rounded away: one float32 sum over a prefix of
+  // millions of near-equal terms would otherwise drift by up to n 2^-24 of itself
+  float m_run = -INFINITY, l_run = 0.0f, l_cmp = 0.0f;
   float zacc[NZ];                                     // asymmetric values: sum of p z_v per block
 #pragma unroll
   for (int z = 0; z < NZ; ++z) zacc[z] = 0.0f;
@@ -413,6 +416,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      l_cmp *= alpha;
 #pragma unroll
       for (int z = 0; z < NZ; ++z) zacc[z] *= alpha;
       m_run = m_new;
@@ -429,12 +433,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     // as the A operand of P.V: K chunk cc covers tokens 32 cc + 4 lq + r and
     // 32 cc + 16 + 4 lq + r.  p <= 2^8 (lazy maximum), so float16 holds it.
     h8 ph[2], pl[2];
+    float l_tile = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pr = __builtin_amdgcn_exp2f(sv[tt][r] - m_run);
-        l_run += pr;
+        l_tile += pr;
         const H2 xs = split_h16(pr);
         ph[tt >> 1][4 * (tt & 1) + r] = xs.hi;
         pl[tt >> 1][4 * (tt & 1) + r] = xs.lo;
@@ -445,6 +450,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
             zacc[blk] = __builtin_fmaf(pr, vmz_s[blk][16 * tt + 4 * lq + r], zacc[blk]);
         }
       }
+    {
+      const float y = l_tile - l_cmp;
+      const float t = l_run + y;
+      l_cmp = (t - l_run) - y;
+      l_run = t;
+    }
     // ---- P.V: ph vh + ph vl + pl vh per 32-token chunk, scaled back by the normaliser
     // of the wave that unpacked the dims
     float gw[4];
@@ -476,6 +487,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   }
 
   // ---- normalise: l (and the zero-point sums) of query j sum the four lanes of the query
+  l_run -= l_cmp;
   l_run += swz_xor16(l_run);
   l_run += __shfl_xor(l_run, 32, 64);
   float inv_l[4];

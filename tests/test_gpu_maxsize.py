@@ -82,3 +82,37 @@ def test_largest_slice(hq, block, quant, meta, kernel):
     cache.close()
     del cache, out
     free_gpu()
+
+
+def test_largest_slice_prefill():
+    """Causal prefill attention of the 97 written rows over the same largest slice: each
+    row sees the 89,478,239 zero tokens before the written ones and the written ones up
+    to its own position (every workgroup streams the whole prefix)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=2, hkv=1)
+    p32, u = params_of(wl)
+    say("largest slice prefill, capacity", CAP)
+    cache = make_cache(wl, CAP, p32)
+    for buf in (cache.k_codes, cache.v_codes, cache.k_meta, cache.v_meta):
+        buf.zero_()
+    pos0 = CAP - N_REAL
+    cache.set_length(pos0)
+    k, v = okv_synth.kv_tokens(wl, pos0, N_REAL, device="cuda")
+    cache.write(k, v)
+    q = okv_synth.query_rows(wl, pos0, N_REAL, device="cuda")
+    say("okv_prefill_attn", N_REAL, "rows over", CAP, "tokens")
+    out = cache.prefill_attn(q)
+    torch.cuda.synchronize()
+    ref = oracle.write_unit(okv_synth.host_f32(k[0, :, 0]), okv_synth.host_f32(v[0, :, 0]), wl, p32)
+    k_hat = oracle.dequantize(ref["k_u"], ref["k_meta"], wl)
+    v_hat = oracle.dequantize(ref["v_u"], ref["v_meta"], wl)
+    q1 = okv_synth.host_f32(q)[0].astype(np.float64) @ u.T          # (rows, heads, d)
+    y_ref = np.stack([zero_token_attention(q1[r], k_hat[:r + 1], v_hat[:r + 1], pos0) @ u
+                      for r in range(N_REAL)])
+    err, worst = out_error(out.cpu().numpy()[0], y_ref)
+    say(f"largest slice prefill: max_err/rms={err:.3e} worst_head={worst:.3e}")
+    assert err <= TOL, err
+    cache.close()
+    del cache, out
+    free_gpu()
