@@ -240,9 +240,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   // (Kahan) sum, l_cmp holding the part rounded away: one float32 sum over a prefix of
   // millions of near-equal terms would otherwise drift by up to n 2^-24 of itself
   float m_run = -INFINITY, l_run = 0.0f, l_cmp = 0.0f;
-  float zacc[NZ];                                     // asymmetric values: sum of p z_v per block
+  // asymmetric values: sum of p z_v per block, compensated like l_run (the zero-points
+  // of a block mostly share a sign)
+  float zacc[NZ], zcmp[NZ];
 #pragma unroll
-  for (int z = 0; z < NZ; ++z) zacc[z] = 0.0f;
+  for (int z = 0; z < NZ; ++z) zacc[z] = zcmp[z] = 0.0f;
   f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -418,7 +420,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       l_run *= alpha;
       l_cmp *= alpha;
 #pragma unroll
-      for (int z = 0; z < NZ; ++z) zacc[z] *= alpha;
+      for (int z = 0; z < NZ; ++z) {
+        zacc[z] *= alpha;
+        zcmp[z] *= alpha;
+      }
       m_run = m_new;
       // accumulator rows of this lane are queries 4 lq + r: their factors
       float al[4];
@@ -433,7 +438,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     // as the A operand of P.V: K chunk cc covers tokens 32 cc + 4 lq + r and
     // 32 cc + 16 + 4 lq + r.  p <= 2^8 (lazy maximum), so float16 holds it.
     h8 ph[2], pl[2];
-    float l_tile = 0.0f;
+    float l_tile = 0.0f, z_tile[NZ];
+#pragma unroll
+    for (int z = 0; z < NZ; ++z) z_tile[z] = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
           // zero-points: sum of p z_v per block, in float32
 #pragma unroll
           for (int blk = 0; blk < NBLK; ++blk)
-            zacc[blk] = __builtin_fmaf(pr, vmz_s[blk][16 * tt + 4 * lq + r], zacc[blk]);
+            z_tile[blk] = __builtin_fmaf(pr, vmz_s[blk][16 * tt + 4 * lq + r], z_tile[blk]);
         }
       }
     {
@@ -455,6 +462,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       const float t = l_run + y;
       l_cmp = (t - l_run) - y;
       l_run = t;
+    }
+    if constexpr (ASYM) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const float y = z_tile[blk] - zcmp[blk];
+        const float t = zacc[blk] + y;
+        zcmp[blk] = (t - zacc[blk]) - y;
+        zacc[blk] = t;
+      }
     }
     // ---- P.V: ph vh + ph vl + pl vh per 32-token chunk, scaled back by the normaliser
     // of the wave that unpacked the dims
@@ -499,7 +515,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   if constexpr (ASYM) {
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
-      float z = zacc[blk];
+      float z = zacc[blk] - zcmp[blk];
       z += swz_xor16(z);
       z += __shfl_xor(z, 32, 64);
       float zr[4];

@@ -94,11 +94,15 @@ def free_gpu():
     torch.cuda.empty_cache()
 
 
-def zero_token_attention(q1, k_hat, v_hat, n_zero):
+def zero_token_attention(q1, k_hat, v_hat, n_zero, v_zero=None):
     """Softmax attention of the rows q1 (G, d) over the given keys / values plus n_zero
-    tokens whose key and value are zero vectors (float64): such a token has logit 0 and
-    adds exp(-m) to the denominator only (m = max(0, largest logit))."""
+    tokens whose key is the zero vector and whose value is v_zero (zero by default),
+    in float64: such a token has logit 0, weight exp(-m) (m = max(0, largest logit)),
+    and adds exp(-m) v_zero to the numerator."""
     logits = q1 @ k_hat.T / np.sqrt(q1.shape[-1])
     m = np.maximum(logits.max(axis=1, keepdims=True), 0.0)
     p = np.exp(logits - m)
-    return (p @ v_hat) / (p.sum(axis=1, keepdims=True) + n_zero * np.exp(-m))
+    num = p @ v_hat
+    if v_zero is not None:
+        num = num + n_zero * np.exp(-m) * np.asarray(v_zero, dtype=np.float64)[None, :]
+    return num / (p.sum(axis=1, keepdims=True) + n_zero * np.exp(-m))

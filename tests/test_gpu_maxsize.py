@@ -116,3 +116,58 @@ def test_largest_slice_prefill():
     cache.close()
     del cache, out
     free_gpu()
+
+
+@pytest.mark.parametrize("call", ["decode", "prefill"])
+def test_largest_slice_asym_zero_points(call):
+    """Asymmetric codes at the largest slice (blocks of 64): the filler tokens keep zero
+    key metadata (key = zero vector) but their value metadata is the E4M3 pair (scale 0,
+    zero-point -0.5), so each has the constant value -0.5 in every rotated dim.  Their
+    89 million weighted zero-points must add up to N0 exp(-m) (-0.5) per dim: a plain
+    float32 running sum of those terms would saturate.  Decode (grouped kernel) or
+    causal prefill of the 97 written rows, against the closed form."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hq = 8 if call == "decode" else 2
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=hq, hkv=1, block=64, quant="asym",
+                                                    scale_dtype="e4m3")
+    p32, u = params_of(wl)
+    z0 = -0.5
+    zb = int(oracle.e4m3_encode(np.array([z0], np.float32))[0])
+    assert float(oracle.e4m3_decode(np.array([zb], np.uint8))[0]) == z0
+    say("largest slice asym zero-points", call, "capacity", CAP)
+    cache = make_cache(wl, CAP, p32)
+    for buf in (cache.k_codes, cache.v_codes, cache.k_meta):
+        buf.zero_()
+    cache.v_meta[..., 0].zero_()          # scale bytes
+    cache.v_meta[..., 1].fill_(zb)        # zero-point bytes
+    pos0 = CAP - N_REAL
+    cache.set_length(pos0)
+    k, v = okv_synth.kv_tokens(wl, pos0, N_REAL, device="cuda")
+    cache.write(k, v)
+    ref = oracle.write_unit(okv_synth.host_f32(k[0, :, 0]), okv_synth.host_f32(v[0, :, 0]), wl, p32)
+    k_hat = oracle.dequantize(ref["k_u"], ref["k_meta"], wl)
+    v_hat = oracle.dequantize(ref["v_u"], ref["v_meta"], wl)
+    vz = np.full(wl.d, z0)
+    if call == "decode":
+        cache.set_decode_kernel("grouped")
+        q = okv_synth.queries(wl, 0, device="cuda")
+        out = cache.decode_attn(q)
+        torch.cuda.synchronize()
+        q1 = okv_synth.host_f32(q)[0].astype(np.float64) @ u.T
+        y_ref = zero_token_attention(q1, k_hat, v_hat, pos0, v_zero=vz) @ u
+        got = out.cpu().numpy()[0]
+    else:
+        q = okv_synth.query_rows(wl, pos0, N_REAL, device="cuda")
+        out = cache.prefill_attn(q)
+        torch.cuda.synchronize()
+        q1 = okv_synth.host_f32(q)[0].astype(np.float64) @ u.T
+        y_ref = np.stack([zero_token_attention(q1[r], k_hat[:r + 1], v_hat[:r + 1], pos0, v_zero=vz) @ u
+                          for r in range(N_REAL)])
+        got = out.cpu().numpy()[0]
+    err, worst = out_error(got, y_ref)
+    say(f"largest slice asym zero-points {call}: max_err/rms={err:.3e} worst_head={worst:.3e}")
+    assert err <= TOL, err
+    cache.close()
+    del cache, out
+    free_gpu()

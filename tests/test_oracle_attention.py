@@ -174,3 +174,10 @@ def test_zero_tokens_closed_form():
         want = oracle.attend_exact(qs, ks, vs)
         got = zero_token_attention(qs, ks[:7], vs[:7], n0)
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+        # filler tokens with a constant value vector (a zero scale and a zero-point z)
+        vz = rng.standard_normal(17)
+        vs_z = vs.copy()
+        vs_z[7:] = vz
+        want = oracle.attend_exact(qs, ks, vs_z)
+        got = zero_token_attention(qs, ks[:7], vs[:7], n0, v_zero=vz)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
