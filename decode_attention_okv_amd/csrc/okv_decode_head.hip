@@ -339,10 +339,10 @@ __global__ __launch_bounds__(256) void decode_head_kernel(const DecodeParams p) 
     }
     float pr[4];
 #pragma unroll
-    for (int hf = 0; hf < 4; ++hf) {
-      pr[hf] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[hf], c_logit, -m_run));
-      l_run += pr[hf];
-    }
+    for (int hf = 0; hf < 4; ++hf) pr[hf] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[hf], c_logit, -m_run));
+    // the step's four weights are summed first, so that the running float32 sum takes
+    // one term per step (its rounding drift grows with the number of terms it takes)
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
       if (qd > 0) {

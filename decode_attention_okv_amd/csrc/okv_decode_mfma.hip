@@ -595,12 +595,14 @@ void decode_grouped_kernel(const DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int hl = 0; hl < HPL; ++hl)
+      for (int hl = 0; hl < HPL; ++hl) {
 #pragma unroll
-        for (int hf = 0; hf < 4; ++hf) {
+        for (int hf = 0; hf < 4; ++hf)
           pr[s][hl][hf] = __builtin_amdgcn_exp2f(__builtin_fmaf(L[s][hl][hf], c_logit[s][hl], -m_run[s][hl]));
-          l_run[s][hl] += pr[s][hl][hf];
-        }
+        // one term per step in the running float32 sum (its rounding drift grows with
+        // the number of terms it takes)
+        l_run[s][hl] += (pr[s][hl][0] + pr[s][hl][1]) + (pr[s][hl][2] + pr[s][hl][3]);
+      }
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
       // ---- weights w = p s_v of row (head, block) as 21-bit integers, byte digits
