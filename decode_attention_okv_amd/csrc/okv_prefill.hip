@@ -45,6 +45,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQT = 64;   // query rows per workgroup (16 per wave)
 constexpr int kKT = 64;   // tokens per key/value tile
+constexpr int kFold = 1024;   // tiles per run of the first-level P.V sums (a power of 2)
 
 __device__ __forceinline__ f4 mfma_f16(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   __shared__ __align__(16) _Float16 sfh_s[NBLK][kKT];   // normalised value scales, hi part
   __shared__ __align__(16) _Float16 sfl_s[NBLK][kKT];   // and lo part
   __shared__ float g_s[4];                              // per wave: 1 / normaliser
+  __shared__ float mf_s[kQT];                           // per row: running maximum at the last fold
 
   const int qt = blockIdx.x;
   const int hq = blockIdx.y;
@@ -245,9 +247,42 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   float zacc[NZ], zcmp[NZ];
 #pragma unroll
   for (int z = 0; z < NZ; ++z) zacc[z] = zcmp[z] = 0.0f;
+  // P.V sums in two levels: acc holds the current run of kFold tiles; at the end of a
+  // run it is added into the lane's elements of its (not yet written) output rows in
+  // global memory, the second level, so that no float32 sum takes more than about 1,400
+  // terms even on a 90-million-token prefix (a value dim whose terms share a sign would
+  // otherwise drift by up to n 2^-24 of itself over n tiles).  The folded sums are in
+  // the frame of the row's running maximum at the last fold, kept in mf_s.
   f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  // out += the folded sums, rescaled to the current maximum (first: out = acc), element
+  // by element; the offset is opaque so that none of the addressing is kept live across
+  // the tile loop, and each dim's loads wait for the previous dim's stores (a handful of
+  // registers at any time: this runs once per kFold tiles)
+  auto fold = [&](bool first, bool store) {
+    const float mf = mf_s[16 * wave + j];
+    const float f_own = first || mf == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mf - m_run);
+    float fm[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fm[r] = __shfl(f_own, 4 * lq + r, 64);
+    size_t o = ((static_cast<size_t>(b) * p.n_q + row0 + 16 * wave + 4 * lq) * p.hq + hq) * D + j;
+    asm volatile("" : "+v"(o));
+    const size_t rs = static_cast<size_t>(p.hq) * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (16 * wave + 4 * lq + r < nrows) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float* e = p.out + o + r * rs + 16 * nt;
+          const float x = first ? acc[nt][r] : __builtin_fmaf(*e, fm[r], acc[nt][r]);
+          if (store) *e = x;
+          else acc[nt][r] = x;
+          asm volatile("" ::: "memory");
+        }
+      }
+    }
+  };
 
   const int T = p.len;
   const int ntiles = (T + kTile - 1) / kTile;
@@ -363,6 +398,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         dl[2 * k] = make_uint2(ol[0], ol[1]);
         dl[2 * k + 1] = make_uint2(ol[2], ol[3]);
       }
+    }
+    if (it > 0 && (it & (kFold - 1)) == 0) {    // uniform; acc holds tiles it - kFold .. it - 1
+      fold(it == kFold, true);
+      if (lq == 0) mf_s[16 * wave + j] = m_run;   // rows of this wave only: no barrier
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     if (it + 1 < n_kt) load_tile(t0 + kKT);
     __syncthreads();
@@ -501,6 +542,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
       for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(c[r], g, acc[nt][r]);
     }
   }
+  if (n_kt > kFold) fold(false, false);           // acc += the folded sums
 
   // ---- normalise: l (and the zero-point sums) of query j sum the four lanes of the query
   l_run -= l_cmp;

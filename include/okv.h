@@ -204,7 +204,9 @@ int okv_decode_attn_noalloc(okv_handle* h, const void* q, float* out, void* hip_
  * values are unpacked from the cache inside the kernel (codes as exact float16
  * integers in LDS, block scales applied in float32; nothing dequantised is written
  * to memory).  q: device [batch][n_q][num_q_heads][d] in the input type; out:
- * device float32 [batch][n_q][num_q_heads][d]; both 16-byte aligned.  1 <= n_q <=
+ * device float32 [batch][n_q][num_q_heads][d]; both 16-byte aligned, and out must not
+ * overlap q or the cache: on prefixes of more than 65,536 tokens the kernel also keeps
+ * partial P.V sums of its rows in out before it writes the result there.  1 <= n_q <=
  * len, else OKV_E_INVALID.  Asynchronous on hip_stream. */
 int okv_prefill_attn(okv_handle* h, const void* q, int32_t n_q, float* out, void* hip_stream);
 

@@ -171,3 +171,55 @@ def test_largest_slice_asym_zero_points(call):
     cache.close()
     del cache, out
     free_gpu()
+
+
+@pytest.mark.parametrize("call", ["decode", "prefill"])
+def test_largest_slice_constant_values(call):
+    """Symmetric codes at the largest slice with filler tokens of zero key codes and scale
+    but value scale 0.7 (float16): each filler value is code 0 dequantised, the same
+    negative non-power-of-two number in every rotated dim, so the 89 million P.V terms of
+    a dim share a sign and none is exact in a short float.  The P.V sums must keep that
+    mass: a single float32 running sum over 1.4 million 64-token tiles would drift by
+    about a tenth.  Decode (grouped kernel, eight query heads) or causal prefill of the
+    97 written rows, against the closed form."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hq = 8 if call == "decode" else 2
+    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=hq, hkv=1)
+    p32, u = params_of(wl)
+    scale = np.float16(0.7)
+    nblk = wl.d // wl.block
+    vz = oracle.dequantize(np.zeros((1, wl.d), np.uint8), np.full((1, nblk), scale), wl)[0].astype(np.float64)
+    assert np.all(vz == vz[0]) and vz[0] < 0
+    say("largest slice constant values", call, "capacity", CAP, "filler value", vz[0])
+    cache = make_cache(wl, CAP, p32)
+    for buf in (cache.k_codes, cache.v_codes, cache.k_meta):
+        buf.zero_()
+    cache.v_meta.fill_(float(scale))
+    pos0 = CAP - N_REAL
+    cache.set_length(pos0)
+    k, v = okv_synth.kv_tokens(wl, pos0, N_REAL, device="cuda")
+    cache.write(k, v)
+    ref = oracle.write_unit(okv_synth.host_f32(k[0, :, 0]), okv_synth.host_f32(v[0, :, 0]), wl, p32)
+    k_hat = oracle.dequantize(ref["k_u"], ref["k_meta"], wl)
+    v_hat = oracle.dequantize(ref["v_u"], ref["v_meta"], wl)
+    if call == "decode":
+        cache.set_decode_kernel("grouped")
+        q = okv_synth.queries(wl, 0, device="cuda")
+        out = cache.decode_attn(q)
+        torch.cuda.synchronize()
+        q1 = okv_synth.host_f32(q)[0].astype(np.float64) @ u.T
+        y_ref = zero_token_attention(q1, k_hat, v_hat, pos0, v_zero=vz) @ u
+    else:
+        q = okv_synth.query_rows(wl, pos0, N_REAL, device="cuda")
+        out = cache.prefill_attn(q)
+        torch.cuda.synchronize()
+        q1 = okv_synth.host_f32(q)[0].astype(np.float64) @ u.T
+        y_ref = np.stack([zero_token_attention(q1[r], k_hat[:r + 1], v_hat[:r + 1], pos0, v_zero=vz) @ u
+                          for r in range(N_REAL)])
+    err, worst = out_error(out.cpu().numpy()[0], y_ref)
+    say(f"largest slice constant values {call}: max_err/rms={err:.3e} worst_head={worst:.3e}")
+    assert err <= TOL, err
+    cache.close()
+    del cache, out
+    free_gpu()
