@@ -483,7 +483,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     }
     // ---- probabilities of query j (tokens 16 tt + 4 lq + r) as float16 hi + lo, packed
     // as the A operand of P.V: K chunk cc covers tokens 32 cc + 4 lq + r and
-    // 32 cc + 16 + 4 lq + r.  p <= 2^8 (lazy maximum), so float16 holds it.
+    // 32 cc + 16 + 4 lq + r.  They are taken 2^7 times p: p <= 2^8 (lazy maximum), so
+    // 2^7 p <= 2^15 still fits float16, while the weights of tokens down to 2^-21 of the
+    // running maximum stay normal numbers (below 2^-14 a float16 keeps an absolute error
+    // of up to 2^-25, which many equal small weights would add up).  Every sum formed
+    // from them (P.V, the softmax sum, the zero-point sums) carries the same factor, and
+    // the normalisation removes it.
+    const float m_p = m_run - 7.0f;
     h8 ph[2], pl[2];
     float l_tile = 0.0f, z_tile[NZ];
 #pragma unroll
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(sv[tt][r] - m_run);
+        const float pr = __builtin_amdgcn_exp2f(sv[tt][r] - m_p);
         l_tile += pr;
         const H2 xs = split_h16(pr);
         ph[tt >> 1][4 * (tt & 1) + r] = xs.hi;
