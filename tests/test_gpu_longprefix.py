@@ -2,8 +2,8 @@
 output rows several times (once per 65,536 tokens), with the running maximum moving
 between folds and after the last one.
 
-The cache (one sequence, one KV head, two query heads, d = 128, b = 3) holds 270,016
-tokens.  Its buffers start with zero key codes and scales and a value scale of 0.7 for
+The cache (one sequence, one KV head, two query heads, b = 3; d = 128 with sign flips,
+or d = 256 with the SO(4) rotation) holds 270,016 tokens.  Its buffers start with zero key codes and scales and a value scale of 0.7 for
 every block: such a filler token has key zero (logit 0) and the value of code 0, the
 same negative number in every rotated dim.  Two runs of tokens are written over it with
 okv_write, their keys scaled by 3 so that their logits reach well above the filler's:
@@ -37,15 +37,16 @@ N_END = 97
 KSCALE = 3.0
 
 
-def test_prefill_folds_with_moving_maximum():
+@pytest.mark.parametrize("shape", ["gqa_h32kv8_t32k", "so4_d256_b32_t8k"])
+def test_prefill_folds_with_moving_maximum(shape):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    wl = okv_synth.workload("gqa_h32kv8_t32k").with_(batch=1, hq=2, hkv=1)
+    wl = okv_synth.workload(shape).with_(batch=1, hq=2, hkv=1)
     p32, u = params_of(wl)
     scale = np.float16(0.7)
     nblk = wl.d // wl.block
     vz = oracle.dequantize(np.zeros((1, wl.d), np.uint8), np.full((1, nblk), scale), wl)[0].astype(np.float64)
-    say("long prefix with folds: tokens", T, "middle run at", MID, "filler value", vz[0])
+    say("long prefix with folds:", shape, "d", wl.d, "tokens", T, "middle run at", MID, "filler value", vz[0])
     cache = make_cache(wl, T, p32)
     for buf in (cache.k_codes, cache.v_codes, cache.k_meta):
         buf.zero_()
