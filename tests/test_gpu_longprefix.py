@@ -3,9 +3,11 @@ output rows several times (once per 65,536 tokens), with the running maximum mov
 between folds and after the last one.
 
 The cache (one sequence, one KV head, two query heads, b = 3; d = 128 with sign flips,
-or d = 256 with the SO(4) rotation) holds 270,016 tokens.  Its buffers start with zero key codes and scales and a value scale of 0.7 for
-every block: such a filler token has key zero (logit 0) and the value of code 0, the
-same negative number in every rotated dim.  Two runs of tokens are written over it with
+d = 256 with the SO(4) rotation, or d = 128 asymmetric with E4M3 metadata per 64 values)
+holds 270,016 tokens.  Its buffers start with zero key codes and scales and a value
+scale of 0.7 for every block (asymmetric: value scale 0 and zero-point -2.75): such a
+filler token has key zero (logit 0) and one value, the same negative number in every
+rotated dim.  Two runs of tokens are written over it with
 okv_write, their keys scaled by 3 so that their logits reach well above the filler's:
   - 64 tokens at position 100,000, between the first fold (65,536) and the second,
     where the running maximum of every row jumps;
@@ -37,20 +39,30 @@ N_END = 97
 KSCALE = 3.0
 
 
-@pytest.mark.parametrize("shape", ["gqa_h32kv8_t32k", "so4_d256_b32_t8k"])
+@pytest.mark.parametrize("shape", ["gqa_h32kv8_t32k", "so4_d256_b32_t8k", "gqa_b16h64kv8_t128k_asym"])
 def test_prefill_folds_with_moving_maximum(shape):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     wl = okv_synth.workload(shape).with_(batch=1, hq=2, hkv=1)
     p32, u = params_of(wl)
-    scale = np.float16(0.7)
-    nblk = wl.d // wl.block
-    vz = oracle.dequantize(np.zeros((1, wl.d), np.uint8), np.full((1, nblk), scale), wl)[0].astype(np.float64)
+    if wl.quant == "asym":
+        z0 = -2.75
+        zb = int(oracle.e4m3_encode(np.array([z0], np.float32))[0])
+        assert float(oracle.e4m3_decode(np.array([zb], np.uint8))[0]) == z0
+        vz = np.full(wl.d, z0)
+    else:
+        scale = np.float16(0.7)
+        nblk = wl.d // wl.block
+        vz = oracle.dequantize(np.zeros((1, wl.d), np.uint8), np.full((1, nblk), scale), wl)[0].astype(np.float64)
     say("long prefix with folds:", shape, "d", wl.d, "tokens", T, "middle run at", MID, "filler value", vz[0])
     cache = make_cache(wl, T, p32)
     for buf in (cache.k_codes, cache.v_codes, cache.k_meta):
         buf.zero_()
-    cache.v_meta.fill_(float(scale))
+    if wl.quant == "asym":
+        cache.v_meta[..., 0].zero_()          # scale bytes
+        cache.v_meta[..., 1].fill_(zb)        # zero-point bytes
+    else:
+        cache.v_meta.fill_(float(scale))
 
     hats = []
     pos_end = T - N_END
