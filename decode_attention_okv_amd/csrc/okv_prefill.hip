@@ -147,8 +147,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   __shared__ float g_s[4];                              // per wave: 1 / normaliser
   __shared__ float mf_s[kQT];                           // per row: running maximum at the last fold
 
-  const int qt = blockIdx.x;
-  const int hq = blockIdx.y;
+  // workgroups start longest first: the flat index runs over the query heads fastest,
+  // then over the row tiles from the last (the longest causal prefix) to the first
+  const size_t lin = static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  const int hq = static_cast<int>(lin % static_cast<size_t>(p.hq));
+  const int qt = static_cast<int>(gridDim.x - 1 - lin / static_cast<size_t>(p.hq));
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
